@@ -1,0 +1,129 @@
+/*
+ * rowstats: one-pass row statistics of temperature-scaled logits and top-K
+ * logprobs of converged slots, for the DiffusionGemma denoise sampler
+ * (vLLM API page "diffusion_gemma_sampler").
+ *
+ * C ABI of librowstats.so (HIP, gfx950). Every pointer argument except the
+ * stream is DEVICE memory owned by the caller; the library keeps no pointer
+ * after a call returns. Work is queued asynchronously on `stream` (a
+ * hipStream_t passed as void*, NULL = the default stream): buffers must stay
+ * alive until that stream has been synchronised. Calls that overlap in time
+ * on one device share the library's scratch memory and must be serialised
+ * by the caller (queue them on one stream).
+ *
+ * All functions return ROWSTATS_OK (0) or a negative rowstats_status; they
+ * never abort and never throw. Argument checks run before any HIP call, so
+ * a rejected call touches neither the device nor the outputs.
+ * rowstats_last_error() describes the last failure of the calling thread.
+ */
+#ifndef ROWSTATS_H
+#define ROWSTATS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rowstats_status {
+  ROWSTATS_OK = 0,
+  ROWSTATS_ERR_NULL = -1,   /* a required pointer is NULL */
+  ROWSTATS_ERR_SHAPE = -2,  /* rows < 0, or (rows > 0 and: vocab < 1,
+                               vocab > 2^31 - 1 - 65536, row_stride < vocab,
+                               canvas_len < 1) */
+  ROWSTATS_ERR_K = -3,      /* K < 1, K > vocab or K > 64 */
+  ROWSTATS_ERR_DTYPE = -4,  /* probs_dtype is not one of rowstats_probs_dtype */
+  ROWSTATS_ERR_HIP = -5,    /* a HIP call failed (allocation, launch); see last_error */
+  ROWSTATS_ERR_COOP = -6,   /* the probs path needs every workgroup of a row
+                               resident at once and the device cannot hold them */
+  ROWSTATS_ERR_DEVICE = -7  /* a kernel flagged a failure (a bounded wait ran out);
+                               reported by rowstats_check_device */
+} rowstats_status;
+
+typedef enum rowstats_probs_dtype {
+  ROWSTATS_PROBS_NONE = 0,
+  ROWSTATS_PROBS_BF16 = 1,
+  ROWSTATS_PROBS_FP16 = 2
+} rowstats_probs_dtype;
+
+/*
+ * Argmax, Gumbel-max sample, entropy and (optionally) the softmax of every
+ * row of a [rows, vocab] fp32 logits matrix.
+ * Defined by: diffusion_gemma_sampler page, module docstring (one read per
+ * row, online max and sum, noise drawn inline, probs written once),
+ * sample_row_stats (arguments, outputs, the greedy rule) and
+ * sample_row_stats_reference (the statistics themselves).
+ *
+ *   logits      fp32, element (r, c) at logits[r * row_stride + c]; unit
+ *               column stride; row_stride >= vocab (padded rows allowed).
+ *               Values are finite or -inf; no row is all -inf; x / T stays
+ *               finite in fp32 (not checked on the device).
+ *   rows, vocab matrix shape; rows == 0 returns at once;
+ *               1 <= vocab <= 2^31 - 1 - 65536.
+ *   temps       fp32, at least ceil(rows / canvas_len) entries; row r uses
+ *               T = temps[r / canvas_len]. T > 0 samples with Gumbel noise;
+ *               T <= 0 is greedy (sample = argmax). The scaled logits are
+ *               s = x / max(T, 1e-10f) (IEEE fp32 division).
+ *   canvas_len  rows per temperature slot, >= 1.
+ *   seed        noise seed: column c of row r draws word c & 3 of
+ *               Philox4x32-10(counter = (c >> 2, 0, lo32(r), hi32(r)),
+ *               key = (lo32(seed), hi32(seed))); u = (w + 0.5) 2^-32 and
+ *               the Gumbel variate is -log(-log u), scored in fp64.
+ *   probs_dtype ROWSTATS_PROBS_NONE, _BF16 or _FP16.
+ *   argmax      int64 [rows]: lowest column attaining max_c s (-0 == +0).
+ *   sample      int64 [rows]: lowest column attaining max_c s + g (T > 0),
+ *               the argmax otherwise.
+ *   entropy     fp32 [rows]: -sum_{p>0} p log p of p = softmax(s).
+ *   probs       NULL when probs_dtype is NONE, else [rows, vocab] contiguous
+ *               (row stride vocab) bf16 or fp16: softmax(s) rounded to
+ *               nearest-even, subnormals kept, 0 on -inf columns.
+ *   stream      hipStream_t or NULL.
+ */
+int rowstats_run(const float *logits, int64_t row_stride, int64_t rows,
+                 int64_t vocab, const float *temps, int64_t canvas_len,
+                 uint64_t seed, int probs_dtype, int64_t *argmax,
+                 int64_t *sample, float *entropy, void *probs, void *stream);
+
+/*
+ * Top-K logprobs of the rows of kept slots.
+ * Defined by: diffusion_gemma_sampler page, stash_converged_logprobs
+ * docstring (rows of slots that did not converge are skipped; kept rows are
+ * divided by their temperature; the K largest with ties to the lower id) and
+ * the _lp_topk_kernel docstring (keys order by value, then by lower index,
+ * so the top-K is unique; the K-th largest block maximum bounds it).
+ *
+ *   logits, row_stride, rows, vocab, temps, canvas_len  as for rowstats_run;
+ *               T <= 0 is clamped to 1e-10 like the entropy's temperature.
+ *   keep_mask   uint8 [ceil(rows / canvas_len)]: nonzero = slot kept.
+ *   K           1 <= K <= min(vocab, 64).
+ *   out_vals    fp32 [rows, K] row-major: out_vals[r, k] = s - log Z at the
+ *               column of rank k (descending value, ties to lower column),
+ *               log Z = log sum_c exp(s_c).
+ *   out_idx     int64 [rows, K]: that column.
+ *   Rows of slots that are not kept are not written.
+ */
+int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows,
+                  int64_t vocab, const float *temps, int64_t canvas_len,
+                  const uint8_t *keep_mask, int32_t K, float *out_vals,
+                  int64_t *out_idx, void *stream);
+
+/* Text of the calling thread's last failure ("" if none). */
+const char *rowstats_last_error(void);
+
+/*
+ * Synchronises `stream` and reports ROWSTATS_ERR_DEVICE if any kernel of
+ * this library flagged a failure on the current device since the last
+ * check (a bounded inter-workgroup wait that ran out; the outputs of that
+ * call are then undefined). Clears the flag.
+ */
+int rowstats_check_device(void *stream);
+
+/* Frees the library's scratch memory on every device (it is re-allocated on
+ * the next call). Call only when no work of this library is in flight. */
+int rowstats_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROWSTATS_H */

@@ -32,7 +32,8 @@
  *     H = log Z - sum p * s written relative to the row maximum m;
  *   - probs are rounded to bf16 / fp16 once, to nearest-even, from the double
  *     probability, subnormals kept;
- *   - the top-K logprob of column c is s_c - log Z with the same clamp on T.
+ *   - the top-K logprob of column c is s_c - log Z with the same clamp on T,
+ *     evaluated as (s_c - m) - log sum exp(s - m).
  *
  * Plain C99, no fast-math, no FMA contraction; OpenMP only splits rows.
  */
@@ -363,11 +364,14 @@ int oracle_topk_logprobs(const float *x, int64_t ld, int64_t n_sel,
       }
       double S = 0.0;
       for (int64_t c = 0; c < vocab; ++c) S += exp((double)e[c].s - (double)m);
-      double logZ = (double)m + log(S);
+      /* s - log Z written as (s - m) - log S: s - m is exact in double, so
+         the result keeps its precision when |m| is large (T clamped to
+         1e-10 scales the logits by 1e10) */
+      double logS = log(S);
       qsort(e, (size_t)vocab, sizeof(entry), cmp_entry);
       for (int32_t k = 0; k < K; ++k) {
         out_idx[i * K + k] = e[k].c;
-        out_vals[i * K + k] = (float)((double)e[k].s - logZ);
+        out_vals[i * K + k] = (float)(((double)e[k].s - (double)m) - logS);
       }
     }
     free(e);

@@ -1,0 +1,168 @@
+"""Python binding of librowstats (HIP, gfx950): one-pass row statistics and
+top-K logprobs for the DiffusionGemma denoise sampler (vLLM API page
+"diffusion_gemma_sampler": ``sample_row_stats`` and
+``stash_converged_logprobs``).
+
+This module only marshals torch tensors (device memory) and torch's current
+HIP stream into the C ABI declared in ``include/rowstats.h``; every step of
+the computation runs in the library's kernels. There is no fallback: if the
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librowstats.so")
+
+ROWSTATS_OK = 0
+STATUS_NAMES = {
+    -1: "ROWSTATS_ERR_NULL", -2: "ROWSTATS_ERR_SHAPE", -3: "ROWSTATS_ERR_K",
+    -4: "ROWSTATS_ERR_DTYPE", -5: "ROWSTATS_ERR_HIP", -6: "ROWSTATS_ERR_COOP",
+    -7: "ROWSTATS_ERR_DEVICE",
+}
+PROBS_CODES = {None: 0, torch.bfloat16: 1, torch.float16: 2}
+
+# Entry points declared in include/rowstats.h, with their ctypes signatures.
+_SIGNATURES = {
+    "rowstats_run": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "topk_logprobs": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p]),
+    "rowstats_last_error": (ctypes.c_char_p, []),
+    "rowstats_check_device": (ctypes.c_int, [ctypes.c_void_p]),
+    "rowstats_release": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+class RowStatsError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what} failed: {STATUS_NAMES.get(code, code)}: {last_error()}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python row_softmax_statistics_amd/build.py`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def last_error() -> str:
+    msg = lib().rowstats_last_error()
+    return msg.decode() if msg else ""
+
+
+def _check(code: int, what: str):
+    if code != ROWSTATS_OK:
+        raise RowStatsError(code, what)
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _check_logits(logits: torch.Tensor):
+    if logits.dim() != 2 or logits.dtype != torch.float32:
+        raise ValueError("logits must be a 2-D float32 tensor")
+    if not logits.is_cuda:
+        raise ValueError("logits must be on the GPU")
+    if logits.shape[0] > 0 and logits.shape[1] > 0 and logits.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+
+
+def sample_row_stats(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int, seed: int,
+                     probs_dtype: torch.dtype | None = None, *, out=None):
+    """Argmax, Gumbel-max sample, entropy and (optionally) softmax per row.
+
+    Row ``i`` of ``logits`` ([rows, vocab] fp32, unit column stride, any row
+    stride) uses temperature ``temps[i // canvas_len]``; a temperature <= 0 is
+    greedy. Returns ``(argmax int64, sample int64, entropy fp32,
+    probs [rows, vocab] in probs_dtype or None)``. ``out`` may pass
+    preallocated ``(argmax, sample, entropy, probs)`` tensors.
+    """
+    _check_logits(logits)
+    if probs_dtype not in PROBS_CODES:
+        raise ValueError("probs_dtype must be None, torch.bfloat16 or torch.float16")
+    if temps.dtype != torch.float32 or not temps.is_cuda or not temps.is_contiguous():
+        raise ValueError("temps must be a contiguous float32 GPU tensor")
+    rows, vocab = logits.shape
+    if rows > 0 and temps.numel() < (rows + canvas_len - 1) // max(canvas_len, 1):
+        raise ValueError("temps needs ceil(rows / canvas_len) entries")
+    dev = logits.device
+    if out is None:
+        argmax = torch.empty(rows, dtype=torch.int64, device=dev)
+        sample = torch.empty(rows, dtype=torch.int64, device=dev)
+        entropy = torch.empty(rows, dtype=torch.float32, device=dev)
+        probs = (torch.empty(rows, vocab, dtype=probs_dtype, device=dev)
+                 if probs_dtype is not None else None)
+    else:
+        argmax, sample, entropy, probs = out
+    rc = lib().rowstats_run(
+        _ptr(logits), logits.stride(0) if rows > 1 else vocab, rows, vocab, _ptr(temps),
+        canvas_len, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), PROBS_CODES[probs_dtype],
+        _ptr(argmax), _ptr(sample), _ptr(entropy), _ptr(probs), _stream_ptr(dev))
+    _check(rc, "rowstats_run")
+    return argmax, sample, entropy, probs
+
+
+def topk_logprobs(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int,
+                  keep_mask: torch.Tensor, K: int, out_vals: torch.Tensor | None = None,
+                  out_idx: torch.Tensor | None = None):
+    """Top-K logprobs (descending, ties to the lower column) of kept slots' rows.
+
+    Rows of slots with ``keep_mask[slot] == 0`` are not written. Returns
+    ``(out_vals fp32 [rows, K], out_idx int64 [rows, K])``.
+    """
+    _check_logits(logits)
+    if temps.dtype != torch.float32 or not temps.is_cuda or not temps.is_contiguous():
+        raise ValueError("temps must be a contiguous float32 GPU tensor")
+    if keep_mask.dtype not in (torch.uint8, torch.bool) or not keep_mask.is_cuda:
+        raise ValueError("keep_mask must be a uint8/bool GPU tensor")
+    keep_mask = keep_mask.contiguous()
+    rows, vocab = logits.shape
+    dev = logits.device
+    if out_vals is None:
+        out_vals = torch.empty(rows, K, dtype=torch.float32, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty(rows, K, dtype=torch.int64, device=dev)
+    if not (out_vals.is_contiguous() and out_idx.is_contiguous()):
+        raise ValueError("outputs must be contiguous")
+    rc = lib().topk_logprobs(
+        _ptr(logits), logits.stride(0) if rows > 1 else vocab, rows, vocab, _ptr(temps),
+        canvas_len, _ptr(keep_mask), int(K), _ptr(out_vals), _ptr(out_idx), _stream_ptr(dev))
+    _check(rc, "topk_logprobs")
+    return out_vals, out_idx
+
+
+def check_device(stream=None):
+    """Synchronise and raise if a kernel flagged a failure (see rowstats.h)."""
+    s = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                        else torch.cuda.current_stream().cuda_stream)
+    _check(lib().rowstats_check_device(s), "rowstats_check_device")
+
+
+def release():
+    _check(lib().rowstats_release(), "rowstats_release")

@@ -1,0 +1,312 @@
+// C ABI of librowstats: argument checks, launch planning, per-device scratch
+// and launches on the caller's stream. Declarations and contracts:
+// include/rowstats.h.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+#include "../../include/rowstats.h"
+#include "rowstats_internal.h"
+#include "topk_internal.h"
+
+using namespace rowstats;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char *what) {
+  return fail(ROWSTATS_ERR_HIP, "%s: %s (hipError %d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr int kMaxDevices = 64;
+// Columns (and the padding columns of a row's last slice) index as int32 and
+// the top-K key stores 0x7FFFFFFF - column: keep them all below 2^31.
+constexpr int64_t kMaxVocab = 0x7FFFFFFFLL - 65536;
+
+// Scratch of one device. Grow-only; counters are zero between calls (every
+// kernel returns the counters it used to zero before it ends).
+struct DeviceState {
+  bool ready = false;
+  int cus = 0;
+  int resident[2][3] = {};  // row-stats blocks per CU by [vector path][probs dtype]
+  int topk_resident[2] = {};
+  void *partials = nullptr;
+  size_t partials_bytes = 0;
+  uint32_t *counters = nullptr;
+  size_t counters_len = 0;
+  uint32_t *err_flag = nullptr;
+};
+
+std::mutex g_mu;
+DeviceState g_dev[kMaxDevices];
+
+__global__ void fill_zero_u32(uint32_t *p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t zero_async(uint32_t *p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  fill_zero_u32<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+int device_state(DeviceState **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ROWSTATS_ERR_HIP, "device %d out of range", dev);
+  DeviceState &d = g_dev[dev];
+  if (!d.ready) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
+    d.cus = prop.multiProcessorCount;
+    for (int vec = 0; vec < 2; ++vec) {
+      for (int k = 0; k < 3; ++k) {
+        e = rowstats_resident_blocks(k, vec != 0, &d.resident[vec][k]);
+        if (e != hipSuccess) return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+      }
+      e = topk_resident_blocks(vec != 0, &d.topk_resident[vec]);
+      if (e != hipSuccess) return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    }
+    e = hipMalloc(&d.err_flag, sizeof(uint32_t));
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc(error flag)");
+    e = hipMemset(d.err_flag, 0, sizeof(uint32_t));
+    if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
+    d.ready = true;
+  }
+  *out = &d;
+  return ROWSTATS_OK;
+}
+
+int ensure_scratch(DeviceState &d, size_t partial_bytes, size_t counters, hipStream_t s) {
+  hipError_t e;
+  if (partial_bytes > d.partials_bytes) {
+    if (d.partials) {
+      e = hipFree(d.partials);
+      if (e != hipSuccess) return fail_hip(e, "hipFree(partials)");
+      d.partials = nullptr;
+      d.partials_bytes = 0;
+    }
+    size_t cap = partial_bytes + partial_bytes / 4;
+    e = hipMalloc(&d.partials, cap);
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc(partials)");
+    d.partials_bytes = cap;
+  }
+  if (counters > d.counters_len) {
+    if (d.counters) {
+      e = hipFree(d.counters);
+      if (e != hipSuccess) return fail_hip(e, "hipFree(counters)");
+      d.counters = nullptr;
+      d.counters_len = 0;
+    }
+    size_t cap = counters + counters / 4 + 64;
+    e = hipMalloc(&d.counters, cap * sizeof(uint32_t));
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc(counters)");
+    d.counters_len = cap;
+    e = zero_async(d.counters, cap, s);
+    if (e != hipSuccess) return fail_hip(e, "zeroing counters");
+  }
+  return ROWSTATS_OK;
+}
+
+int check_common(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
+                 const float *temps, int64_t canvas_len) {
+  if (vocab < 1 || vocab > kMaxVocab)
+    return fail(ROWSTATS_ERR_SHAPE, "vocab must be in [1, %lld], got %lld", (long long)kMaxVocab,
+                (long long)vocab);
+  if (row_stride < vocab)
+    return fail(ROWSTATS_ERR_SHAPE, "row_stride %lld < vocab %lld", (long long)row_stride,
+                (long long)vocab);
+  if (canvas_len < 1)
+    return fail(ROWSTATS_ERR_SHAPE, "canvas_len must be >= 1, got %lld", (long long)canvas_len);
+  if (!logits) return fail(ROWSTATS_ERR_NULL, "logits is NULL");
+  if (!temps) return fail(ROWSTATS_ERR_NULL, "temps is NULL");
+  (void)rows;
+  return ROWSTATS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rowstats_last_error(void) { return g_last_error.c_str(); }
+
+int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
+                 const float *temps, int64_t canvas_len, uint64_t seed, int probs_dtype,
+                 int64_t *argmax, int64_t *sample, float *entropy, void *probs, void *stream) {
+  g_last_error.clear();
+  if (probs_dtype < ROWSTATS_PROBS_NONE || probs_dtype > ROWSTATS_PROBS_FP16)
+    return fail(ROWSTATS_ERR_DTYPE, "probs_dtype must be 0 (none), 1 (bf16) or 2 (fp16), got %d",
+                probs_dtype);
+  if (rows < 0) return fail(ROWSTATS_ERR_SHAPE, "rows must be >= 0, got %lld", (long long)rows);
+  if (rows == 0) return ROWSTATS_OK;
+  int rc = check_common(logits, row_stride, rows, vocab, temps, canvas_len);
+  if (rc) return rc;
+  if (!argmax || !sample || !entropy) return fail(ROWSTATS_ERR_NULL, "an output pointer is NULL");
+  if (probs_dtype != ROWSTATS_PROBS_NONE && !probs)
+    return fail(ROWSTATS_ERR_NULL, "probs is NULL but probs_dtype asks for probabilities");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState *d = nullptr;
+  if ((rc = device_state(&d))) return rc;
+
+  RowStatsParams p = {};
+  p.logits = logits;
+  p.ld = row_stride;
+  p.rows = rows;
+  p.vocab = (int32_t)vocab;
+  p.nq = (int32_t)((vocab + 3) / 4);
+  p.nq_full = (int32_t)(vocab / 4);
+  p.G = (p.nq + kRowThreads * kQPT - 1) / (kRowThreads * kQPT);
+  p.vec_ok = ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) && (row_stride % 4 == 0) &&
+             (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(probs) & 7) == 0);
+  p.temps = temps;
+  p.canvas_len = canvas_len;
+  p.seed = seed;
+  p.argmax = argmax;
+  p.sample = sample;
+  p.entropy = entropy;
+  p.probs = probs;
+
+  const int64_t resident = (int64_t)d->resident[p.vec_ok][probs_dtype] * d->cus;
+  if (resident < 1) return fail(ROWSTATS_ERR_HIP, "row-stats kernel cannot be resident");
+  int64_t grid;
+  if (probs_dtype == ROWSTATS_PROBS_NONE) {
+    const int64_t items = rows * (int64_t)p.G;
+    grid = items < resident ? items : resident;
+    p.n_groups = 0;
+    p.xcd_map = (grid % 8 == 0);
+  } else {
+    int64_t groups = resident / p.G;
+    if (groups < 1)
+      return fail(ROWSTATS_ERR_COOP,
+                  "vocab %lld needs %d co-resident workgroups per row, the device holds %lld",
+                  (long long)vocab, p.G, (long long)resident);
+    if (groups > rows) groups = rows;
+    if (groups >= 8) groups -= groups % 8;
+    p.n_groups = (int32_t)groups;
+    grid = groups * p.G;
+    p.xcd_map = (groups % 8 == 0);
+  }
+  if ((rc = ensure_scratch(*d, (size_t)rows * p.G * sizeof(Partial), (size_t)rows, s))) return rc;
+  p.partials = reinterpret_cast<Partial *>(d->partials);
+  p.counters = d->counters;
+  p.err_flag = d->err_flag;
+  hipError_t e = rowstats_launch(p, probs_dtype, (int)grid, s);
+  if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
+  return ROWSTATS_OK;
+}
+
+int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
+                  const float *temps, int64_t canvas_len, const uint8_t *keep_mask, int32_t K,
+                  float *out_vals, int64_t *out_idx, void *stream) {
+  g_last_error.clear();
+  if (rows < 0) return fail(ROWSTATS_ERR_SHAPE, "rows must be >= 0, got %lld", (long long)rows);
+  if (rows == 0) return ROWSTATS_OK;
+  int rc = check_common(logits, row_stride, rows, vocab, temps, canvas_len);
+  if (rc) return rc;
+  if (K < 1 || (int64_t)K > vocab)
+    return fail(ROWSTATS_ERR_K, "K must be in [1, vocab=%lld], got %d", (long long)vocab, K);
+  if (K > kTopKMax) return fail(ROWSTATS_ERR_K, "K must be <= %d, got %d", kTopKMax, K);
+  if (!keep_mask) return fail(ROWSTATS_ERR_NULL, "keep_mask is NULL");
+  if (!out_vals || !out_idx) return fail(ROWSTATS_ERR_NULL, "an output pointer is NULL");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState *d = nullptr;
+  if ((rc = device_state(&d))) return rc;
+
+  TopKParams p = {};
+  p.logits = logits;
+  p.ld = row_stride;
+  p.rows = rows;
+  p.vocab = (int32_t)vocab;
+  p.nq = (int32_t)((vocab + 3) / 4);
+  p.nq_full = (int32_t)(vocab / 4);
+  p.G = (p.nq + kTopKThreads * kTopKQPT - 1) / (kTopKThreads * kTopKQPT);
+  p.vec_ok = ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) && (row_stride % 4 == 0) &&
+             (vocab % 4 == 0);
+  p.temps = temps;
+  p.canvas_len = canvas_len;
+  p.keep = keep_mask;
+  p.K = K;
+  p.out_vals = out_vals;
+  p.out_idx = out_idx;
+  const int64_t resident = (int64_t)d->topk_resident[p.vec_ok] * d->cus;
+  if (resident < 1) return fail(ROWSTATS_ERR_HIP, "top-K kernel cannot be resident");
+  const int64_t items = rows * (int64_t)p.G;
+  const int64_t grid = items < resident ? items : resident;
+  p.xcd_map = (grid % 8 == 0);
+  if ((rc = ensure_scratch(*d, (size_t)rows * p.G * topk_partial_bytes(K), (size_t)rows, s)))
+    return rc;
+  p.partials = d->partials;
+  p.counters = d->counters;
+  hipError_t e = topk_launch(p, (int)grid, s);
+  if (e != hipSuccess) return fail_hip(e, "top-K kernel launch");
+  return ROWSTATS_OK;
+}
+
+int rowstats_check_device(void *stream) {
+  g_last_error.clear();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState *d = nullptr;
+  int rc = device_state(&d);
+  if (rc) return rc;
+  uint32_t flag = 0;
+  e = hipMemcpy(&flag, d->err_flag, sizeof flag, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpy(error flag)");
+  if (flag == 0) return ROWSTATS_OK;
+  // a wait ran out: counters of that call may be left non-zero
+  e = hipMemset(d->err_flag, 0, sizeof(uint32_t));
+  if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
+  if (d->counters) {
+    e = zero_async(d->counters, d->counters_len, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail_hip(e, "zeroing counters");
+  }
+  return fail(ROWSTATS_ERR_DEVICE, "a kernel's inter-workgroup wait ran out (flag %u)", flag);
+}
+
+int rowstats_release(void) {
+  g_last_error.clear();
+  std::lock_guard<std::mutex> lock(g_mu);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  for (int dev = 0; dev < kMaxDevices; ++dev) {
+    DeviceState &d = g_dev[dev];
+    if (!d.ready) continue;
+    if ((e = hipSetDevice(dev)) != hipSuccess) return fail_hip(e, "hipSetDevice");
+    if (d.partials) (void)hipFree(d.partials);
+    if (d.counters) (void)hipFree(d.counters);
+    if (d.err_flag) (void)hipFree(d.err_flag);
+    d = DeviceState();
+  }
+  if ((e = hipSetDevice(cur)) != hipSuccess) return fail_hip(e, "hipSetDevice");
+  return ROWSTATS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,274 @@
+// Device helpers shared by the row-statistics and top-K kernels (gfx950,
+// wave64): Philox4x32-10, exact temperature scaling, order keys, wave and
+// workgroup reductions, and fp32 -> bf16/fp16 rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rowstats {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): per round two 32x32->64
+// products of counter words 0 and 2, xor-mixed with words 1 and 3 and the
+// key; the key advances by the Weyl constants between rounds.
+// Counter layout of the noise: (quad, 0, lo32(row), hi32(row)); key (seed).
+// ---------------------------------------------------------------------------
+struct Philox {
+  static constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  static constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+};
+
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += Philox::W0;
+      k1 += Philox::W1;
+    }
+    const uint64_t p0 = (uint64_t)Philox::M0 * c0;
+    const uint64_t p1 = (uint64_t)Philox::M1 * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n3 = (uint32_t)p0;
+    c0 = n0;
+    c1 = n1;
+    c2 = n2;
+    c3 = n3;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+__device__ __forceinline__ uint32_t pick(const uint4 &w, int i) {
+  return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
+}
+
+// Standard Gumbel variate of a 32-bit word: u = (w + 0.5) 2^-32 lies in
+// (0, 1) and is exact in double; g = -log(-log u). Kept out of line: its
+// fp64 constants would otherwise be hoisted into registers of the caller's
+// whole loop, and it only runs for a few columns per slice.
+__device__ __attribute__((noinline)) double gumbel_of_word(uint32_t w) {
+  const double u = ((double)w + 0.5) * 0x1p-32;
+  return -log(-log(u));
+}
+
+// Largest Gumbel variate any word can give (w = 2^32 - 1), rounded up.
+constexpr double kGumbelMax = 22.8739;
+
+// ---------------------------------------------------------------------------
+// Temperature: T <= 0 (and NaN-free T below 1e-10) clamps to 1e-10f.
+// s = fl32(x / Tc) is computed as fl32((double)x * fl64(1 / Tc)): the double
+// product is within 2^-52 (relative) of x / Tc, while x / Tc is never within
+// 2^-49 of a midpoint between two fp32 values unless it equals one, and it
+// can equal one only if x / Tc needs 25 significant bits, which two 24-bit
+// operands cannot produce. So the final rounding is the IEEE quotient.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float clamp_temp(float t) { return t > 1e-10f ? t : 1e-10f; }
+
+__device__ __forceinline__ float scale(float x, double rtc) {
+  return (float)((double)x * rtc);
+}
+
+// Order-preserving int32 of the fp32 bits (after +0.0f so that -0 == +0).
+__device__ __forceinline__ int32_t key32(float s) {
+  const int32_t b = __float_as_int(s + 0.0f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float key32_value(int32_t k) {
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
+}
+// 64-bit key: value key in the high word, 0x7FFFFFFF - column in the low word.
+__device__ __forceinline__ int64_t key64(float s, int32_t col) {
+  return ((int64_t)key32(s) << 32) | (int64_t)(uint32_t)(0x7FFFFFFF - col);
+}
+__device__ __forceinline__ int32_t key64_col(int64_t k) {
+  return 0x7FFFFFFF - (int32_t)(uint32_t)(k & 0xFFFFFFFF);
+}
+
+// ---------------------------------------------------------------------------
+// float4 component access (indices are compile-time after unrolling).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float max4(const float4 &a) {
+  return fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+}
+__device__ __forceinline__ float comp(const float4 &a, int i) {
+  return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : a.w;
+}
+__device__ __forceinline__ void set_comp(float4 &a, int i, float v) {
+  if (i == 0) a.x = v;
+  else if (i == 1) a.y = v;
+  else if (i == 2) a.z = v;
+  else a.w = v;
+}
+
+// ---------------------------------------------------------------------------
+// Buffer resources. A slice is addressed through a raw buffer descriptor
+// whose base is the slice start and whose size stops at the row end: loads
+// past the end return 0 and stores past it are dropped by the hardware, and
+// every per-iteration offset is a constant, so no per-lane 64-bit addresses
+// are kept in registers.
+// ---------------------------------------------------------------------------
+using Rsrc = __amdgpu_buffer_rsrc_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data, gfx9-family descriptor
+constexpr int kNonTemporal = 2;         // cache policy bit: streaming store
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+// Column of element (j, i) of thread t in a slice starting at quad q0:
+// 4 * (q0 + j * NT + t) + i. Element k = 4 j + i is a compile-time index.
+template <int NT>
+__device__ __forceinline__ int32_t slice_col(int32_t q0, int k) {
+  return 4 * (q0 + (k >> 2) * NT + (int32_t)threadIdx.x) + (k & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Loads one slice of a row into registers and scales it, s = fl32(x / Tc).
+// Thread t holds quads q0 + j * NT + t (j < QPT): each load instruction of a
+// wave covers 1 KiB of contiguous logits. VEC (row base 16-byte aligned,
+// vocab % 4 == 0) uses one 16-byte load per quad, otherwise four 4-byte
+// loads. Columns past the row end become -inf. Returns the thread's maximum
+// of s.
+// ---------------------------------------------------------------------------
+template <int QPT, int NT, bool VEC>
+__device__ __forceinline__ float load_scaled_slice(const float *xrow, int32_t q0, int32_t V,
+                                                   double rtc, float4 (&v)[QPT]) {
+  const int32_t c0 = 4 * q0;
+  const int32_t left = V - c0;  // valid columns from the slice start (> 0)
+  const int32_t span = 4 * NT * QPT;
+  const Rsrc r = make_rsrc(xrow + c0, 4u * (uint32_t)min(left, span));
+  const uint32_t voff = 16u * threadIdx.x;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 16 * j * NT, 0);
+      v[j] = make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]),
+                         __uint_as_float(t[3]));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < QPT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        set_comp(v[j], i,
+                 __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 16 * j * NT + 4 * i, 0)));
+  }
+  if (left < span) {  // the slice runs past the row end
+    const int32_t tcol = 4 * (int32_t)threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        set_comp(v[j], i, (tcol + 4 * j * NT + i < left) ? comp(v[j], i) : -INFINITY);
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    v[j].x = scale(v[j].x, rtc);
+    v[j].y = scale(v[j].y, rtc);
+    v[j].z = scale(v[j].z, rtc);
+    v[j].w = scale(v[j].w, rtc);
+    mt = fmaxf(mt, max4(v[j]));
+  }
+  return mt;
+}
+
+// One logit of the slice (for rare re-reads), column c = 4 * q0 + cl.
+__device__ __forceinline__ float load_one(const float *xrow, int32_t q0, int32_t cl) {
+  return xrow[4 * (int64_t)q0 + cl];
+}
+
+// ---------------------------------------------------------------------------
+// Rounding to the probs dtypes. p is finite and >= 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t bf16_rne_bits(float p) {
+  const uint32_t b = __float_as_uint(p);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t fp16_rne_bits(float p) {
+  // fp32 -> fp16 conversion rounds to nearest-even; fp16 denormals are kept
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p);
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions with DPP inside 16-lane rows and lane swaps across rows.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+constexpr int kDppQuadSwap1 = 0xB1, kDppQuadSwap2 = 0x4E, kDppHalfMirror = 0x141,
+              kDppMirror = 0x140;
+
+__device__ __forceinline__ uint32_t xor_lanes(uint32_t v, int mask) {
+  return (uint32_t)__shfl_xor((int)v, mask, kWave);
+}
+
+template <int STEP>
+__device__ __forceinline__ uint32_t lane_exchange(uint32_t v) {
+  if constexpr (STEP == 1) return dpp32<kDppQuadSwap1>(v);
+  else if constexpr (STEP == 2) return dpp32<kDppQuadSwap2>(v);
+  else if constexpr (STEP == 4) return dpp32<kDppHalfMirror>(v);
+  else if constexpr (STEP == 8) return dpp32<kDppMirror>(v);
+  else return xor_lanes(v, STEP);
+}
+
+// Applies `op` over the 64 lanes; every lane ends with the result. The lane
+// pairing differs per step (xor, mirror) but each step merges two disjoint
+// halves of equal size, so the result is the full reduction.
+template <class T, class Op>
+__device__ __forceinline__ T wave_allreduce(T v, Op op) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+#define ROWSTATS_STEP(S)                                                          \
+  {                                                                               \
+    T o;                                                                          \
+    if constexpr (sizeof(T) == 4) {                                               \
+      uint32_t b = __builtin_bit_cast(uint32_t, v);                               \
+      o = __builtin_bit_cast(T, lane_exchange<S>(b));                             \
+    } else {                                                                      \
+      uint64_t b = __builtin_bit_cast(uint64_t, v);                               \
+      uint32_t lo = lane_exchange<S>((uint32_t)b), hi = lane_exchange<S>((uint32_t)(b >> 32)); \
+      o = __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);                       \
+    }                                                                             \
+    v = op(v, o);                                                                 \
+  }
+  ROWSTATS_STEP(1)
+  ROWSTATS_STEP(2)
+  ROWSTATS_STEP(4)
+  ROWSTATS_STEP(8)
+  ROWSTATS_STEP(16)
+  ROWSTATS_STEP(32)
+#undef ROWSTATS_STEP
+  return v;
+}
+
+struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct MinI { __device__ int32_t operator()(int32_t a, int32_t b) const { return a < b ? a : b; } };
+struct SumD { __device__ double operator()(double a, double b) const { return a + b; } };
+struct MaxD { __device__ double operator()(double a, double b) const { return fmax(a, b); } };
+struct MaxI64 { __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; } };
+
+// Workgroup-wide reductions through one LDS slot per wave.
+template <int NT, class T, class Op>
+__device__ __forceinline__ T block_allreduce(T v, Op op, T *lds) {
+  v = wave_allreduce(v, op);
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[wave] = v;
+  __syncthreads();
+  T r = lds[0];
+#pragma unroll
+  for (int w = 1; w < (NT / kWave); ++w) r = op(r, lds[w]);
+  __syncthreads();
+  return r;
+}
+
+}  // namespace rowstats

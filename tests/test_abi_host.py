@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/rowstats.h declares,
+and reject bad arguments with the documented status codes before it makes
+any HIP call (so these run without a device). Contracts: include/rowstats.h.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import row_softmax_statistics_amd as rs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rowstats.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_K, ERR_DTYPE = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+NULL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["rowstats_run", "topk_logprobs", "rowstats_last_error",
+                                           "rowstats_check_device", "rowstats_release"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rs.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # the binding covers exactly the declared entry points
+    assert sorted(rs._SIGNATURES) == declared_functions()
+
+
+def run(logits=FAKE, stride=8, rows=4, vocab=8, temps=FAKE, canvas=2, seed=1, dtype=0,
+        argmax=FAKE, sample=FAKE, entropy=FAKE, probs=NULL):
+    return rs.lib().rowstats_run(logits, stride, rows, vocab, temps, canvas, seed, dtype,
+                                 argmax, sample, entropy, probs, NULL)
+
+
+def topk(logits=FAKE, stride=8, rows=4, vocab=8, temps=FAKE, canvas=2, keep=FAKE, K=2,
+         vals=FAKE, idx=FAKE):
+    return rs.lib().topk_logprobs(logits, stride, rows, vocab, temps, canvas, keep, K, vals, idx,
+                                  NULL)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dtype=3), ERR_DTYPE),
+    (dict(dtype=-1), ERR_DTYPE),
+    (dict(rows=-1), ERR_SHAPE),
+    (dict(vocab=0), ERR_SHAPE),
+    (dict(vocab=2**31), ERR_SHAPE),
+    (dict(stride=7), ERR_SHAPE),
+    (dict(canvas=0), ERR_SHAPE),
+    (dict(logits=NULL), ERR_NULL),
+    (dict(temps=NULL), ERR_NULL),
+    (dict(argmax=NULL), ERR_NULL),
+    (dict(sample=NULL), ERR_NULL),
+    (dict(entropy=NULL), ERR_NULL),
+    (dict(dtype=1, probs=NULL), ERR_NULL),
+    (dict(dtype=2, probs=NULL), ERR_NULL),
+])
+def test_rowstats_run_rejects(kwargs, code):
+    assert run(**kwargs) == code
+    assert rs.last_error() != ""
+
+
+def test_rowstats_run_zero_rows_is_a_no_op():
+    # nothing is dereferenced and no HIP call is made
+    assert run(rows=0, logits=NULL, temps=NULL, argmax=NULL, sample=NULL, entropy=NULL) == OK
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(K=0), ERR_K),
+    (dict(K=9), ERR_K),
+    (dict(K=65, vocab=100, stride=100), ERR_K),
+    (dict(rows=-2), ERR_SHAPE),
+    (dict(vocab=0), ERR_SHAPE),
+    (dict(stride=3), ERR_SHAPE),
+    (dict(canvas=0), ERR_SHAPE),
+    (dict(keep=NULL), ERR_NULL),
+    (dict(vals=NULL), ERR_NULL),
+    (dict(idx=NULL), ERR_NULL),
+    (dict(logits=NULL), ERR_NULL),
+])
+def test_topk_rejects(kwargs, code):
+    assert topk(**kwargs) == code
+    assert rs.last_error() != ""
+
+
+def test_topk_zero_rows_is_a_no_op():
+    assert topk(rows=0, logits=NULL, keep=NULL, vals=NULL, idx=NULL) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 8)
+    with pytest.raises(ValueError):
+        rs.sample_row_stats(x, torch.ones(1), 2, 0)

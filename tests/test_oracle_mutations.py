@@ -34,8 +34,8 @@ MUTANTS = [
     ("bf16_truncates", "double r = nearbyint(v / quantum);", "double r = floor(v / quantum);"),
     ("fp16_min_exponent", "round_to_format(p, 10, -14);", "round_to_format(p, 10, -15);"),
     ("topk_tie_order", "return (x->c < y->c) ? -1 : (x->c > y->c);", "return (x->c > y->c) ? -1 : (x->c < y->c);"),
-    ("topk_logprob_uses_max", "out_vals[i * K + k] = (float)((double)e[k].s - logZ);",
-     "out_vals[i * K + k] = (float)((double)e[k].s - (double)m);"),
+    ("topk_logprob_drops_logS", "out_vals[i * K + k] = (float)(((double)e[k].s - (double)m) - logS);",
+     "out_vals[i * K + k] = (float)(((double)e[k].s - (double)m));"),
     ("temperature_slot", "float t = temps[row / canvas_len];", "float t = temps[row % canvas_len];"),
     ("probs_unnormalised", "double p = exp(d) / S;", "double p = exp(d);"),
     ("sample_without_noise", "double z = (double)s[c] + g;", "double z = (double)s[c] + 0.0 * g;"),

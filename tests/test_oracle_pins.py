@@ -336,9 +336,14 @@ def test_topk_matches_bruteforce_sort():
         s = oracle.scale_row(x[r], temps[slot])
         order = np.lexsort((np.arange(vocab), -s.astype(np.float64)))
         assert np.array_equal(idx[r], order[:K]), r
-        logz = scipy.special.logsumexp(s.astype(np.float64))
-        assert np.allclose(vals[r], (s[order[:K]].astype(np.float64) - logz).astype(np.float32),
-                           rtol=1e-6, atol=1e-6)
+        # reference in the row-centred frame: (s - m) - logsumexp(s - m)
+        sd = s.astype(np.float64) - float(s.max())
+        ref = (sd[order[:K]] - scipy.special.logsumexp(sd)).astype(np.float32)
+        assert np.allclose(vals[r], ref, rtol=1e-6, atol=1e-6)
+        if temps[slot] <= 0:
+            # greedy rows: the tied maxima share the mass exactly, -log(#ties)
+            nt = int(np.sum(s == s.max()))
+            assert vals[r][0] == np.float32(-math.log(nt))
 
 
 def test_topk_full_row_logprobs_normalise():

@@ -1,0 +1,238 @@
+"""Benchmark of the one-pass row-statistics sampler on one MI355X.
+
+A step is one call of rowstats_run (one kernel launch: scale, max/argmax,
+sum-exp and entropy, inline Gumbel sample, probs written once) over the
+C2 workload: 4096 rows (16 slots x canvas 256) x 262144 vocab fp32 logits
+N(0, 2.5^2) with 512 rows peaked (+15), slot temperatures {0, 0.7, 1.0},
+bf16 probs. Inputs are resident in HBM before the timed region.
+
+Prints one JSON line: the metric (algorithmic logits+probs GB/s), the
+roofline of the kernel (HBM, 8 TB/s), the oracle's CPU rate on a bounded
+sample of the same workload, and secondary measurements of the other
+workloads (C3 stats-only, C4 top-K, C5 large padded) under "others".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others]
+       [--no-cpu] [--only C2|C3|C4|C5] [--calib-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "row-stats logits GB/s and % of HBM peak at V=262144 (rows/s alongside)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def algorithmic_bytes(rows: int, vocab: int, probs_bytes: int, slots: int = 0) -> int:
+    """Logits read once + probs written once + 20 B of outputs per row
+    (argmax, sample, entropy) + one fp32 temperature per slot."""
+    return rows * vocab * (4 + probs_bytes) + 20 * rows + 4 * slots
+
+
+def topk_algorithmic_bytes(kept_rows: int, vocab: int, K: int, slots: int = 0) -> int:
+    """Logits of kept rows read once + K (value, index) pairs per kept row +
+    a temperature and a keep flag per slot."""
+    return kept_rows * (4 * vocab + 12 * K) + 5 * slots
+
+
+def source_hash() -> str:
+    h = hashlib.sha1()
+    for f in sorted(glob.glob(os.path.join(ROOT, "row_softmax_statistics_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters for the current
+    kernel sources, or None when absent or taken from other sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m = re.search(r"^source_hash\s+(\w+)", txt, flags=re.M)
+    if not m or m.group(1) != source_hash():
+        return None
+    m = re.search(rf"^{workload}\s+.*?fetch_bytes=(\d+)\s+write_bytes=(\d+)", txt, flags=re.M)
+    if not m:
+        return None
+    return int(m.group(1)) + int(m.group(2))
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Runs fn warmup times, then times `steps` calls with HIP events on the
+    current stream (each call is one kernel launch). Returns (ms per call
+    from events, wall ms per call)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return start.elapsed_time(end) / steps, wall
+
+
+def bench_rowstats(w, steps, warmup):
+    import torch
+    import row_softmax_statistics_amd as rs
+    rows, vocab = w.rows, w.vocab
+    dev = w.logits.device
+    pb = 0 if w.probs_dtype is None else 2
+    out = (torch.empty(rows, dtype=torch.int64, device=dev),
+           torch.empty(rows, dtype=torch.int64, device=dev),
+           torch.empty(rows, dtype=torch.float32, device=dev),
+           torch.empty(rows, vocab, dtype=w.probs_dtype, device=dev) if pb else None)
+
+    def step():
+        rs.sample_row_stats(w.logits, w.temps, w.canvas_len, w.seed, w.probs_dtype, out=out)
+
+    ms, wall = time_launches(step, steps, warmup)
+    rs.check_device()
+    nbytes = algorithmic_bytes(rows, vocab, pb, w.temps.numel())
+    return {"ms": ms, "wall_ms": wall, "bytes": nbytes, "gbs": nbytes / ms / 1e6,
+            "rows_per_s": rows / ms * 1e3}
+
+
+def bench_topk(w, steps, warmup):
+    import torch
+    import row_softmax_statistics_amd as rs
+    dev = w.logits.device
+    vals = torch.empty(w.rows, w.K, dtype=torch.float32, device=dev)
+    idx = torch.empty(w.rows, w.K, dtype=torch.int64, device=dev)
+
+    def step():
+        rs.topk_logprobs(w.logits, w.temps, w.canvas_len, w.keep_mask, w.K, vals, idx)
+
+    ms, wall = time_launches(step, steps, warmup)
+    rs.check_device()
+    slot = torch.arange(w.rows, device=dev) // w.canvas_len
+    kept = int((w.keep_mask[slot] != 0).sum())
+    nbytes = topk_algorithmic_bytes(kept, w.vocab, w.K, w.temps.numel())
+    return {"ms": ms, "wall_ms": wall, "bytes": nbytes, "gbs": nbytes / ms / 1e6,
+            "kept_rows_per_s": kept / ms * 1e3}
+
+
+def cpu_baseline(w, n_rows: int):
+    """The oracle, as it is, on a seeded sample of the workload's rows."""
+    import numpy as np
+    import torch
+    import oracle
+    rng = np.random.default_rng(99)
+    rows = np.sort(rng.choice(w.rows, size=min(n_rows, w.rows), replace=False))
+    x = w.logits.index_select(0, torch.as_tensor(rows, device=w.logits.device)).cpu().numpy()
+    temps = w.temps.cpu().numpy()
+    code = {None: oracle.PROBS_NONE, torch.bfloat16: oracle.PROBS_BF16}[w.probs_dtype]
+    t0 = time.perf_counter()
+    oracle.rowstats(x, rows, temps, w.canvas_len, w.seed, code)
+    dt = time.perf_counter() - t0
+    nbytes = algorithmic_bytes(len(rows), w.vocab, 0 if code == 0 else 2)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "rows_per_s": round(len(rows) / dt, 1), "seconds": round(dt, 2),
+            "sample": f"{len(rows)} seeded rows of {w.name} ({w.rows} x {w.vocab}), full rows"}
+
+
+def calib_copy(steps=5):
+    """A plain copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": 4 * n, "calib_copy_bytes_written": 4 * n,
+                      "launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--only", choices=["C2", "C3", "C4", "C5"], default=None)
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the method's "
+              "hot path is measured on one MI355X; sharding is described, not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic as syn
+    if args.calib_copy:
+        calib_copy()
+        return
+    dev = "cuda:0"
+
+    if args.only:
+        w = syn.WORKLOADS[args.only](dev)
+        r = bench_topk(w, args.steps, args.warmup) if args.only == "C4" else \
+            bench_rowstats(w, args.steps, args.warmup)
+        print(json.dumps({"workload": args.only, **{k: round(v, 4) if isinstance(v, float) else v
+                                                     for k, v in r.items()}}))
+        return
+
+    w = syn.c2(dev)
+    r = bench_rowstats(w, args.steps, args.warmup)
+    traffic = recorded_traffic("C2")
+    roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "rowstats_kernel<8,1,true>", "bytes_per_launch": r["bytes"],
+            "avg_launch_ms": round(r["ms"], 4)}
+    line = {
+        "metric": METRIC, "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded on the GPU)",
+        "config": {"workload": "C2: 4096 rows (16 slots x canvas 256) x 262144 vocab, fp32 "
+                               "N(0,2.5^2) logits, 512 rows +15 peaked, slot temps {0,0.7,1.0}, "
+                               "bf16 probs, noise seed 1234",
+                   "rows": w.rows, "vocab": w.vocab, "probs_dtype": "bf16",
+                   "rows_per_s": round(r["rows_per_s"], 1),
+                   "pct_hbm_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
+                   "wall_ms_per_step": round(r["wall_ms"], 4)},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    del w
+    torch.cuda.empty_cache()
+    if not args.no_others:
+        others = {}
+        for name in ("C3", "C5", "C4"):
+            wo = syn.WORKLOADS[name](dev)
+            ro = bench_topk(wo, max(5, args.steps // 2), 2) if name == "C4" else \
+                bench_rowstats(wo, max(5, args.steps // 2), 2)
+            ro = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in ro.items()}
+            ro["pct_hbm_peak"] = round(100 * ro["gbs"] / HBM_PEAK_GBS, 2)
+            ro["traffic"] = recorded_traffic(name)
+            others[name] = ro
+            del wo
+            torch.cuda.empty_cache()
+        line["others"] = others
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

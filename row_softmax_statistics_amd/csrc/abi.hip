@@ -208,8 +208,10 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
     grid = groups * p.G;
     p.xcd_map = (groups % 8 == 0);
   }
-  if ((rc = ensure_scratch(*d, (size_t)rows * p.G * sizeof(Partial), (size_t)rows, s))) return rc;
-  p.partials = reinterpret_cast<Partial *>(d->partials);
+  if ((rc = ensure_scratch(*d, (size_t)rows * p.G * kSliceTupleWords * sizeof(uint64_t),
+                          (size_t)rows, s)))
+    return rc;
+  p.partials = reinterpret_cast<uint64_t *>(d->partials);
   p.counters = d->counters;
   p.err_flag = d->err_flag;
   hipError_t e = rowstats_launch(p, probs_dtype, (int)grid, s);

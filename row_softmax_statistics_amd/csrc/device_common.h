@@ -47,18 +47,6 @@ __device__ __forceinline__ uint32_t pick(const uint4 &w, int i) {
   return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
 }
 
-// Standard Gumbel variate of a 32-bit word: u = (w + 0.5) 2^-32 lies in
-// (0, 1) and is exact in double; g = -log(-log u). Kept out of line: its
-// fp64 constants would otherwise be hoisted into registers of the caller's
-// whole loop, and it only runs for a few columns per slice.
-__device__ __attribute__((noinline)) double gumbel_of_word(uint32_t w) {
-  const double u = ((double)w + 0.5) * 0x1p-32;
-  return -log(-log(u));
-}
-
-// Largest Gumbel variate any word can give (w = 2^32 - 1), rounded up.
-constexpr double kGumbelMax = 22.8739;
-
 // ---------------------------------------------------------------------------
 // Temperature: T <= 0 (and NaN-free T below 1e-10) clamps to 1e-10f.
 // s = fl32(x / Tc) is computed as fl32((double)x * fl64(1 / Tc)): the double
@@ -253,6 +241,7 @@ __device__ __forceinline__ T wave_allreduce(T v, Op op) {
 
 struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
 struct MinI { __device__ int32_t operator()(int32_t a, int32_t b) const { return a < b ? a : b; } };
+struct SumF { __device__ float operator()(float a, float b) const { return a + b; } };
 struct SumD { __device__ double operator()(double a, double b) const { return a + b; } };
 struct MaxD { __device__ double operator()(double a, double b) const { return fmax(a, b); } };
 struct MaxI64 { __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; } };

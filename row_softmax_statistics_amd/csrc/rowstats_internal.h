@@ -12,16 +12,8 @@ constexpr int kQPT = 8;
 constexpr int kRowThreads = 512;
 constexpr int kSliceCols = kRowThreads * kQPT * 4;
 
-// Per-slice tuple of the row-statistics kernel (48 bytes).
-struct alignas(16) Partial {
-  double S;    // sum over the slice of 2^32 exp(s - m)
-  double W;    // sum over the slice of 2^32 exp(s - m) (s - m), exp > 0
-  double zb;   // best perturbed score s + g of the slice (-inf: none)
-  float m;     // slice max of s
-  int32_t am;  // lowest column attaining m
-  int32_t zc;  // lowest column attaining zb
-  int32_t pad;
-};
+// Words of global scratch per slice tuple (see the kernel).
+constexpr int kSliceTupleWords = 5;
 
 struct RowStatsParams {
   const float *logits;
@@ -41,7 +33,7 @@ struct RowStatsParams {
   int64_t *sample;
   float *entropy;
   void *probs;
-  Partial *partials;  // [rows, G]
+  uint64_t *partials; // [rows, G] slice tuples of kSliceTupleWords words
   uint32_t *counters; // [rows], zero between calls
   uint32_t *err_flag;
 };

@@ -37,8 +37,9 @@ constexpr int kMaxDevices = 64;
 // the top-K key stores 0x7FFFFFFF - column: keep them all below 2^31.
 constexpr int64_t kMaxVocab = 0x7FFFFFFFLL - 65536;
 
-// Scratch of one device. Grow-only; counters are zero between calls (every
-// kernel returns the counters it used to zero before it ends).
+// Scratch of one device. Grow-only. The row counters form two banks of
+// counters_len / 2 words: a call counts in bank `parity` and its kernel
+// zeroes the other bank, which the next call uses.
 struct DeviceState {
   bool ready = false;
   int cus = 0;
@@ -49,6 +50,8 @@ struct DeviceState {
   uint32_t *counters = nullptr;
   size_t counters_len = 0;
   uint32_t *err_flag = nullptr;
+  bool xcc_round_robin = false;  // workgroup b of a launch runs on XCC b % 8
+  int parity = 0;                // counter bank of the next call
 };
 
 std::mutex g_mu;
@@ -58,6 +61,28 @@ __global__ void fill_zero_u32(uint32_t *p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0u;
+}
+
+// Records the XCC of each workgroup of a cooperative launch.
+__global__ void xcc_of_workgroups(int *out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = (int)__builtin_amdgcn_s_getreg((20) | ((4 - 1) << 11));
+}
+
+// Whether workgroups are placed on XCCs round-robin by their index, the
+// placement the row-statistics kernel's XCD-local synchronisation needs.
+bool probe_xcc_round_robin(int cus) {
+  const int n = 8 * (cus / 8 > 0 ? cus / 8 : 1);
+  int *d = nullptr;
+  if (hipMalloc(&d, n * sizeof(int)) != hipSuccess) return false;
+  void *args[] = {&d};
+  bool ok = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&xcc_of_workgroups), dim3(n),
+                                       dim3(64), args, 0, nullptr) == hipSuccess;
+  int *h = new int[n];
+  ok = ok && hipMemcpy(h, d, n * sizeof(int), hipMemcpyDeviceToHost) == hipSuccess;
+  for (int i = 0; ok && i < n; ++i) ok = (h[i] == i % 8);
+  delete[] h;
+  (void)hipFree(d);
+  return ok;
 }
 
 hipError_t zero_async(uint32_t *p, size_t n, hipStream_t s) {
@@ -91,6 +116,7 @@ int device_state(DeviceState **out) {
     if (e != hipSuccess) return fail_hip(e, "hipMalloc(error flag)");
     e = hipMemset(d.err_flag, 0, sizeof(uint32_t));
     if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
+    d.xcc_round_robin = probe_xcc_round_robin(d.cus);
     d.ready = true;
   }
   *out = &d;
@@ -196,6 +222,9 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
     grid = items < resident ? items : resident;
     p.n_groups = 0;
     p.xcd_map = (grid % 8 == 0);
+    // an ordinary launch may place workgroups off XCC b % 8 (seen right
+    // after other kernels), and this path never waits: agent scope
+    p.l2_sync = 0;
   } else {
     int64_t groups = resident / p.G;
     if (groups < 1)
@@ -207,15 +236,21 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
     p.n_groups = (int32_t)groups;
     grid = groups * p.G;
     p.xcd_map = (groups % 8 == 0);
+    // the cooperative launch places workgroup b on XCC b % 8 (probed at
+    // init, checked by every workgroup), so each row's group shares an L2
+    p.l2_sync = d->xcc_round_robin && p.xcd_map;
   }
   if ((rc = ensure_scratch(*d, (size_t)rows * p.G * kSliceTupleWords * sizeof(uint64_t),
-                          (size_t)rows, s)))
+                          2 * (size_t)rows, s)))
     return rc;
   p.partials = reinterpret_cast<uint64_t *>(d->partials);
   p.counters = d->counters;
+  p.counter_stride = (int64_t)(d->counters_len / 2);
+  p.parity = d->parity;
   p.err_flag = d->err_flag;
   hipError_t e = rowstats_launch(p, probs_dtype, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
+  d->parity ^= 1;
   return ROWSTATS_OK;
 }
 
@@ -259,12 +294,15 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   const int64_t items = rows * (int64_t)p.G;
   const int64_t grid = items < resident ? items : resident;
   p.xcd_map = (grid % 8 == 0);
-  if ((rc = ensure_scratch(*d, (size_t)rows * p.G * topk_partial_bytes(K), (size_t)rows, s)))
+  if ((rc = ensure_scratch(*d, (size_t)rows * p.G * topk_partial_bytes(K), 2 * (size_t)rows, s)))
     return rc;
   p.partials = d->partials;
   p.counters = d->counters;
+  p.counter_stride = (int64_t)(d->counters_len / 2);
+  p.parity = d->parity;
   hipError_t e = topk_launch(p, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "top-K kernel launch");
+  d->parity ^= 1;
   return ROWSTATS_OK;
 }
 
@@ -281,6 +319,8 @@ int rowstats_check_device(void *stream) {
   e = hipMemcpy(&flag, d->err_flag, sizeof flag, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpy(error flag)");
   if (flag == 0) return ROWSTATS_OK;
+  // a workgroup ran off its expected XCC: stop relying on the placement
+  if (flag & 2u) d->xcc_round_robin = false;
   // a wait ran out: counters of that call may be left non-zero
   e = hipMemset(d->err_flag, 0, sizeof(uint32_t));
   if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
@@ -289,7 +329,9 @@ int rowstats_check_device(void *stream) {
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail_hip(e, "zeroing counters");
   }
-  return fail(ROWSTATS_ERR_DEVICE, "a kernel's inter-workgroup wait ran out (flag %u)", flag);
+  return fail(ROWSTATS_ERR_DEVICE, "a kernel flagged %s (flag %u)",
+              (flag & 2u) ? "a workgroup off its expected XCD" : "an inter-workgroup wait that ran out",
+              flag);
 }
 
 int rowstats_release(void) {

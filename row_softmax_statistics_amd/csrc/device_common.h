@@ -119,20 +119,22 @@ __device__ __forceinline__ int32_t slice_col(int32_t q0, int k) {
 }
 
 // ---------------------------------------------------------------------------
-// Loads one slice of a row into registers and scales it, s = fl32(x / Tc).
-// Thread t holds quads q0 + j * NT + t (j < QPT): each load instruction of a
-// wave covers 1 KiB of contiguous logits. VEC (row base 16-byte aligned,
-// vocab % 4 == 0) uses one 16-byte load per quad, otherwise four 4-byte
-// loads. Columns past the row end become -inf. Returns the thread's maximum
-// of s.
+// Slice loads. Thread t of an NT-thread workgroup holds quads q0 + j NT + t
+// (j < QPT): each load instruction of a wave covers 1 KiB of contiguous
+// logits. VEC (row base 16-byte aligned, vocab % 4 == 0) moves 16 bytes per
+// quad, otherwise four 4-byte loads. Columns past the row end read as 0 and
+// are set to -inf by scale_slice.
 // ---------------------------------------------------------------------------
+template <int QPT, int NT>
+__device__ __forceinline__ Rsrc slice_rsrc(const float *xrow, int32_t q0, int32_t V) {
+  const int32_t left = V - 4 * q0;  // valid columns from the slice start (> 0)
+  return make_rsrc(xrow + 4 * q0, 4u * (uint32_t)min(left, 4 * NT * QPT));
+}
+
 template <int QPT, int NT, bool VEC>
-__device__ __forceinline__ float load_scaled_slice(const float *xrow, int32_t q0, int32_t V,
-                                                   double rtc, float4 (&v)[QPT]) {
-  const int32_t c0 = 4 * q0;
-  const int32_t left = V - c0;  // valid columns from the slice start (> 0)
-  const int32_t span = 4 * NT * QPT;
-  const Rsrc r = make_rsrc(xrow + c0, 4u * (uint32_t)min(left, span));
+__device__ __forceinline__ void load_slice(const float *xrow, int32_t q0, int32_t V,
+                                           float4 (&v)[QPT]) {
+  const Rsrc r = slice_rsrc<QPT, NT>(xrow, q0, V);
   const uint32_t voff = 16u * threadIdx.x;
   if constexpr (VEC) {
 #pragma unroll
@@ -149,7 +151,51 @@ __device__ __forceinline__ float load_scaled_slice(const float *xrow, int32_t q0
         set_comp(v[j], i,
                  __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 16 * j * NT + 4 * i, 0)));
   }
-  if (left < span) {  // the slice runs past the row end
+}
+
+// Asynchronous copy of a slice (VEC layout) into an LDS stage of NT * QPT
+// quads laid out like the registers: quad j of thread t at stage[j NT + t].
+// Waves 1..NW-1 issue all the copies (wave 0 keeps its memory queue free for
+// latency-critical work: waits on it would otherwise also wait for the
+// in-order copies). Before reading, every copying wave waits for its copies
+// (stage_wait) and the workgroup synchronises.
+template <int QPT, int NT>
+__device__ __forceinline__ void stage_slice_async(float4 *stage, const float *xrow, int32_t q0,
+                                                  int32_t V) {
+  constexpr int NW = NT / 64;
+  const int wave = threadIdx.x / 64;
+  if (wave == 0) return;
+  const Rsrc r = slice_rsrc<QPT, NT>(xrow, q0, V);
+  const uint32_t voff = 16u * (threadIdx.x & 63);
+  for (int n = wave - 1; n < QPT * NW; n += NW - 1) {
+    const int off = (n / NW) * NT + (n % NW) * 64;  // quad offset of 64 lanes
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)(stage + off), 16, voff, 16 * off, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void stage_wait() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+}
+
+template <int QPT, int NT>
+__device__ __forceinline__ void read_stage(const float4 *stage, float4 (&v)[QPT]) {
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) v[j] = stage[j * NT + threadIdx.x];
+}
+
+// Scalar (uniform-address) load through the constant address space.
+__device__ __forceinline__ float load_uniform(const float *p) {
+  return *(const __attribute__((address_space(4))) float *)p;
+}
+
+// Masks columns past the row end to -inf and scales s = fl32(x / Tc).
+// Returns the thread's maximum of s.
+template <int QPT, int NT>
+__device__ __forceinline__ float scale_slice(float4 (&v)[QPT], int32_t q0, int32_t V,
+                                             double rtc) {
+  const int32_t left = V - 4 * q0;
+  if (left < 4 * NT * QPT) {  // the slice runs past the row end
     const int32_t tcol = 4 * (int32_t)threadIdx.x;
 #pragma unroll
     for (int j = 0; j < QPT; ++j)
@@ -167,6 +213,13 @@ __device__ __forceinline__ float load_scaled_slice(const float *xrow, int32_t q0
     mt = fmaxf(mt, max4(v[j]));
   }
   return mt;
+}
+
+template <int QPT, int NT, bool VEC>
+__device__ __forceinline__ float load_scaled_slice(const float *xrow, int32_t q0, int32_t V,
+                                                   double rtc, float4 (&v)[QPT]) {
+  load_slice<QPT, NT, VEC>(xrow, q0, V, v);
+  return scale_slice<QPT, NT>(v, q0, V, rtc);
 }
 
 // One logit of the slice (for rare re-reads), column c = 4 * q0 + cl.
@@ -208,6 +261,34 @@ __device__ __forceinline__ uint32_t lane_exchange(uint32_t v) {
   else if constexpr (STEP == 4) return dpp32<kDppHalfMirror>(v);
   else if constexpr (STEP == 8) return dpp32<kDppMirror>(v);
   else return xor_lanes(v, STEP);
+}
+
+// Applies `op` over groups of WIDTH lanes (WIDTH = 2..64, a power of 2);
+// every lane ends with its group's result. Narrow widths reduce few items
+// (the items sit in the first lanes) in fewer dependent steps.
+template <int WIDTH, class T, class Op>
+__device__ __forceinline__ T group_allreduce(T v, Op op) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+#define ROWSTATS_GSTEP(S)                                                         \
+  if constexpr (WIDTH > S) {                                                      \
+    T o;                                                                          \
+    if constexpr (sizeof(T) == 4) {                                               \
+      o = __builtin_bit_cast(T, lane_exchange<S>(__builtin_bit_cast(uint32_t, v))); \
+    } else {                                                                      \
+      uint64_t b = __builtin_bit_cast(uint64_t, v);                               \
+      uint32_t lo = lane_exchange<S>((uint32_t)b), hi = lane_exchange<S>((uint32_t)(b >> 32)); \
+      o = __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);                       \
+    }                                                                             \
+    v = op(v, o);                                                                 \
+  }
+  ROWSTATS_GSTEP(1)
+  ROWSTATS_GSTEP(2)
+  ROWSTATS_GSTEP(4)
+  ROWSTATS_GSTEP(8)
+  ROWSTATS_GSTEP(16)
+  ROWSTATS_GSTEP(32)
+#undef ROWSTATS_GSTEP
+  return v;
 }
 
 // Applies `op` over the 64 lanes; every lane ends with the result. The lane

@@ -34,15 +34,17 @@ __constant__ const MathTable kMath = {
     0x1.71547652b82fep+0,
 };
 
-__device__ __forceinline__ const MathTable *math_table() {
-  const MathTable *t = &kMath;
+typedef const __attribute__((address_space(4))) MathTable *MathTablePtr;
+
+__device__ __forceinline__ MathTablePtr math_table() {
+  MathTablePtr t = (MathTablePtr)&kMath;
   __asm__ volatile("" : "+s"(t));
   return t;
 }
 
 // Natural log of a positive, finite, normal x.
 __device__ __forceinline__ double log_d(double x) {
-  const MathTable *T = math_table();
+  MathTablePtr T = math_table();
   const uint64_t b = (uint64_t)__double_as_longlong(x);
   int k = (int)((b >> 52) & 0x7FF) - 1023;
   double m = __longlong_as_double((long long)((b & 0x000FFFFFFFFFFFFFull) | 0x3FF0000000000000ull));
@@ -69,7 +71,7 @@ __device__ __forceinline__ double log_d(double x) {
 
 // exp of x; underflows to 0 below about -745.
 __device__ __forceinline__ double exp_d(double x) {
-  const MathTable *T = math_table();
+  MathTablePtr T = math_table();
   if (x < -745.2) return 0.0;
   const double k = rint(x * T->inv_ln2);
   double r = fma(-k, T->ln2_hi, x);

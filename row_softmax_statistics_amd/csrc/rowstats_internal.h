@@ -26,6 +26,7 @@ struct RowStatsParams {
   int32_t n_groups;   // probs path: rows processed concurrently
   int32_t vec_ok;     // logits and probs aligned, ld % 4 == 0, vocab % 4 == 0
   int32_t xcd_map;    // grid is a multiple of 8 with G | grid / 8
+  int32_t l2_sync;    // the workgroups of every row share one XCD (see the kernel)
   const float *temps;
   int64_t canvas_len;
   uint64_t seed;
@@ -34,7 +35,9 @@ struct RowStatsParams {
   float *entropy;
   void *probs;
   uint64_t *partials; // [rows, G] slice tuples of kSliceTupleWords words
-  uint32_t *counters; // [rows], zero between calls
+  uint32_t *counters; // two banks of counter_stride words (see the kernel)
+  int64_t counter_stride;
+  int32_t parity;     // bank this call counts in
   uint32_t *err_flag;
 };
 

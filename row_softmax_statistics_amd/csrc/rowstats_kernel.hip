@@ -62,65 +62,114 @@ struct SliceShared {
   float scale[kWaves];
 };
 
-// Merge over the wave of items 0..n-1 (lane i takes i, i + 64, ...); the
-// result is valid in every lane. `get(i)` returns item i.
-template <class Get>
+// Merge of items 0..n-1 of a wave (lane i takes i, i + 64, ...; n <= WIDTH
+// unless WIDTH is 64). The result is valid in every lane of the first WIDTH.
+// The factors exp(m_i - m) are fp32 (relative error near 1e-7); the sums
+// stay fp64.
+template <int WIDTH, class Get>
 __device__ __forceinline__ Tuple merge_tuples(int n, Get get) {
   const int lane = threadIdx.x & (kWave - 1);
   float m = -INFINITY;
   for (int i = lane; i < n; i += kWave) m = fmaxf(m, get(i).m);
-  m = wave_allreduce(m, MaxF());
+  m = group_allreduce<WIDTH>(m, MaxF());
   double S = 0.0, W = 0.0, zb = -INFINITY;
   int32_t am = INT_MAX;
   for (int i = lane; i < n; i += kWave) {
     const Tuple t = get(i);
     if (t.S > 0.0) {
-      const double dm = (double)t.m - (double)m;
-      const double f = exp_d(dm);
+      const float dm = fmaxf(t.m - m, -FLT_MAX);  // <= 0, exact when the maxima are close
+      const double f = (double)__builtin_amdgcn_exp2f(dm * kLog2e);
       S += t.S * f;
-      W += f * (t.W + t.S * dm);
+      W += f * (t.W + t.S * (double)dm);
     }
     if (t.m == m) am = min(am, t.am);
     zb = fmax(zb, t.zb);
   }
   Tuple r;
   r.m = m;
-  r.S = wave_allreduce(S, SumD());
-  r.W = wave_allreduce(W, SumD());
-  r.am = wave_allreduce(am, MinI());
-  r.zb = wave_allreduce(zb, MaxD());
+  r.S = group_allreduce<WIDTH>(S, SumD());
+  r.W = group_allreduce<WIDTH>(W, SumD());
+  r.am = group_allreduce<WIDTH>(am, MinI());
+  r.zb = group_allreduce<WIDTH>(zb, MaxD());
   int32_t zc = INT_MAX;
   for (int i = lane; i < n; i += kWave) {
     const Tuple t = get(i);
     if (t.zb == r.zb) zc = min(zc, t.zc);
   }
-  r.zc = wave_allreduce(zc, MinI());
+  r.zc = group_allreduce<WIDTH>(zc, MinI());
   return r;
 }
 
-// Slice tuples in global scratch: five 64-bit words written and read with
-// relaxed agent-scope atomics, so each access is coherent across XCDs
-// without flushing or invalidating whole caches.
-constexpr int kTupleWords = kSliceTupleWords;
-
-__device__ __forceinline__ void store_tuple_word(uint64_t *dst, int k, const Tuple &t) {
-  uint64_t v;
-  switch (k) {
-    case 0: v = (uint64_t)__float_as_uint(t.m) | ((uint64_t)(uint32_t)t.am << 32); break;
-    case 1: v = (uint64_t)__double_as_longlong(t.S); break;
-    case 2: v = (uint64_t)__double_as_longlong(t.W); break;
-    case 3: v = (uint64_t)__double_as_longlong(t.zb); break;
-    default: v = (uint64_t)(uint32_t)t.zc; break;
-  }
-  __hip_atomic_store(dst + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Row merge of G slice tuples with the narrowest lane width that holds them.
+template <class Get>
+__device__ __forceinline__ Tuple merge_slices(int G, Get get) {
+  if (G <= 8) return merge_tuples<8>(G, get);
+  if (G <= 16) return merge_tuples<16>(G, get);
+  if (G <= 32) return merge_tuples<32>(G, get);
+  return merge_tuples<64>(G, get);
 }
 
-__device__ __forceinline__ Tuple load_tuple(const uint64_t *src) {
+// Slice tuples in global scratch, five 64-bit words each, and one counter
+// per row. Two coherence modes:
+//   XCD-local (p.l2_sync): every workgroup of a row runs on one XCD (the
+//     launch places them so and each workgroup checks its XCC id), so the
+//     XCD's L2 is their point of coherence: stores write through L1 into
+//     L2, atomics execute in L2 (the counter is polled with an atomic), and
+//     a reader invalidates its CU's L1 before loading tuples. Round trips
+//     stay on-chip instead of queueing behind the HBM stream.
+//   agent: relaxed agent-scope atomics, each coherent across XCDs on its own.
+// Either way a writer waits for its stores before counting the slice in.
+constexpr int kTupleWords = kSliceTupleWords;
+constexpr int kL1Bypass = 1;  // sc0 cache-policy bit
+
+struct SyncScratch {
+  Rsrc tuples, counters;
+  uint64_t *tuple_ptr;
+  uint32_t *counter_ptr;
+  bool l2;
+};
+
+__device__ __forceinline__ SyncScratch sync_scratch(const RowStatsParams &p) {
+  SyncScratch s;
+  s.tuple_ptr = p.partials;
+  s.tuples = make_rsrc(p.partials, (uint32_t)(p.rows * p.G * kTupleWords * 8));
+  s.counters = make_rsrc(p.counters + (size_t)p.parity * p.counter_stride, (uint32_t)(p.rows * 4));
+  s.counter_ptr = p.counters + (size_t)p.parity * p.counter_stride;
+  s.l2 = p.l2_sync != 0;
+  return s;
+}
+
+__device__ __forceinline__ uint64_t tuple_word(const Tuple &t, int k) {
+  switch (k) {
+    case 0: return (uint64_t)__float_as_uint(t.m) | ((uint64_t)(uint32_t)t.am << 32);
+    case 1: return (uint64_t)__double_as_longlong(t.S);
+    case 2: return (uint64_t)__double_as_longlong(t.W);
+    case 3: return (uint64_t)__double_as_longlong(t.zb);
+    default: return (uint64_t)(uint32_t)t.zc;
+  }
+}
+
+// word index of tuple (row, g), word k
+__device__ __forceinline__ uint32_t tuple_index(const RowStatsParams &p, int64_t row, int g, int k) {
+  return (uint32_t)((row * p.G + g) * kTupleWords + k);
+}
+
+// Drops this CU's L1 lines so that later loads read the XCD's L2.
+__device__ __forceinline__ void l1_invalidate(const SyncScratch &s) {
+  if (s.l2) __asm__ volatile("buffer_inv sc0" ::: "memory");
+}
+
+__device__ __forceinline__ Tuple load_tuple(const SyncScratch &s, uint32_t w0) {
   uint64_t w[kTupleWords];
 #pragma unroll
-  for (int k = 0; k < kTupleWords; ++k)
-    w[k] = __hip_atomic_load(const_cast<uint64_t *>(src) + k, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+  for (int k = 0; k < kTupleWords; ++k) {
+    if (s.l2) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(s.tuples, 8u * (w0 + k), 0, kL1Bypass);
+      w[k] = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+    } else {
+      w[k] = __hip_atomic_load(s.tuple_ptr + w0 + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   Tuple t;
   t.m = __uint_as_float((uint32_t)w[0]);
   t.am = (int32_t)(uint32_t)(w[0] >> 32);
@@ -131,18 +180,49 @@ __device__ __forceinline__ Tuple load_tuple(const uint64_t *src) {
   return t;
 }
 
+__device__ __forceinline__ uint32_t counter_add(const SyncScratch &s, int64_t row) {
+  if (s.l2) return (uint32_t)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, s.counters, 4u * (uint32_t)row, 0, 0);
+  return __hip_atomic_fetch_add(s.counter_ptr + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t counter_load(const SyncScratch &s, int64_t row) {
+  if (s.l2) {
+    // add an opaque zero: an add of a known 0 would be folded into a load,
+    // which may hit a stale L1 line; the atomic always reads the L2
+    uint32_t zero = 0;
+    __asm__ volatile("" : "+v"(zero));
+    return __hip_atomic_fetch_add(s.counter_ptr + row, zero, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  return __hip_atomic_load(s.counter_ptr + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Publishes a slice tuple (lanes 0..4 of the calling wave store one word
 // each), waits until the stores are done, then counts the slice in. Returns
 // the counter value before the add, in every lane.
-__device__ __forceinline__ uint32_t publish_tuple(uint64_t *dst, const Tuple &t, uint32_t *ctr) {
+__device__ __forceinline__ uint32_t publish_tuple(const SyncScratch &s, uint32_t w0, const Tuple &t,
+                                                  int64_t row) {
   const int lane = threadIdx.x & (kWave - 1);
-  if (lane < kTupleWords) store_tuple_word(dst, lane, t);
+  if (lane < kTupleWords) {
+    const uint64_t v = tuple_word(t, lane);
+    if (s.l2) {
+      const u32x2 pk = {(uint32_t)v, (uint32_t)(v >> 32)};
+      __builtin_amdgcn_raw_buffer_store_b64(pk, s.tuples, 8u * (w0 + lane), 0, 0);
+    } else {
+      __hip_atomic_store(s.tuple_ptr + w0 + lane, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) old = counter_add(s, row);
   return (uint32_t)__shfl((int)old, 0, kWave);
+}
+
+// XCC (XCD) id of the executing workgroup.
+__device__ __forceinline__ uint32_t xcc_id() {
+  return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11));  // HW_REG_XCC_ID[3:0]
 }
 
 __device__ __forceinline__ void write_row_outputs(const RowStatsParams &p, int64_t row,
@@ -154,23 +234,26 @@ __device__ __forceinline__ void write_row_outputs(const RowStatsParams &p, int64
   p.entropy[row] = (float)H;
 }
 
-// Everything one workgroup does for slice g of `row`.
+// Everything one workgroup does for slice g of `row`. On entry v holds the
+// slice's raw logits; `stage` (vector path) still holds them too and is
+// refilled with the next slice (`next_xrow`, `next_q0`) once no wave reads
+// it any more.
 template <int QPT, int PROBS, bool VEC>
 __device__ __forceinline__ void process_slice(const RowStatsParams &p, int64_t row, int g,
-                                              SliceShared &sh) {
+                                              SliceShared &sh, float4 (&v)[QPT], float4 *stage,
+                                              const float *next_xrow, int32_t next_q0) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int32_t V = p.vocab;
-  const float T = p.temps[row / p.canvas_len];
+  const float T = load_uniform(p.temps + row / p.canvas_len);
   const bool greedy = !(T > 0.0f);
   const double rtc = 1.0 / (double)clamp_temp(T);
   const float *xrow = p.logits + row * p.ld;
   const int32_t q0 = g * (kThreads * QPT);
 
-  // ---- load the slice once and scale it: s = fl32(x / Tc) ----
-  float4 v[QPT];
-  const float mt = load_scaled_slice<QPT, kThreads, VEC>(xrow, q0, V, rtc, v);
+  // ---- scale the slice: s = fl32(x / Tc) ----
+  const float mt = scale_slice<QPT, kThreads>(v, q0, V, rtc);
   const float mw = wave_allreduce(mt, MaxF());
 
   // ---- lowest column of the wave attaining its max ----
@@ -208,6 +291,11 @@ __device__ __forceinline__ void process_slice(const RowStatsParams &p, int64_t r
   if (!greedy && mw != -INFINITY) {
     const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
     const uint32_t r0 = (uint32_t)(uint64_t)row, r1 = (uint32_t)((uint64_t)row >> 32);
+    // raw logit of element k of this thread (re-read, never kept in registers)
+    auto raw_x = [&](int k) -> float {
+      if constexpr (VEC) return comp(stage[(k >> 2) * kThreads + tid], k & 3);
+      else return xrow[slice_col<kThreads>(q0, k)];
+    };
     // a = exp(m - zlb) = -log u of the argmax's word, zlb = m + g_argmax
     float a = neg_log_u_f32(
         pick(philox4x32_10((uint32_t)(amw >> 2), 0u, r0, r1, k0, k1), amw & 3));
@@ -248,18 +336,37 @@ __device__ __forceinline__ void process_slice(const RowStatsParams &p, int64_t r
           cm |= (uint64_t)((float)(~pick(w, i)) <= comp(v[j], i) * kc) << (4 * j + i);
       }
     }
-    // exact fp64 scores of the candidates: re-read x, redraw the word
-    while (cm) {
-      const int k = __builtin_ctzll(cm);
-      cm &= cm - 1;
+    // Candidates in two rounds: an fp32 score relative to m (error below
+    // 1e-3: s - m is exact for every candidate, -log of -log u is off by at
+    // most 2^-12) picks those within 2^-8 of the wave's best, and only
+    // those get the exact fp64 score.
+    float za = -INFINITY;
+    for (uint64_t c2 = cm; c2; c2 &= c2 - 1) {
+      const int k = __builtin_ctzll(c2);
       const int32_t c = slice_col<kThreads>(q0, k);
       if (c < V) {
-        const float s = scale(xrow[c], rtc);
+        const float d = scale(raw_x(k), rtc) - mw;
         const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, r0, r1, k0, k1);
-        const double z = (double)s + gumbel_of_word(pick(w, c & 3));
-        if (z > bz || (z == bz && c < bc)) {
-          bz = z;
-          bc = c;
+        const float ga = -__builtin_amdgcn_logf(neg_log_u_f32(pick(w, c & 3))) *
+                         0.693147180559945309f;
+        za = fmaxf(za, d + ga);
+      }
+    }
+    const float zcut = wave_allreduce(za, MaxF()) - 0x1p-8f;
+    for (; cm; cm &= cm - 1) {
+      const int k = __builtin_ctzll(cm);
+      const int32_t c = slice_col<kThreads>(q0, k);
+      if (c < V) {
+        const float s = scale(raw_x(k), rtc);
+        const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, r0, r1, k0, k1);
+        const uint32_t wc = pick(w, c & 3);
+        const float ga = -__builtin_amdgcn_logf(neg_log_u_f32(wc)) * 0.693147180559945309f;
+        if ((s - mw) + ga >= zcut) {
+          const double z = (double)s + gumbel_of_word(wc);
+          if (z > bz || (z == bz && c < bc)) {
+            bz = z;
+            bc = c;
+          }
         }
       }
     }
@@ -277,31 +384,32 @@ __device__ __forceinline__ void process_slice(const RowStatsParams &p, int64_t r
     if (lane == 0) sh.wave[wave] = t;
   }
   __syncthreads();
-  uint64_t *P = p.partials + (row * p.G) * kTupleWords;
-  uint32_t *ctr = p.counters + row;
+  // no wave reads the stage any more: start copying the next slice
+  if constexpr (VEC) {
+    if (next_xrow) stage_slice_async<QPT, kThreads>(stage, next_xrow, next_q0, V);
+  }
+  const SyncScratch sy = sync_scratch(p);
+  const uint32_t w_row = tuple_index(p, row, 0, 0);
 
   if constexpr (PROBS == 0) {
     if (wave == 0) {
-      const Tuple st = merge_tuples(kWaves, [&](int i) { return sh.wave[i]; });
-      const uint32_t old = publish_tuple(P + g * kTupleWords, st, ctr);
+      const Tuple st = merge_tuples<kWaves>(kWaves, [&](int i) { return sh.wave[i]; });
+      const uint32_t old = publish_tuple(sy, w_row + g * kTupleWords, st, row);
       if (old == (uint32_t)(p.G - 1)) {
         // last slice of the row: every tuple was stored before its count
-        const Tuple r = merge_tuples(p.G, [&](int i) { return load_tuple(P + i * kTupleWords); });
-        if (lane == 0) {
-          write_row_outputs(p, row, greedy, r);
-          __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        l1_invalidate(sy);
+        const Tuple r =
+            merge_slices(p.G, [&](int i) { return load_tuple(sy, w_row + i * kTupleWords); });
+        if (lane == 0) write_row_outputs(p, row, greedy, r);
       }
     }
-    __syncthreads();  // sh.wave is rewritten by the next slice
   } else {
     if (wave == 0) {
-      const Tuple st = merge_tuples(kWaves, [&](int i) { return sh.wave[i]; });
-      publish_tuple(P + g * kTupleWords, st, ctr);
+      const Tuple st = merge_tuples<kWaves>(kWaves, [&](int i) { return sh.wave[i]; });
+      publish_tuple(sy, w_row + g * kTupleWords, st, row);
       if (lane == 0) {
         uint32_t spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               (uint32_t)p.G) {
+        while (counter_load(sy, row) < (uint32_t)p.G) {
           __builtin_amdgcn_s_sleep(1);
           if (++spins > kSpinLimit) {
             atomicOr(p.err_flag, 1u);
@@ -310,24 +418,20 @@ __device__ __forceinline__ void process_slice(const RowStatsParams &p, int64_t r
         }
       }
       // the loads below are issued after lane 0 has seen every count
-      const Tuple r = merge_tuples(p.G, [&](int i) { return load_tuple(P + i * kTupleWords); });
+      l1_invalidate(sy);
+      const Tuple r =
+          merge_slices(p.G, [&](int i) { return load_tuple(sy, w_row + i * kTupleWords); });
       // exp value of wave i -> probability: p = e exp(m_i - m) / S
       if (lane < kWaves) {
         const Tuple t = sh.wave[lane];
-        sh.scale[lane] =
-            (t.m == -INFINITY) ? 0.0f : (float)(exp_d((double)t.m - (double)r.m) / r.S);
+        sh.scale[lane] = (t.m == -INFINITY)
+                             ? 0.0f
+                             : (float)((double)__builtin_amdgcn_exp2f(fmaxf(t.m - r.m, -FLT_MAX) * kLog2e) / r.S);
       }
-      if (lane == 0) {
-        if (g == 0) write_row_outputs(p, row, greedy, r);
-        const uint32_t old =
-            __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == (uint32_t)(2 * p.G - 1))
-          __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (lane == 0 && g == 0) write_row_outputs(p, row, greedy, r);
     }
     __syncthreads();
     const float sc = sh.scale[wave];
-    __syncthreads();  // sh is rewritten by the next slice
 
     // ---- write the slice's probabilities once ----
     const int32_t c0 = 4 * q0;
@@ -353,29 +457,74 @@ __device__ __forceinline__ void process_slice(const RowStatsParams &p, int64_t r
       }
     }
   }
+  __syncthreads();  // sh is rewritten by the next slice
 }
+
+// Slice items of one workgroup: linear item index row * G + g.
+struct ItemCursor {
+  int64_t it, step, end;
+};
 
 template <int QPT, int PROBS, bool VEC>
 __global__ __launch_bounds__(kThreads, 4) void rowstats_kernel(RowStatsParams p) {
   __shared__ SliceShared sh;
+  // LDS stage of the slice (vector path): the next slice's HBM copies run
+  // while the current one waits for its row and writes its probs.
+  __shared__ float4 stage[VEC ? kThreads * QPT : 1];
   const int nwg = gridDim.x;
   // XCD-aware logical id: hardware workgroup b runs on XCD b % 8; logical
   // ids that share a row (consecutive ids) are placed on one XCD.
   int L = blockIdx.x;
   if (p.xcd_map) L = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+  // Row counters come in two banks used by alternate calls: this call counts
+  // in bank `parity` (zeroed by the previous call) and zeroes the other one
+  // for the next call, so no counter is ever reset while in use.
+  {
+    uint32_t *other = p.counters + (size_t)(p.parity ^ 1) * p.counter_stride;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < p.counter_stride;
+         i += (int64_t)nwg * kThreads)
+      other[i] = 0u;
+  }
+  // XCD-local synchronisation relies on workgroup b running on XCC b % 8
+  if (p.l2_sync && threadIdx.x == 0 && xcc_id() != blockIdx.x % 8) atomicOr(p.err_flag, 2u);
+  // Items: without probs, linear items L, L + nwg, ...; with probs, slice g
+  // of rows group, group + n_groups, ...
+  ItemCursor cur;
   if constexpr (PROBS == 0) {
-    const int64_t items = p.rows * (int64_t)p.G;
-    for (int64_t it = L; it < items; it += nwg) {
-      const int64_t row = it / p.G;
-      const int g = (int)(it - row * p.G);
-      process_slice<QPT, PROBS, VEC>(p, row, g, sh);
-    }
+    cur = {L, nwg, p.rows * (int64_t)p.G};
   } else {
     const int group = L / p.G;
-    const int g = L - group * p.G;
     if (group >= p.n_groups) return;
-    for (int64_t row = group; row < p.rows; row += p.n_groups)
-      process_slice<QPT, PROBS, VEC>(p, row, g, sh);
+    cur = {(int64_t)group * p.G + (L - group * p.G), (int64_t)p.n_groups * p.G,
+           p.rows * (int64_t)p.G};
+  }
+  if (cur.it >= cur.end) return;
+  constexpr int32_t span = kThreads * QPT;
+  if constexpr (VEC) {
+    const int64_t row = cur.it / p.G;
+    stage_slice_async<QPT, kThreads>(stage, p.logits + row * p.ld,
+                                     (int32_t)(cur.it - row * p.G) * span, p.vocab);
+  }
+  for (; cur.it < cur.end; cur.it += cur.step) {
+    const int64_t row = cur.it / p.G;
+    const int g = (int)(cur.it - row * p.G);
+    float4 v[QPT];
+    const float *next_xrow = nullptr;
+    int32_t next_q0 = 0;
+    if constexpr (VEC) {
+      stage_wait();
+      __syncthreads();
+      read_stage<QPT, kThreads>(stage, v);
+      const int64_t nx = cur.it + cur.step;
+      if (nx < cur.end) {
+        const int64_t nrow = nx / p.G;
+        next_xrow = p.logits + nrow * p.ld;
+        next_q0 = (int32_t)(nx - nrow * p.G) * span;
+      }
+    } else {
+      load_slice<QPT, kThreads, VEC>(p.logits + row * p.ld, g * span, p.vocab, v);
+    }
+    process_slice<QPT, PROBS, VEC>(p, row, g, sh, v, stage, next_xrow, next_q0);
   }
 }
 

@@ -27,7 +27,9 @@ struct TopKParams {
   float *out_vals;
   int64_t *out_idx;
   void *partials;       // [rows, G] records of topk_partial_bytes(K)
-  uint32_t *counters;   // [rows], zero between calls
+  uint32_t *counters;   // two banks of counter_stride words, alternated by call
+  int64_t counter_stride;
+  int32_t parity;       // bank this call counts in
 };
 
 // Per-slice record: double S, float m, pad, then K 64-bit keys.

@@ -160,7 +160,7 @@ __device__ void topk_slice(const TopKParams &p, int64_t row, int g, TopKShared &
   // ---- publish the slice record (wave 0 writes, lane 0 releases) ----
   const size_t rec_bytes = topk_partial_bytes(K);
   char *base = reinterpret_cast<char *>(p.partials) + (size_t)row * p.G * rec_bytes;
-  uint32_t *ctr = p.counters + row;
+  uint32_t *ctr = p.counters + (size_t)p.parity * p.counter_stride + row;
   if (wave == 0) {
     SliceRecord *rec = reinterpret_cast<SliceRecord *>(base + (size_t)g * rec_bytes);
     if (lane < K) record_keys(rec)[lane] = sh.tops[lane];
@@ -217,7 +217,6 @@ __device__ void topk_slice(const TopKParams &p, int64_t row, int g, TopKShared &
     p.out_idx[row * K + tid] = key64_col(key);
     p.out_vals[row * K + tid] = (float)(((double)s - (double)m) - logS);
   }
-  if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int QPT, bool VEC>
@@ -226,6 +225,13 @@ __global__ __launch_bounds__(kT, 4) void topk_kernel(TopKParams p) {
   const int nwg = gridDim.x;
   int L = blockIdx.x;
   if (p.xcd_map) L = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+  // this call counts in bank `parity`; zero the other bank for the next call
+  {
+    uint32_t *other = p.counters + (size_t)(p.parity ^ 1) * p.counter_stride;
+    for (int64_t i = (int64_t)blockIdx.x * kT + threadIdx.x; i < p.counter_stride;
+         i += (int64_t)nwg * kT)
+      other[i] = 0u;
+  }
   const int64_t items = p.rows * (int64_t)p.G;
   for (int64_t it = L; it < items; it += nwg) {
     const int64_t row = it / p.G;

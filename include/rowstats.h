@@ -34,8 +34,10 @@ typedef enum rowstats_status {
   ROWSTATS_ERR_K = -3,      /* K < 1, K > vocab or K > 64 */
   ROWSTATS_ERR_DTYPE = -4,  /* probs_dtype is not one of rowstats_probs_dtype */
   ROWSTATS_ERR_HIP = -5,    /* a HIP call failed (allocation, launch); see last_error */
-  ROWSTATS_ERR_COOP = -6,   /* the probs path needs every workgroup of a row
-                               resident at once and the device cannot hold them */
+  ROWSTATS_ERR_COOP = -6,   /* rowstats_run keeps the ceil(vocab / 2048) chunks of a
+                               row in co-resident waves at once and the device
+                               cannot hold them (vocab above about 4.2 million on
+                               one MI355X) */
   ROWSTATS_ERR_DEVICE = -7  /* a kernel flagged a failure (a bounded wait ran out);
                                reported by rowstats_check_device */
 } rowstats_status;

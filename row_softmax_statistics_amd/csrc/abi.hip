@@ -37,21 +37,27 @@ constexpr int kMaxDevices = 64;
 // the top-K key stores 0x7FFFFFFF - column: keep them all below 2^31.
 constexpr int64_t kMaxVocab = 0x7FFFFFFFLL - 65536;
 
-// Scratch of one device. Grow-only. The row counters form two banks of
-// counters_len / 2 words: a call counts in bank `parity` and its kernel
-// zeroes the other bank, which the next call uses.
+// Scratch of one device, grow-only.
+//  - row-statistics scratch: tagged member summaries and row results; zeroed
+//    when allocated, after which words are only ever told apart by the call
+//    epoch in their high half (epoch 0 never occurs);
+//  - top-K scratch: slice records and two banks of row counters of
+//    counters_len / 2 words; a call counts in bank `parity` and its kernel
+//    zeroes the other bank, which the next call uses.
 struct DeviceState {
   bool ready = false;
   int cus = 0;
   int resident[2][3] = {};  // row-stats blocks per CU by [vector path][probs dtype]
   int topk_resident[2] = {};
+  void *row_scratch = nullptr;
+  size_t row_scratch_bytes = 0;
+  uint32_t epoch = 0;            // epoch of the last row-statistics call
   void *partials = nullptr;
   size_t partials_bytes = 0;
   uint32_t *counters = nullptr;
   size_t counters_len = 0;
   uint32_t *err_flag = nullptr;
-  bool xcc_round_robin = false;  // workgroup b of a launch runs on XCC b % 8
-  int parity = 0;                // counter bank of the next call
+  int parity = 0;                // top-K counter bank of the next call
 };
 
 std::mutex g_mu;
@@ -61,28 +67,6 @@ __global__ void fill_zero_u32(uint32_t *p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0u;
-}
-
-// Records the XCC of each workgroup of a cooperative launch.
-__global__ void xcc_of_workgroups(int *out) {
-  if (threadIdx.x == 0) out[blockIdx.x] = (int)__builtin_amdgcn_s_getreg((20) | ((4 - 1) << 11));
-}
-
-// Whether workgroups are placed on XCCs round-robin by their index, the
-// placement the row-statistics kernel's XCD-local synchronisation needs.
-bool probe_xcc_round_robin(int cus) {
-  const int n = 8 * (cus / 8 > 0 ? cus / 8 : 1);
-  int *d = nullptr;
-  if (hipMalloc(&d, n * sizeof(int)) != hipSuccess) return false;
-  void *args[] = {&d};
-  bool ok = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&xcc_of_workgroups), dim3(n),
-                                       dim3(64), args, 0, nullptr) == hipSuccess;
-  int *h = new int[n];
-  ok = ok && hipMemcpy(h, d, n * sizeof(int), hipMemcpyDeviceToHost) == hipSuccess;
-  for (int i = 0; ok && i < n; ++i) ok = (h[i] == i % 8);
-  delete[] h;
-  (void)hipFree(d);
-  return ok;
 }
 
 hipError_t zero_async(uint32_t *p, size_t n, hipStream_t s) {
@@ -116,7 +100,6 @@ int device_state(DeviceState **out) {
     if (e != hipSuccess) return fail_hip(e, "hipMalloc(error flag)");
     e = hipMemset(d.err_flag, 0, sizeof(uint32_t));
     if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
-    d.xcc_round_robin = probe_xcc_round_robin(d.cus);
     d.ready = true;
   }
   *out = &d;
@@ -151,6 +134,26 @@ int ensure_scratch(DeviceState &d, size_t partial_bytes, size_t counters, hipStr
     e = zero_async(d.counters, cap, s);
     if (e != hipSuccess) return fail_hip(e, "zeroing counters");
   }
+  return ROWSTATS_OK;
+}
+
+// Row-statistics scratch of at least `bytes`; a new buffer is zeroed.
+int ensure_row_scratch(DeviceState &d, size_t bytes, hipStream_t s) {
+  if (bytes <= d.row_scratch_bytes) return ROWSTATS_OK;
+  hipError_t e;
+  if (d.row_scratch) {
+    e = hipFree(d.row_scratch);
+    if (e != hipSuccess) return fail_hip(e, "hipFree(row scratch)");
+    d.row_scratch = nullptr;
+    d.row_scratch_bytes = 0;
+  }
+  size_t cap = bytes + bytes / 4;
+  cap = (cap + 255) & ~(size_t)255;
+  e = hipMalloc(&d.row_scratch, cap);
+  if (e != hipSuccess) return fail_hip(e, "hipMalloc(row scratch)");
+  d.row_scratch_bytes = cap;
+  e = zero_async(reinterpret_cast<uint32_t *>(d.row_scratch), cap / 4, s);
+  if (e != hipSuccess) return fail_hip(e, "zeroing row scratch");
   return ROWSTATS_OK;
 }
 
@@ -201,9 +204,7 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
   p.ld = row_stride;
   p.rows = rows;
   p.vocab = (int32_t)vocab;
-  p.nq = (int32_t)((vocab + 3) / 4);
-  p.nq_full = (int32_t)(vocab / 4);
-  p.G = (p.nq + kRowThreads * kQPT - 1) / (kRowThreads * kQPT);
+  p.C = (int32_t)((vocab + kChunkCols - 1) / kChunkCols);
   p.vec_ok = ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) && (row_stride % 4 == 0) &&
              (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(probs) & 7) == 0);
   p.temps = temps;
@@ -214,43 +215,36 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
   p.entropy = entropy;
   p.probs = probs;
 
-  const int64_t resident = (int64_t)d->resident[p.vec_ok][probs_dtype] * d->cus;
-  if (resident < 1) return fail(ROWSTATS_ERR_HIP, "row-stats kernel cannot be resident");
-  int64_t grid;
-  if (probs_dtype == ROWSTATS_PROBS_NONE) {
-    const int64_t items = rows * (int64_t)p.G;
-    grid = items < resident ? items : resident;
-    p.n_groups = 0;
-    p.xcd_map = (grid % 8 == 0);
-    // an ordinary launch may place workgroups off XCC b % 8 (seen right
-    // after other kernels), and this path never waits: agent scope
-    p.l2_sync = 0;
-  } else {
-    int64_t groups = resident / p.G;
-    if (groups < 1)
-      return fail(ROWSTATS_ERR_COOP,
-                  "vocab %lld needs %d co-resident workgroups per row, the device holds %lld",
-                  (long long)vocab, p.G, (long long)resident);
-    if (groups > rows) groups = rows;
-    if (groups >= 8) groups -= groups % 8;
-    p.n_groups = (int32_t)groups;
-    grid = groups * p.G;
-    p.xcd_map = (groups % 8 == 0);
-    // the cooperative launch places workgroup b on XCC b % 8 (probed at
-    // init, checked by every workgroup), so each row's group shares an L2
-    p.l2_sync = d->xcc_round_robin && p.xcd_map;
+  // Every wave of the launch is resident (cooperative launch); the C waves
+  // of a row's group keep their chunks in registers until the row is
+  // merged, so a group must fit.
+  constexpr int kWavesPerBlock = kRowThreads / 64;
+  const int64_t waves = (int64_t)d->resident[p.vec_ok][probs_dtype] * d->cus * kWavesPerBlock;
+  if (waves < 1) return fail(ROWSTATS_ERR_HIP, "row-stats kernel cannot be resident");
+  if (p.C > waves)
+    return fail(ROWSTATS_ERR_COOP,
+                "vocab %lld needs %d co-resident waves per row, the device holds %lld",
+                (long long)vocab, p.C, (long long)waves);
+  int64_t groups = waves / p.C;
+  if (groups > rows) groups = rows;
+  p.n_groups = (int32_t)groups;
+  const int64_t grid = (groups * p.C + kWavesPerBlock - 1) / kWavesPerBlock;
+
+  const size_t tuple_bytes = (size_t)rows * p.C * kTupleBytes;
+  const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
+  if ((rc = ensure_row_scratch(*d, tuple_bytes + rowres_bytes, s))) return rc;
+  if (++d->epoch == 0) {
+    // the epoch wrapped: clear every tag it could still match
+    hipError_t e = zero_async(reinterpret_cast<uint32_t *>(d->row_scratch), d->row_scratch_bytes / 4, s);
+    if (e != hipSuccess) return fail_hip(e, "zeroing row scratch");
+    d->epoch = 1;
   }
-  if ((rc = ensure_scratch(*d, (size_t)rows * p.G * kSliceTupleWords * sizeof(uint64_t),
-                          2 * (size_t)rows, s)))
-    return rc;
-  p.partials = reinterpret_cast<uint64_t *>(d->partials);
-  p.counters = d->counters;
-  p.counter_stride = (int64_t)(d->counters_len / 2);
-  p.parity = d->parity;
+  p.epoch = d->epoch;
+  p.tuples = reinterpret_cast<uint64_t *>(d->row_scratch);
+  p.rowres = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(d->row_scratch) + tuple_bytes);
   p.err_flag = d->err_flag;
   hipError_t e = rowstats_launch(p, probs_dtype, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
-  d->parity ^= 1;
   return ROWSTATS_OK;
 }
 
@@ -319,9 +313,7 @@ int rowstats_check_device(void *stream) {
   e = hipMemcpy(&flag, d->err_flag, sizeof flag, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpy(error flag)");
   if (flag == 0) return ROWSTATS_OK;
-  // a workgroup ran off its expected XCC: stop relying on the placement
-  if (flag & 2u) d->xcc_round_robin = false;
-  // a wait ran out: counters of that call may be left non-zero
+  // a wait ran out: top-K counters of that call may be left non-zero
   e = hipMemset(d->err_flag, 0, sizeof(uint32_t));
   if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
   if (d->counters) {
@@ -329,8 +321,7 @@ int rowstats_check_device(void *stream) {
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail_hip(e, "zeroing counters");
   }
-  return fail(ROWSTATS_ERR_DEVICE, "a kernel flagged %s (flag %u)",
-              (flag & 2u) ? "a workgroup off its expected XCD" : "an inter-workgroup wait that ran out",
+  return fail(ROWSTATS_ERR_DEVICE, "a kernel flagged an inter-workgroup wait that ran out (flag %u)",
               flag);
 }
 
@@ -344,6 +335,7 @@ int rowstats_release(void) {
     DeviceState &d = g_dev[dev];
     if (!d.ready) continue;
     if ((e = hipSetDevice(dev)) != hipSuccess) return fail_hip(e, "hipSetDevice");
+    if (d.row_scratch) (void)hipFree(d.row_scratch);
     if (d.partials) (void)hipFree(d.partials);
     if (d.counters) (void)hipFree(d.counters);
     if (d.err_flag) (void)hipFree(d.err_flag);

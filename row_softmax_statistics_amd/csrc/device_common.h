@@ -31,9 +31,10 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     }
     const uint64_t p0 = (uint64_t)Philox::M0 * c0;
     const uint64_t p1 = (uint64_t)Philox::M1 * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    // three-input xor in one instruction (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
     const uint32_t n1 = (uint32_t)p1;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     const uint32_t n3 = (uint32_t)p0;
     c0 = n0;
     c1 = n1;
@@ -239,6 +240,21 @@ __device__ __forceinline__ uint32_t fp16_rne_bits(float p) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p);
 }
 
+// Two values rounded to nearest-even and packed (a in the low half), with
+// one gfx950 conversion instruction (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32;
+// round-to-nearest-even is the default rounding mode, denormals are kept).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t pack_fp16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
 // ---------------------------------------------------------------------------
 // Wave reductions with DPP inside 16-lane rows and lane swaps across rows.
 // ---------------------------------------------------------------------------
@@ -263,61 +279,62 @@ __device__ __forceinline__ uint32_t lane_exchange(uint32_t v) {
   else return xor_lanes(v, STEP);
 }
 
+// One reduction step across lanes STEP apart (STEP = 1..32, a power of 2):
+// every lane ends with op(own, partner), partner = lane ^ STEP for STEP <= 8
+// (DPP inside 16-lane rows). For 16 and 32 the gfx950 permlane swaps
+// exchange whole rows / halves in the VALU: after v_permlane16_swap of two
+// copies of v, one copy holds v and the other the value 16 lanes away in
+// every lane (which copy is which depends on the row), so op of the two
+// copies is the step's result for a commutative op.
+template <int STEP, class T, class Op>
+__device__ __forceinline__ T reduce_step(T v, Op op) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (STEP <= 8) {
+    T o;
+    if constexpr (sizeof(T) == 4) {
+      o = __builtin_bit_cast(T, lane_exchange<STEP>(__builtin_bit_cast(uint32_t, v)));
+    } else {
+      const uint64_t b = __builtin_bit_cast(uint64_t, v);
+      const uint32_t lo = lane_exchange<STEP>((uint32_t)b), hi = lane_exchange<STEP>((uint32_t)(b >> 32));
+      o = __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+    }
+    return op(v, o);
+  } else {
+    auto swap = [](uint32_t x) {
+      if constexpr (STEP == 16) return __builtin_amdgcn_permlane16_swap(x, x, false, false);
+      else return __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    };
+    if constexpr (sizeof(T) == 4) {
+      const auto r = swap(__builtin_bit_cast(uint32_t, v));
+      return op(__builtin_bit_cast(T, (uint32_t)r[0]), __builtin_bit_cast(T, (uint32_t)r[1]));
+    } else {
+      const uint64_t b = __builtin_bit_cast(uint64_t, v);
+      const auto lo = swap((uint32_t)b), hi = swap((uint32_t)(b >> 32));
+      const T a = __builtin_bit_cast(T, ((uint64_t)(uint32_t)hi[0] << 32) | (uint32_t)lo[0]);
+      const T c = __builtin_bit_cast(T, ((uint64_t)(uint32_t)hi[1] << 32) | (uint32_t)lo[1]);
+      return op(a, c);
+    }
+  }
+}
+
 // Applies `op` over groups of WIDTH lanes (WIDTH = 2..64, a power of 2);
 // every lane ends with its group's result. Narrow widths reduce few items
 // (the items sit in the first lanes) in fewer dependent steps.
 template <int WIDTH, class T, class Op>
 __device__ __forceinline__ T group_allreduce(T v, Op op) {
-  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
-#define ROWSTATS_GSTEP(S)                                                         \
-  if constexpr (WIDTH > S) {                                                      \
-    T o;                                                                          \
-    if constexpr (sizeof(T) == 4) {                                               \
-      o = __builtin_bit_cast(T, lane_exchange<S>(__builtin_bit_cast(uint32_t, v))); \
-    } else {                                                                      \
-      uint64_t b = __builtin_bit_cast(uint64_t, v);                               \
-      uint32_t lo = lane_exchange<S>((uint32_t)b), hi = lane_exchange<S>((uint32_t)(b >> 32)); \
-      o = __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);                       \
-    }                                                                             \
-    v = op(v, o);                                                                 \
-  }
-  ROWSTATS_GSTEP(1)
-  ROWSTATS_GSTEP(2)
-  ROWSTATS_GSTEP(4)
-  ROWSTATS_GSTEP(8)
-  ROWSTATS_GSTEP(16)
-  ROWSTATS_GSTEP(32)
-#undef ROWSTATS_GSTEP
+  if constexpr (WIDTH > 1) v = reduce_step<1>(v, op);
+  if constexpr (WIDTH > 2) v = reduce_step<2>(v, op);
+  if constexpr (WIDTH > 4) v = reduce_step<4>(v, op);
+  if constexpr (WIDTH > 8) v = reduce_step<8>(v, op);
+  if constexpr (WIDTH > 16) v = reduce_step<16>(v, op);
+  if constexpr (WIDTH > 32) v = reduce_step<32>(v, op);
   return v;
 }
 
-// Applies `op` over the 64 lanes; every lane ends with the result. The lane
-// pairing differs per step (xor, mirror) but each step merges two disjoint
-// halves of equal size, so the result is the full reduction.
+// Applies `op` over the 64 lanes; every lane ends with the result.
 template <class T, class Op>
 __device__ __forceinline__ T wave_allreduce(T v, Op op) {
-  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
-#define ROWSTATS_STEP(S)                                                          \
-  {                                                                               \
-    T o;                                                                          \
-    if constexpr (sizeof(T) == 4) {                                               \
-      uint32_t b = __builtin_bit_cast(uint32_t, v);                               \
-      o = __builtin_bit_cast(T, lane_exchange<S>(b));                             \
-    } else {                                                                      \
-      uint64_t b = __builtin_bit_cast(uint64_t, v);                               \
-      uint32_t lo = lane_exchange<S>((uint32_t)b), hi = lane_exchange<S>((uint32_t)(b >> 32)); \
-      o = __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);                       \
-    }                                                                             \
-    v = op(v, o);                                                                 \
-  }
-  ROWSTATS_STEP(1)
-  ROWSTATS_STEP(2)
-  ROWSTATS_STEP(4)
-  ROWSTATS_STEP(8)
-  ROWSTATS_STEP(16)
-  ROWSTATS_STEP(32)
-#undef ROWSTATS_STEP
-  return v;
+  return group_allreduce<64>(v, op);
 }
 
 struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };

@@ -6,27 +6,29 @@
 
 namespace rowstats {
 
-// Quads (4 columns) per thread held in registers by the row-statistics
-// kernel; a slice is 512 threads x kQPT quads = 16384 columns.
-constexpr int kQPT = 8;
+// Row-statistics work split: a row is cut into chunks of kChunkCols columns;
+// one wave reduces one chunk at a time, each lane holding kWaveQuads quads
+// (4 columns) in registers. Workgroups of kRowThreads threads only group
+// waves for launch and LDS; waves exchange results through global scratch.
+constexpr int kWaveQuads = 8;
 constexpr int kRowThreads = 512;
-constexpr int kSliceCols = kRowThreads * kQPT * 4;
+constexpr int kChunkQuads = 64 * kWaveQuads;  // 512
+constexpr int kChunkCols = 4 * kChunkQuads;   // 2048
 
-// Words of global scratch per slice tuple (see the kernel).
-constexpr int kSliceTupleWords = 5;
+// Global scratch per (row, member wave): eight tagged 64-bit words.
+constexpr int kTupleBytes = 64;
+// Per row: two tagged words (row maximum, 1 / sum) read by the probs writers.
+constexpr int kRowResultBytes = 16;
 
 struct RowStatsParams {
   const float *logits;
   int64_t ld;
   int64_t rows;
   int32_t vocab;
-  int32_t G;          // slices per row
-  int32_t nq;         // quads per row, ceil(vocab / 4)
-  int32_t nq_full;    // quads entirely inside the row, vocab / 4
-  int32_t n_groups;   // probs path: rows processed concurrently
-  int32_t vec_ok;     // logits and probs aligned, ld % 4 == 0, vocab % 4 == 0
-  int32_t xcd_map;    // grid is a multiple of 8 with G | grid / 8
-  int32_t l2_sync;    // the workgroups of every row share one XCD (see the kernel)
+  int32_t C;          // chunks per row, ceil(vocab / kChunkCols): the waves of a group
+  int32_t n_groups;   // groups, each reducing rows group, group + n_groups, ...
+  int32_t vec_ok;     // 16-byte aligned rows, ld % 4 == 0, vocab % 4 == 0, probs 8-byte aligned
+  uint32_t epoch;     // tag of this call's scratch words (never 0)
   const float *temps;
   int64_t canvas_len;
   uint64_t seed;
@@ -34,10 +36,8 @@ struct RowStatsParams {
   int64_t *sample;
   float *entropy;
   void *probs;
-  uint64_t *partials; // [rows, G] slice tuples of kSliceTupleWords words
-  uint32_t *counters; // two banks of counter_stride words (see the kernel)
-  int64_t counter_stride;
-  int32_t parity;     // bank this call counts in
+  uint64_t *tuples;   // [rows, C] tuples of kTupleBytes
+  uint64_t *rowres;   // [rows] row results of kRowResultBytes
   uint32_t *err_flag;
 };
 

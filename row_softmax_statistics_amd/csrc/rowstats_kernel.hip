@@ -6,20 +6,26 @@
 // the probabilities are written once) and sample_row_stats /
 // sample_row_stats_reference (the statistics and the greedy rule).
 //
-// Work split. A row of `vocab` columns is cut into G slices of 16384
-// columns; one 512-thread workgroup owns one slice at a time and keeps it in
-// registers (8 float4 per thread), so every logit is read from HBM once.
-// Each wave reduces its 2048 columns on its own to a tuple
+// Work split. A row is cut into C chunks of 2048 columns, and a group of C
+// member waves reduces one row at a time, one chunk each; each group walks
+// its own rows. A wave keeps its chunk in registers (8 float4 per lane), so
+// each logit is read from HBM once, and waves never meet at a barrier.
+// While a wave reduces one chunk, its next chunk is copied from HBM into
+// the wave's LDS buffer (buffer_load ... lds).
+//
+// A wave reduces its chunk to a summary relative to its own maximum m:
 //   (m, lowest column of m, S = sum 2^32 exp(s - m),
-//    W = sum 2^32 exp(s - m) (s - m), best perturbed score z, its column),
-// the slice tuple is their merge, and the row tuple the merge of its G
-// slice tuples, exchanged through global scratch with agent-scope atomics.
-//   - Without probs: the last slice of a row to arrive merges the row and
-//     writes its outputs.
-//   - With probs: the grid is persistent and cooperative (all workgroups
-//     resident); the G workgroups of a row wait for each other's tuples,
-//     each merges them and rescales its register-resident exp values into
-//     probabilities, so the probs are written once and logits never re-read.
+//    W = sum 2^32 exp(s - m) (s - m), best perturbed score z, its column)
+// and stores it in global scratch as eight 64-bit words, each carrying the
+// call's epoch in its high half; stores and loads of these words are
+// device-scope coherent and 64-bit words are never torn, so a word that
+// shows the current epoch is final. One member per row (the merger,
+// rotating over the members) polls the row's summaries one chunk later,
+// merges them, writes the row's argmax, sample and entropy, and publishes
+// (m, 1 / S) of the row. Every member waits for that row result two chunks
+// later: with probs it then writes its chunk's probabilities from the exp
+// values it kept in registers, so the exchange overlaps two chunks of work.
+// The launch is cooperative (every wave resident), so each wait ends.
 //
 // Gumbel sample (T > 0). The wave's argmax a gives a lower bound
 // zlb = s_a + g_a on its best perturbed score. A column can reach zlb only
@@ -39,190 +45,154 @@ namespace rowstats {
 
 constexpr int kThreads = kRowThreads;
 constexpr int kWaves = kThreads / kWave;
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kQ = kWaveQuads;
+// Polls of one wait before it gives up and flags the call (about a second);
+// once any wait has given up, every later wait of the call gives up at once.
+constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr float kLog2e = 1.44269504088896340736f;
 // 2^32 exp(-22.8739) = 0.49998, lowered for the 2^-13 error of -log u and
 // the rounding of e: a quad whose exp values are all below kQuadSkip / a,
 // a = -log u of the bound's word, cannot reach the bound.
 constexpr float kQuadSkip = 0.4993f;
 constexpr float kTestMargin = 1.0f + 0x1p-10f;
+// Cache-policy bit sc1: a device-scope coherent load or store (the CU's L1
+// is bypassed and the access is coherent across XCDs).
+constexpr int kDevScope = 16;
 
-// A wave, slice or row summary relative to its own maximum m.
+typedef __attribute__((address_space(3))) void *LdsPtr;
+
+// A wave, chunk or row summary relative to its own maximum m.
 struct Tuple {
   float m;
   int32_t am;
   double S;
   double W;
-  double zb;
-  int32_t zc;
+  double zb;  // best perturbed score z = s + g of the summarised columns
+  int32_t zc;  // its column
+  int32_t zx;  // 1: zb is exact (fp64); 0: fp32 estimate, within 2^-9 of exact
 };
 
-struct SliceShared {
-  Tuple wave[kWaves];
-  float scale[kWaves];
-};
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Merge of items 0..n-1 of a wave (lane i takes i, i + 64, ...; n <= WIDTH
-// unless WIDTH is 64). The result is valid in every lane of the first WIDTH.
-// The factors exp(m_i - m) are fp32 (relative error near 1e-7); the sums
-// stay fp64.
-template <int WIDTH, class Get>
-__device__ __forceinline__ Tuple merge_tuples(int n, Get get) {
-  const int lane = threadIdx.x & (kWave - 1);
-  float m = -INFINITY;
-  for (int i = lane; i < n; i += kWave) m = fmaxf(m, get(i).m);
-  m = group_allreduce<WIDTH>(m, MaxF());
-  double S = 0.0, W = 0.0, zb = -INFINITY;
-  int32_t am = INT_MAX;
-  for (int i = lane; i < n; i += kWave) {
-    const Tuple t = get(i);
-    if (t.S > 0.0) {
-      const float dm = fmaxf(t.m - m, -FLT_MAX);  // <= 0, exact when the maxima are close
-      const double f = (double)__builtin_amdgcn_exp2f(dm * kLog2e);
-      S += t.S * f;
-      W += f * (t.W + t.S * (double)dm);
-    }
-    if (t.m == m) am = min(am, t.am);
-    zb = fmax(zb, t.zb);
-  }
-  Tuple r;
-  r.m = m;
-  r.S = group_allreduce<WIDTH>(S, SumD());
-  r.W = group_allreduce<WIDTH>(W, SumD());
-  r.am = group_allreduce<WIDTH>(am, MinI());
-  r.zb = group_allreduce<WIDTH>(zb, MaxD());
-  int32_t zc = INT_MAX;
-  for (int i = lane; i < n; i += kWave) {
-    const Tuple t = get(i);
-    if (t.zb == r.zb) zc = min(zc, t.zc);
-  }
-  r.zc = group_allreduce<WIDTH>(zc, MinI());
-  return r;
-}
-
-// Row merge of G slice tuples with the narrowest lane width that holds them.
-template <class Get>
-__device__ __forceinline__ Tuple merge_slices(int G, Get get) {
-  if (G <= 8) return merge_tuples<8>(G, get);
-  if (G <= 16) return merge_tuples<16>(G, get);
-  if (G <= 32) return merge_tuples<32>(G, get);
-  return merge_tuples<64>(G, get);
-}
-
-// Slice tuples in global scratch, five 64-bit words each, and one counter
-// per row. Two coherence modes:
-//   XCD-local (p.l2_sync): every workgroup of a row runs on one XCD (the
-//     launch places them so and each workgroup checks its XCC id), so the
-//     XCD's L2 is their point of coherence: stores write through L1 into
-//     L2, atomics execute in L2 (the counter is polled with an atomic), and
-//     a reader invalidates its CU's L1 before loading tuples. Round trips
-//     stay on-chip instead of queueing behind the HBM stream.
-//   agent: relaxed agent-scope atomics, each coherent across XCDs on its own.
-// Either way a writer waits for its stores before counting the slice in.
-constexpr int kTupleWords = kSliceTupleWords;
-constexpr int kL1Bypass = 1;  // sc0 cache-policy bit
-
-struct SyncScratch {
-  Rsrc tuples, counters;
-  uint64_t *tuple_ptr;
-  uint32_t *counter_ptr;
-  bool l2;
-};
-
-__device__ __forceinline__ SyncScratch sync_scratch(const RowStatsParams &p) {
-  SyncScratch s;
-  s.tuple_ptr = p.partials;
-  s.tuples = make_rsrc(p.partials, (uint32_t)(p.rows * p.G * kTupleWords * 8));
-  s.counters = make_rsrc(p.counters + (size_t)p.parity * p.counter_stride, (uint32_t)(p.rows * 4));
-  s.counter_ptr = p.counters + (size_t)p.parity * p.counter_stride;
-  s.l2 = p.l2_sync != 0;
-  return s;
-}
-
-__device__ __forceinline__ uint64_t tuple_word(const Tuple &t, int k) {
-  switch (k) {
-    case 0: return (uint64_t)__float_as_uint(t.m) | ((uint64_t)(uint32_t)t.am << 32);
-    case 1: return (uint64_t)__double_as_longlong(t.S);
-    case 2: return (uint64_t)__double_as_longlong(t.W);
-    case 3: return (uint64_t)__double_as_longlong(t.zb);
-    default: return (uint64_t)(uint32_t)t.zc;
-  }
-}
-
-// word index of tuple (row, g), word k
-__device__ __forceinline__ uint32_t tuple_index(const RowStatsParams &p, int64_t row, int g, int k) {
-  return (uint32_t)((row * p.G + g) * kTupleWords + k);
-}
-
-// Drops this CU's L1 lines so that later loads read the XCD's L2.
-__device__ __forceinline__ void l1_invalidate(const SyncScratch &s) {
-  if (s.l2) __asm__ volatile("buffer_inv sc0" ::: "memory");
-}
-
-__device__ __forceinline__ Tuple load_tuple(const SyncScratch &s, uint32_t w0) {
-  uint64_t w[kTupleWords];
-#pragma unroll
-  for (int k = 0; k < kTupleWords; ++k) {
-    if (s.l2) {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(s.tuples, 8u * (w0 + k), 0, kL1Bypass);
-      w[k] = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
-    } else {
-      w[k] = __hip_atomic_load(s.tuple_ptr + w0 + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+__device__ __forceinline__ Tuple empty_tuple() {
   Tuple t;
-  t.m = __uint_as_float((uint32_t)w[0]);
-  t.am = (int32_t)(uint32_t)(w[0] >> 32);
-  t.S = __longlong_as_double((long long)w[1]);
-  t.W = __longlong_as_double((long long)w[2]);
-  t.zb = __longlong_as_double((long long)w[3]);
-  t.zc = (int32_t)(uint32_t)w[4];
+  t.m = -INFINITY;
+  t.am = INT_MAX;
+  t.S = 0.0;
+  t.W = 0.0;
+  t.zb = -INFINITY;
+  t.zc = INT_MAX;
+  t.zx = 1;
   return t;
 }
 
-__device__ __forceinline__ uint32_t counter_add(const SyncScratch &s, int64_t row) {
-  if (s.l2) return (uint32_t)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, s.counters, 4u * (uint32_t)row, 0, 0);
-  return __hip_atomic_fetch_add(s.counter_ptr + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint32_t counter_load(const SyncScratch &s, int64_t row) {
-  if (s.l2) {
-    // add an opaque zero: an add of a known 0 would be folded into a load,
-    // which may hit a stale L1 line; the atomic always reads the L2
-    uint32_t zero = 0;
-    __asm__ volatile("" : "+v"(zero));
-    return __hip_atomic_fetch_add(s.counter_ptr + row, zero, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+// Adds summary t, rescaled from its maximum to m, into (S, W). The factors
+// exp(t.m - m) are fp32 (relative error near 1e-7); the sums are fp64.
+__device__ __forceinline__ void add_rescaled(const Tuple &t, float m, double &S, double &W) {
+  if (t.S > 0.0) {
+    const float dm = fmaxf(t.m - m, -FLT_MAX);  // <= 0
+    const double f = (double)__builtin_amdgcn_exp2f(dm * kLog2e);
+    S += t.S * f;
+    W += f * (t.W + t.S * (double)dm);
   }
-  return __hip_atomic_load(s.counter_ptr + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Publishes a slice tuple (lanes 0..4 of the calling wave store one word
-// each), waits until the stores are done, then counts the slice in. Returns
-// the counter value before the add, in every lane.
-__device__ __forceinline__ uint32_t publish_tuple(const SyncScratch &s, uint32_t w0, const Tuple &t,
-                                                  int64_t row) {
-  const int lane = threadIdx.x & (kWave - 1);
-  if (lane < kTupleWords) {
-    const uint64_t v = tuple_word(t, lane);
-    if (s.l2) {
-      const u32x2 pk = {(uint32_t)v, (uint32_t)(v >> 32)};
-      __builtin_amdgcn_raw_buffer_store_b64(pk, s.tuples, 8u * (w0 + lane), 0, 0);
-    } else {
-      __hip_atomic_store(s.tuple_ptr + w0 + lane, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+// Merge of two summaries.
+__device__ __forceinline__ Tuple combine(const Tuple &a, const Tuple &b) {
+  Tuple r;
+  r.m = fmaxf(a.m, b.m);
+  r.S = 0.0;
+  r.W = 0.0;
+  add_rescaled(a, r.m, r.S, r.W);
+  add_rescaled(b, r.m, r.S, r.W);
+  r.am = min(a.m == r.m ? a.am : INT_MAX, b.m == r.m ? b.am : INT_MAX);
+  r.zb = fmax(a.zb, b.zb);
+  r.zc = min(a.zb == r.zb ? a.zc : INT_MAX, b.zb == r.zb ? b.zc : INT_MAX);
+  r.zx = a.zx & b.zx;
+  return r;
+}
+
+// Merge of the summaries held by the 64 lanes; every lane gets the result.
+__device__ __forceinline__ Tuple wave_merge(const Tuple &t) {
+  Tuple r;
+  r.m = wave_allreduce(t.m, MaxF());
+  double S = 0.0, W = 0.0;
+  add_rescaled(t, r.m, S, W);
+  r.S = wave_allreduce(S, SumD());
+  r.W = wave_allreduce(W, SumD());
+  r.am = wave_allreduce(t.m == r.m ? t.am : INT_MAX, MinI());
+  r.zb = wave_allreduce(t.zb, MaxD());
+  r.zc = wave_allreduce(t.zb == r.zb ? t.zc : INT_MAX, MinI());
+  r.zx = wave_allreduce(t.zx, MinI());
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Tagged scratch words. A member's summary is eight 64-bit words, payload in
+// the low half and the epoch in the high half: m, argmax, S (fp32), W (fp32),
+// the two halves of the best score, its column, the score's exactness flag.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ Rsrc tuple_rsrc(const RowStatsParams &p, int64_t row) {
+  return make_rsrc(p.tuples + row * p.C * (kTupleBytes / 8), (uint32_t)(p.C * kTupleBytes));
+}
+
+__device__ __forceinline__ Rsrc rowres_rsrc(const RowStatsParams &p, int64_t row) {
+  return make_rsrc(p.rowres + row * (kRowResultBytes / 8), (uint32_t)kRowResultBytes);
+}
+
+__device__ __forceinline__ uint32_t tuple_payload(const Tuple &t, int k) {
+  switch (k) {
+    case 0: return __float_as_uint(t.m);
+    case 1: return (uint32_t)t.am;
+    case 2: return __float_as_uint((float)t.S);
+    case 3: return __float_as_uint((float)t.W);
+    case 4: return (uint32_t)(uint64_t)__double_as_longlong(t.zb);
+    case 5: return (uint32_t)((uint64_t)__double_as_longlong(t.zb) >> 32);
+    case 6: return (uint32_t)t.zc;
+    default: return (uint32_t)t.zx;
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  uint32_t old = 0;
-  if (lane == 0) old = counter_add(s, row);
-  return (uint32_t)__shfl((int)old, 0, kWave);
 }
 
-// XCC (XCD) id of the executing workgroup.
-__device__ __forceinline__ uint32_t xcc_id() {
-  return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11));  // HW_REG_XCC_ID[3:0]
+// Lanes 0..3 store two tagged words each (one 16-byte store instruction).
+__device__ __forceinline__ void publish_tuple(const Rsrc &r, int member, const Tuple &t,
+                                              uint32_t epoch) {
+  const int lane = lane_id();
+  if (lane < 4) {
+    const u32x4 v = {tuple_payload(t, 2 * lane), epoch, tuple_payload(t, 2 * lane + 1), epoch};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (uint32_t)(member * kTupleBytes + 16 * lane), 0,
+                                           kDevScope);
+  }
+}
+
+// Reads member `member`'s summary; true when all eight words are this call's.
+__device__ __forceinline__ bool read_tuple(const Rsrc &r, int member, uint32_t epoch, Tuple &t) {
+  const uint32_t off = (uint32_t)(member * kTupleBytes);
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDevScope);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kDevScope);
+  const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(r, off + 32, 0, kDevScope);
+  const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, off + 48, 0, kDevScope);
+  t.m = __uint_as_float(a[0]);
+  t.am = (int32_t)a[2];
+  t.S = (double)__uint_as_float(b[0]);
+  t.W = (double)__uint_as_float(b[2]);
+  t.zb = __longlong_as_double((long long)((uint64_t)c[0] | ((uint64_t)c[2] << 32)));
+  t.zc = (int32_t)d[0];
+  t.zx = (int32_t)d[2];
+  return ((a[1] == epoch) & (a[3] == epoch) & (b[1] == epoch) & (b[3] == epoch) &
+          (c[1] == epoch) & (c[3] == epoch) & (d[1] == epoch) & (d[3] == epoch)) != 0;
+}
+
+// The row result read by the probs writers: (m, 1 / S), both tagged.
+__device__ __forceinline__ u32x4 load_rowres(const RowStatsParams &p, int64_t row) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rowres_rsrc(p, row), 0u, 0, kDevScope);
+}
+__device__ __forceinline__ bool rowres_ready(const u32x4 &v, uint32_t epoch) {
+  return ((v[1] == epoch) & (v[3] == epoch)) != 0;
+}
+
+// Whether some wait of this call has already given up.
+__device__ __forceinline__ bool call_failed(const RowStatsParams &p) {
+  return __hip_atomic_load(p.err_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
 
 __device__ __forceinline__ void write_row_outputs(const RowStatsParams &p, int64_t row,
@@ -234,37 +204,227 @@ __device__ __forceinline__ void write_row_outputs(const RowStatsParams &p, int64
   p.entropy[row] = (float)H;
 }
 
-// Everything one workgroup does for slice g of `row`. On entry v holds the
-// slice's raw logits; `stage` (vector path) still holds them too and is
-// refilled with the next slice (`next_xrow`, `next_q0`) once no wave reads
-// it any more.
-template <int QPT, int PROBS, bool VEC>
-__device__ __forceinline__ void process_slice(const RowStatsParams &p, int64_t row, int g,
-                                              SliceShared &sh, float4 (&v)[QPT], float4 *stage,
-                                              const float *next_xrow, int32_t next_q0) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+// Exact perturbed score of column c of `row`: s from the raw logit (re-read
+// from HBM), g in fp64.
+__device__ __forceinline__ double exact_score(const RowStatsParams &p, int64_t row, double rtc,
+                                              int32_t c) {
+  const float s = scale(p.logits[row * p.ld + c], rtc);
+  const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, (uint32_t)(uint64_t)row,
+                                (uint32_t)((uint64_t)row >> 32), (uint32_t)p.seed,
+                                (uint32_t)(p.seed >> 32));
+  return (double)s + gumbel_of_word(pick(w, c & 3));
+}
+
+// The merger's work for `row`: waits for the C member summaries, merges
+// them, writes the row's outputs and, with probs, the row result.
+// The sample is the member winner with the largest score; when another
+// member's score is within 2^-8 of it (both may be fp32 estimates, each
+// within 2^-9), the close ones are rescored exactly and the largest exact
+// score wins, ties to the lower column.
+template <int PROBS>
+__device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) {
+  const Rsrc r = tuple_rsrc(p, row);
+  const int lane = lane_id();
+  Tuple acc = empty_tuple();
+  double b1 = -INFINITY, b2 = -INFINITY;  // this lane's best and second-best member scores
+  int32_t c1 = INT_MAX, x1 = 1;
+  for (int i = lane; i < p.C; i += kWave) {
+    Tuple t;
+    uint32_t spins = 0;
+    while (!read_tuple(r, i, p.epoch, t)) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit || call_failed(p)) {
+        atomicOr(p.err_flag, 1u);
+        break;
+      }
+    }
+    acc = combine(acc, t);
+    if (t.zb > b1 || (t.zb == b1 && t.zc < c1)) {
+      b2 = b1;
+      b1 = t.zb;
+      c1 = t.zc;
+      x1 = t.zx;
+    } else {
+      b2 = fmax(b2, t.zb);
+    }
+  }
+  Tuple m = wave_merge(acc);
+  const float T = load_uniform(p.temps + row / p.canvas_len);
+  const bool greedy = !(T > 0.0f);
+  const double zmax = wave_allreduce(b1, MaxD());
+  if (!greedy && zmax != -INFINITY) {
+    const double zcut = zmax - 0x1p-8;
+    const uint64_t near = __ballot(b1 >= zcut);
+    if (__popcll(near) == 1 && __ballot(b2 >= zcut) == 0) {
+      m.zc = __builtin_amdgcn_readlane(c1, __builtin_ctzll(near));
+    } else {
+      const double rtc = 1.0 / (double)clamp_temp(T);
+      double bz = -INFINITY;
+      int32_t bc = INT_MAX;
+      auto consider = [&](double zrep, int32_t c, int32_t zx) {
+        const double z = zx ? zrep : exact_score(p, row, rtc, c);
+        if (z > bz || (z == bz && c < bc)) {
+          bz = z;
+          bc = c;
+        }
+      };
+      if (b1 >= zcut) consider(b1, c1, x1);
+      if (b2 >= zcut) {
+        // two close members in this lane (rare): every member within the cut
+        for (int i = lane; i < p.C; i += kWave) {
+          Tuple t;
+          read_tuple(r, i, p.epoch, t);
+          if (t.zb >= zcut && t.zc != c1) consider(t.zb, t.zc, t.zx);
+        }
+      }
+      const double zbx = wave_allreduce(bz, MaxD());
+      m.zc = wave_allreduce(bz == zbx ? bc : INT_MAX, MinI());
+    }
+  }
+  if (lane == 0) {
+    write_row_outputs(p, row, greedy, m);
+    // the row result: with probs the writers need it, without probs it only
+    // paces the members
+    const u32x4 v = {__float_as_uint(m.m), p.epoch, __float_as_uint((float)(1.0 / m.S)), p.epoch};
+    __builtin_amdgcn_raw_buffer_store_b128(v, rowres_rsrc(p, row), 0u, 0, kDevScope);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk transfers. Lane l holds quads j * 64 + l (j < 8) of the chunk, so
+// each load instruction of the wave covers 1 KiB of contiguous logits; the
+// buffer descriptor stops at the row end (loads past it read 0 and are masked
+// to -inf, stores past it are dropped).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ Rsrc chunk_rsrc(const float *xrow, int32_t c0, int32_t V) {
+  // the size is wave-uniform; readfirstlane keeps it (and the descriptor) in
+  // scalar registers even where the compiler clamps it with a vector op
+  const int32_t cols = __builtin_amdgcn_readfirstlane(max(min(V - c0, kChunkCols), 0));
+  return make_rsrc(xrow + c0, 4u * (uint32_t)cols);
+}
+
+// Vector path: asynchronous copy of the chunk into the wave's LDS buffer
+// (quad j * 64 + l at buf[j * 64 + l]).
+__device__ __forceinline__ void chunk_copy_async(float4 *buf, const float *xrow, int32_t c0,
+                                                 int32_t V) {
+  const Rsrc r = chunk_rsrc(xrow, c0, V);
+  const uint32_t voff = 16u * lane_id();
+#pragma unroll
+  for (int j = 0; j < kQ; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(buf + j * kWave), 16, voff,
+                                             16 * kWave * j, 0, 0);
+}
+
+// Scalar path (unaligned rows or vocab % 4 != 0): four 4-byte loads a quad.
+__device__ __forceinline__ void chunk_load(float4 (&v)[kQ], const float *xrow, int32_t c0,
+                                           int32_t V) {
+  const Rsrc r = chunk_rsrc(xrow, c0, V);
+  const uint32_t voff = 16u * lane_id();
+#pragma unroll
+  for (int j = 0; j < kQ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      set_comp(v[j], i,
+               __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 16 * kWave * j + 4 * i, 0)));
+}
+
+// Read of the wave's LDS buffer, written as inline assembly (ending with its
+// own lgkmcnt wait): the compiler would otherwise wait for every copy still
+// in flight into LDS before the read, including the one it must overlap.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const float4 *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float4 *)p;
+}
+
+// Quads j * 64 + lane (j < 8) of the buffer at `buf`.
+__device__ __forceinline__ void lds_read_chunk(float4 (&v)[kQ], const float4 *buf) {
+  const uint32_t a = lds_addr(buf) + 16u * (uint32_t)lane_id();
+  f32x4 r0, r1, r2, r3, r4, r5, r6, r7;
+  __asm__ volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %8 offset:1024\n"
+      "ds_read_b128 %2, %8 offset:2048\n"
+      "ds_read_b128 %3, %8 offset:3072\n"
+      "ds_read_b128 %4, %8 offset:4096\n"
+      "ds_read_b128 %5, %8 offset:5120\n"
+      "ds_read_b128 %6, %8 offset:6144\n"
+      "ds_read_b128 %7, %8 offset:7168\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(a)
+      : "memory");
+  const f32x4 r[kQ] = {r0, r1, r2, r3, r4, r5, r6, r7};
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) v[j] = make_float4(r[j][0], r[j][1], r[j][2], r[j][3]);
+}
+
+// s_waitcnt vmcnt(n): at most n of this wave's vector memory operations are
+// still outstanding. They complete in issue order, so an operation followed
+// by at least n others has completed.
+// Keeps the compiler from moving memory operations across this point, so
+// the counts above hold for the issue order written here.
+__device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  compiler_fence();
+}
+
+// ---------------------------------------------------------------------------
+// Reduction of one chunk. On entry v holds the chunk's raw logits; on return
+// v holds the exp values 2^32 exp(s - m) of the wave and every lane holds the
+// wave's summary (its best score exact when `exact` is set).
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t row, int32_t chunk,
+                                              float4 (&v)[kQ], bool exact) {
+  const int lane = lane_id();
   const int32_t V = p.vocab;
   const float T = load_uniform(p.temps + row / p.canvas_len);
   const bool greedy = !(T > 0.0f);
   const double rtc = 1.0 / (double)clamp_temp(T);
   const float *xrow = p.logits + row * p.ld;
-  const int32_t q0 = g * (kThreads * QPT);
+  const int32_t c0 = chunk * kChunkCols;
+  // column of element k = 4 j + i of this lane
+  auto col_of = [&](int k) -> int32_t { return c0 + 4 * ((k >> 2) * kWave + lane) + (k & 3); };
 
-  // ---- scale the slice: s = fl32(x / Tc) ----
-  const float mt = scale_slice<QPT, kThreads>(v, q0, V, rtc);
+  // ---- mask the row end, scale s = fl32(x / Tc) ----
+  const int32_t left = V - c0;
+  if (left < kChunkCols) {
+#pragma unroll
+    for (int j = 0; j < kQ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        set_comp(v[j], i, (4 * (j * kWave + lane) + i < left) ? comp(v[j], i) : -INFINITY);
+  }
+  float mt = -INFINITY;
+  if (T == 1.0f) {  // x / 1 = x
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) mt = fmaxf(mt, max4(v[j]));
+  } else {
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      v[j].x = scale(v[j].x, rtc);
+      v[j].y = scale(v[j].y, rtc);
+      v[j].z = scale(v[j].z, rtc);
+      v[j].w = scale(v[j].w, rtc);
+      mt = fmaxf(mt, max4(v[j]));
+    }
+  }
   const float mw = wave_allreduce(mt, MaxF());
 
   // ---- lowest column of the wave attaining its max ----
   int32_t amk = INT_MAX;
   if (mt == mw) {
 #pragma unroll
-    for (int k = 4 * QPT - 1; k >= 0; --k)
+    for (int k = 4 * kQ - 1; k >= 0; --k)
       if (comp(v[k >> 2], k & 3) == mw) amk = k;
   }
-  const int32_t amw =
-      wave_allreduce(amk == INT_MAX ? INT_MAX : slice_col<kThreads>(q0, amk), MinI());
+  const int32_t amw = wave_allreduce(amk == INT_MAX ? INT_MAX : col_of(amk), MinI());
 
   // ---- exp values e = 2^32 exp(s - m) in place of s, and their sums ----
   // The 2^32 factor keeps every probability that survives rounding to
@@ -272,7 +432,7 @@ __device__ __forceinline__ void process_slice(const RowStatsParams &p, int64_t r
   const float mu = (mw == -INFINITY) ? 0.0f : mw;
   float St = 0.0f, Wt = 0.0f;
 #pragma unroll
-  for (int j = 0; j < QPT; ++j) {
+  for (int j = 0; j < kQ; ++j) {
     float4 e;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -286,268 +446,289 @@ __device__ __forceinline__ void process_slice(const RowStatsParams &p, int64_t r
   }
 
   // ---- Gumbel-max over the wave's columns (T > 0) ----
-  double bz = -INFINITY;
-  int32_t bc = INT_MAX;
+  // The wave reports its best perturbed score z = s + g and that column. The
+  // score is an fp32 estimate (within 2^-9 of exact) unless the wave had to
+  // compare candidates closer than that, or `exact` asks for it; then it is
+  // the exact fp64 score. The row merge settles close calls between chunks.
+  double zb = -INFINITY;
+  int32_t zc = INT_MAX, zx = 1;
   if (!greedy && mw != -INFINITY) {
     const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
     const uint32_t r0 = (uint32_t)(uint64_t)row, r1 = (uint32_t)((uint64_t)row >> 32);
-    // raw logit of element k of this thread (re-read, never kept in registers)
-    auto raw_x = [&](int k) -> float {
-      if constexpr (VEC) return comp(stage[(k >> 2) * kThreads + tid], k & 3);
-      else return xrow[slice_col<kThreads>(q0, k)];
-    };
+    const uint32_t qb = (uint32_t)chunk * kChunkQuads + (uint32_t)lane;  // quad of j = 0
+    constexpr float kLn2 = 0.693147180559945309f;
+    // fp32 Gumbel value -log(-log u) of a word, error below 2^-12
+    auto g32 = [&](uint32_t w) { return -__builtin_amdgcn_logf(neg_log_u_f32(w)) * kLn2; };
     // a = exp(m - zlb) = -log u of the argmax's word, zlb = m + g_argmax
     float a = neg_log_u_f32(
         pick(philox4x32_10((uint32_t)(amw >> 2), 0u, r0, r1, k0, k1), amw & 3));
     // Flat waves let many columns pass the test; the expected number is
     // sum_c exp(s_c - zlb) = a sum e / 2^32. When it is large, raise zlb to
-    // the best exact score among every lane's own maximum.
+    // a lower bound of the best score among every lane's own maximum.
     const float Sw = wave_allreduce(St, SumF());
     if (Sw * 0x1p-32f * a > 8.0f) {
-      double zt = -INFINITY;
+      float zt = -INFINITY;  // relative to m
       if (mt != -INFINITY) {
         // e is monotone in s, so the first element with e == e(mt) holds mt
         const float et = __builtin_amdgcn_exp2f(fmaf(fmaxf(mt - mu, -FLT_MAX), kLog2e, 32.0f));
         int32_t kt = INT_MAX;
 #pragma unroll
-        for (int k = 4 * QPT - 1; k >= 0; --k)
+        for (int k = 4 * kQ - 1; k >= 0; --k)
           if (comp(v[k >> 2], k & 3) == et) kt = k;
         if (kt != INT_MAX) {
-          const int32_t ct = slice_col<kThreads>(q0, kt);
+          const int32_t ct = col_of(kt);
           const uint4 w = philox4x32_10((uint32_t)(ct >> 2), 0u, r0, r1, k0, k1);
-          zt = (double)mt + gumbel_of_word(pick(w, ct & 3));
-          bz = zt;
-          bc = ct;
+          zt = (mt - mw) + g32(pick(w, ct & 3)) - 0x1p-10f;
         }
       }
-      zt = wave_allreduce(zt, MaxD());
-      a = fminf(a, (float)exp_d((double)mw - zt) * (1.0f + 0x1p-20f));
+      zt = wave_allreduce(zt, MaxF());
+      a = fminf(a, __builtin_amdgcn_exp2f(-zt * kLog2e) * (1.0f + 0x1p-12f));
     }
     const float kc = a * kTestMargin;
     const float ethr = kQuadSkip / a;
-    uint64_t cm = 0;
+    // Candidates. In the quads of the wave that hold one (few), every
+    // candidate gets an fp32 score relative to m: s - m read back from its
+    // exp value (log2 e - 32 = (s - m) log2(e), error near 1e-5) plus its
+    // fp32 Gumbel value. Each lane keeps its best two scores.
+    uint32_t cm = 0;  // candidate elements of this lane, bit k = 4 j + i
+    float za1 = -INFINITY, za2 = -INFINITY;
+    int32_t kbest = 0;
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
+    for (int j = 0; j < kQ; ++j) {
       if (max4(v[j]) >= ethr) {
-        const uint32_t q = (uint32_t)(q0 + j * kThreads + tid);
-        const uint4 w = philox4x32_10(q, 0u, r0, r1, k0, k1);
+        const uint4 w = philox4x32_10(qb + (uint32_t)(j * kWave), 0u, r0, r1, k0, k1);
+        uint32_t cq = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          cm |= (uint64_t)((float)(~pick(w, i)) <= comp(v[j], i) * kc) << (4 * j + i);
+          cq |= (uint32_t)((float)(~pick(w, i)) <= comp(v[j], i) * kc) << i;
+        if (__ballot(cq != 0) != 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (cq & (1u << i)) {
+              const float z = (__builtin_amdgcn_logf(comp(v[j], i)) - 32.0f) * kLn2 + g32(pick(w, i));
+              if (z > za1) {
+                za2 = za1;
+                za1 = z;
+                kbest = 4 * j + i;
+              } else {
+                za2 = fmaxf(za2, z);
+              }
+            }
+          }
+          cm |= cq << (4 * j);
+        }
       }
     }
-    // Candidates in two rounds: an fp32 score relative to m (error below
-    // 1e-3: s - m is exact for every candidate, -log of -log u is off by at
-    // most 2^-12) picks those within 2^-8 of the wave's best, and only
-    // those get the exact fp64 score.
-    float za = -INFINITY;
-    for (uint64_t c2 = cm; c2; c2 &= c2 - 1) {
-      const int k = __builtin_ctzll(c2);
-      const int32_t c = slice_col<kThreads>(q0, k);
-      if (c < V) {
-        const float d = scale(raw_x(k), rtc) - mw;
-        const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, r0, r1, k0, k1);
-        const float ga = -__builtin_amdgcn_logf(neg_log_u_f32(pick(w, c & 3))) *
-                         0.693147180559945309f;
-        za = fmaxf(za, d + ga);
-      }
-    }
-    const float zcut = wave_allreduce(za, MaxF()) - 0x1p-8f;
-    for (; cm; cm &= cm - 1) {
-      const int k = __builtin_ctzll(cm);
-      const int32_t c = slice_col<kThreads>(q0, k);
-      if (c < V) {
-        const float s = scale(raw_x(k), rtc);
-        const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, r0, r1, k0, k1);
-        const uint32_t wc = pick(w, c & 3);
-        const float ga = -__builtin_amdgcn_logf(neg_log_u_f32(wc)) * 0.693147180559945309f;
-        if ((s - mw) + ga >= zcut) {
-          const double z = (double)s + gumbel_of_word(wc);
+    // Only candidates within 2^-8 of the wave's best estimate can win.
+    const float zmax = wave_allreduce(za1, MaxF());
+    const float zcut = zmax - 0x1p-8f;
+    const uint64_t near = __ballot(za1 >= zcut);
+    if (!exact && __popcll(near) == 1 && __ballot(za2 >= zcut) == 0) {
+      zc = __builtin_amdgcn_readlane(col_of(kbest), __builtin_ctzll(near));
+      zb = (double)mw + (double)zmax;
+      zx = 0;
+    } else {
+      // exact fp64 scores of the candidates within the cut
+      double bz = -INFINITY;
+      int32_t bc = INT_MAX;
+      auto score_exact = [&](int k) {
+        const int32_t c = col_of(k);
+        if (c < V) {
+          const double z = exact_score(p, row, rtc, c);
           if (z > bz || (z == bz && c < bc)) {
             bz = z;
             bc = c;
           }
         }
+      };
+      if (za1 >= zcut) score_exact(kbest);
+      if (za2 >= zcut) {
+        for (uint32_t c2 = cm & ~(1u << kbest); c2; c2 &= c2 - 1) score_exact(__builtin_ctz(c2));
       }
+      zb = wave_allreduce(bz, MaxD());
+      zc = wave_allreduce(bz == zb ? bc : INT_MAX, MinI());
+      zx = 1;
     }
   }
 
-  // ---- wave tuple, then the slice tuple (wave 0) ----
-  {
-    Tuple t;
-    t.m = mw;
-    t.am = amw;
-    t.S = wave_allreduce((double)St, SumD());
-    t.W = wave_allreduce((double)Wt, SumD());
-    t.zb = wave_allreduce(bz, MaxD());
-    t.zc = wave_allreduce(bz == t.zb ? bc : INT_MAX, MinI());
-    if (lane == 0) sh.wave[wave] = t;
-  }
-  __syncthreads();
-  // no wave reads the stage any more: start copying the next slice
-  if constexpr (VEC) {
-    if (next_xrow) stage_slice_async<QPT, kThreads>(stage, next_xrow, next_q0, V);
-  }
-  const SyncScratch sy = sync_scratch(p);
-  const uint32_t w_row = tuple_index(p, row, 0, 0);
-
-  if constexpr (PROBS == 0) {
-    if (wave == 0) {
-      const Tuple st = merge_tuples<kWaves>(kWaves, [&](int i) { return sh.wave[i]; });
-      const uint32_t old = publish_tuple(sy, w_row + g * kTupleWords, st, row);
-      if (old == (uint32_t)(p.G - 1)) {
-        // last slice of the row: every tuple was stored before its count
-        l1_invalidate(sy);
-        const Tuple r =
-            merge_slices(p.G, [&](int i) { return load_tuple(sy, w_row + i * kTupleWords); });
-        if (lane == 0) write_row_outputs(p, row, greedy, r);
-      }
-    }
-  } else {
-    if (wave == 0) {
-      const Tuple st = merge_tuples<kWaves>(kWaves, [&](int i) { return sh.wave[i]; });
-      publish_tuple(sy, w_row + g * kTupleWords, st, row);
-      if (lane == 0) {
-        uint32_t spins = 0;
-        while (counter_load(sy, row) < (uint32_t)p.G) {
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins > kSpinLimit) {
-            atomicOr(p.err_flag, 1u);
-            break;
-          }
-        }
-      }
-      // the loads below are issued after lane 0 has seen every count
-      l1_invalidate(sy);
-      const Tuple r =
-          merge_slices(p.G, [&](int i) { return load_tuple(sy, w_row + i * kTupleWords); });
-      // exp value of wave i -> probability: p = e exp(m_i - m) / S
-      if (lane < kWaves) {
-        const Tuple t = sh.wave[lane];
-        sh.scale[lane] = (t.m == -INFINITY)
-                             ? 0.0f
-                             : (float)((double)__builtin_amdgcn_exp2f(fmaxf(t.m - r.m, -FLT_MAX) * kLog2e) / r.S);
-      }
-      if (lane == 0 && g == 0) write_row_outputs(p, row, greedy, r);
-    }
-    __syncthreads();
-    const float sc = sh.scale[wave];
-
-    // ---- write the slice's probabilities once ----
-    const int32_t c0 = 4 * q0;
-    const int32_t left = V - c0;
-    const Rsrc w = make_rsrc(reinterpret_cast<uint16_t *>(p.probs) + row * (int64_t)V + c0,
-                             2u * (uint32_t)min(left, 4 * kThreads * QPT));
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      uint32_t b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = comp(v[j], i) * sc;
-        b[i] = (PROBS == 1) ? bf16_rne_bits(pv) : fp16_rne_bits(pv);
-      }
-      if constexpr (VEC) {
-        const u32x2 pk = {b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-        __builtin_amdgcn_raw_buffer_store_b64(pk, w, 8u * tid, 8 * j * kThreads, kNonTemporal);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)b[i], w, 8u * tid,
-                                                8 * j * kThreads + 2 * i, kNonTemporal);
-      }
-    }
-  }
-  __syncthreads();  // sh is rewritten by the next slice
+  Tuple t;
+  t.m = mw;
+  t.am = amw;
+  t.S = wave_allreduce((double)St, SumD());
+  t.W = wave_allreduce((double)Wt, SumD());
+  t.zb = zb;
+  t.zc = zc;
+  t.zx = zx;
+  return t;
 }
 
-// Slice items of one workgroup: linear item index row * G + g.
-struct ItemCursor {
-  int64_t it, step, end;
-};
+// exp value of a chunk whose wave maximum is mw -> probability:
+// p = e exp(mw - m) / S
+__device__ __forceinline__ float prob_scale(float mw, float m, float inv_s) {
+  if (mw == -INFINITY) return 0.0f;
+  return __builtin_amdgcn_exp2f(fmaxf(mw - m, -FLT_MAX) * kLog2e) * inv_s;
+}
 
-template <int QPT, int PROBS, bool VEC>
-__global__ __launch_bounds__(kThreads, 4) void rowstats_kernel(RowStatsParams p) {
-  __shared__ SliceShared sh;
-  // LDS stage of the slice (vector path): the next slice's HBM copies run
-  // while the current one waits for its row and writes its probs.
-  __shared__ float4 stage[VEC ? kThreads * QPT : 1];
-  const int nwg = gridDim.x;
-  // XCD-aware logical id: hardware workgroup b runs on XCD b % 8; logical
-  // ids that share a row (consecutive ids) are placed on one XCD.
-  int L = blockIdx.x;
-  if (p.xcd_map) L = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
-  // Row counters come in two banks used by alternate calls: this call counts
-  // in bank `parity` (zeroed by the previous call) and zeroes the other one
-  // for the next call, so no counter is ever reset while in use.
-  {
-    uint32_t *other = p.counters + (size_t)(p.parity ^ 1) * p.counter_stride;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < p.counter_stride;
-         i += (int64_t)nwg * kThreads)
-      other[i] = 0u;
-  }
-  // XCD-local synchronisation relies on workgroup b running on XCC b % 8
-  if (p.l2_sync && threadIdx.x == 0 && xcc_id() != blockIdx.x % 8) atomicOr(p.err_flag, 2u);
-  // Items: without probs, linear items L, L + nwg, ...; with probs, slice g
-  // of rows group, group + n_groups, ...
-  ItemCursor cur;
-  if constexpr (PROBS == 0) {
-    cur = {L, nwg, p.rows * (int64_t)p.G};
-  } else {
-    const int group = L / p.G;
-    if (group >= p.n_groups) return;
-    cur = {(int64_t)group * p.G + (L - group * p.G), (int64_t)p.n_groups * p.G,
-           p.rows * (int64_t)p.G};
-  }
-  if (cur.it >= cur.end) return;
-  constexpr int32_t span = kThreads * QPT;
-  if constexpr (VEC) {
-    const int64_t row = cur.it / p.G;
-    stage_slice_async<QPT, kThreads>(stage, p.logits + row * p.ld,
-                                     (int32_t)(cur.it - row * p.G) * span, p.vocab);
-  }
-  for (; cur.it < cur.end; cur.it += cur.step) {
-    const int64_t row = cur.it / p.G;
-    const int g = (int)(cur.it - row * p.G);
-    float4 v[QPT];
-    const float *next_xrow = nullptr;
-    int32_t next_q0 = 0;
+template <int PROBS, bool VEC>
+__device__ __forceinline__ void write_probs(const RowStatsParams &p, int64_t row, int32_t chunk,
+                                            const float4 (&e)[kQ], float sc) {
+  const int lane = lane_id();
+  const int32_t c0 = chunk * kChunkCols;
+  const Rsrc w = make_rsrc(reinterpret_cast<uint16_t *>(p.probs) + row * (int64_t)p.vocab + c0,
+                           2u * (uint32_t)min(p.vocab - c0, kChunkCols));
+  auto pack = [](float a, float b) {
+    return (PROBS == 1) ? pack_bf16x2(a, b) : pack_fp16x2(a, b);
+  };
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) {
+    const u32x2 pk = {pack(e[j].x * sc, e[j].y * sc), pack(e[j].z * sc, e[j].w * sc)};
     if constexpr (VEC) {
-      stage_wait();
-      __syncthreads();
-      read_stage<QPT, kThreads>(stage, v);
-      const int64_t nx = cur.it + cur.step;
-      if (nx < cur.end) {
-        const int64_t nrow = nx / p.G;
-        next_xrow = p.logits + nrow * p.ld;
-        next_q0 = (int32_t)(nx - nrow * p.G) * span;
-      }
+      __builtin_amdgcn_raw_buffer_store_b64(pk, w, 8u * lane, 8 * kWave * j, kNonTemporal);
     } else {
-      load_slice<QPT, kThreads, VEC>(p.logits + row * p.ld, g * span, p.vocab, v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk[i >> 1] >> (16 * (i & 1))), w, 8u * lane,
+                                              8 * kWave * j + 2 * i, kNonTemporal);
     }
-    process_slice<QPT, PROBS, VEC>(p, row, g, sh, v, stage, next_xrow, next_q0);
+  }
+}
+
+// Waits until the row result of `row` (pre-loaded in v) shows this call's
+// epoch; returns it.
+__device__ __forceinline__ u32x4 wait_row_result(const RowStatsParams &p, int64_t row, u32x4 v) {
+  // the retry loop sits off the common path: a loop header there would make
+  // the compiler wait for every outstanding copy before the first check
+  if (!rowres_ready(v, p.epoch)) {
+    uint32_t spins = 0;
+    do {
+      __builtin_amdgcn_s_sleep(1);
+      v = load_rowres(p, row);
+    } while (!rowres_ready(v, p.epoch) && ++spins <= kSpinLimit && !call_failed(p));
+    if (!rowres_ready(v, p.epoch) && lane_id() == 0) atomicOr(p.err_flag, 1u);
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// The kernel. Global wave gw belongs to group gw / C as member gw % C: the
+// group reduces rows group, group + n_groups, ..., the member chunk `member`
+// of each. The merger of the group's n-th row is member n % C; it merges
+// row n after reducing row n + 1. Before publishing row n, every member
+// waits for the result of row n - 2 (normally long there): with probs it
+// needs it to write row n - 2's probabilities, and without probs the wait
+// keeps the waves of a SIMD in step (otherwise the older wave, favoured by
+// the issue arbiter, would finish early and leave the SIMD half idle).
+// ---------------------------------------------------------------------------
+template <int PROBS, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void rowstats_kernel(RowStatsParams p) {
+  // one LDS buffer of one chunk per wave (vector path): the next chunk is
+  // copied in as soon as the current one has been read into registers
+  __shared__ float4 stage[VEC ? kWaves * kChunkQuads : 1];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int gw = (int)blockIdx.x * kWaves + wave;
+  const int group = gw / p.C;
+  const int member = gw - group * p.C;
+  if (group >= p.n_groups) return;
+  const int64_t nrows = (p.rows - group + p.n_groups - 1) / p.n_groups;
+  if (nrows <= 0) return;
+  const int32_t chunk = member;
+  auto row_of = [&](int64_t n) -> int64_t { return group + n * p.n_groups; };
+  float4 *const buf = stage + (VEC ? wave * kChunkQuads : 0);
+  // Copies the chunk of the group's row n into the wave's buffer. Past the
+  // last row the copy still issues (through a zero-size descriptor: nothing
+  // is read, the buffer gets zeros), so every path issues the same
+  // operations and the compiler can count them exactly.
+  auto copy_chunk = [&](int64_t n) {
+    if (n < nrows)
+      chunk_copy_async(buf, p.logits + row_of(n) * p.ld, chunk * kChunkCols, p.vocab);
+    else
+      chunk_copy_async(buf, p.logits, 0, 0);
+  };
+
+  float4 cur[kQ];
+  float4 p1[PROBS ? kQ : 1], p2[PROBS ? kQ : 1];  // exp values of rows n - 1, n - 2
+  float m1 = -INFINITY, m2 = -INFINITY;            // and their wave maxima
+  int mturn = 0;                                   // (n - 1) % C
+  if constexpr (VEC) copy_chunk(0);
+  for (int64_t n = 0; n < nrows; ++n) {
+    const int64_t row = row_of(n);
+    // row result of row n - 2, written by its merger a chunk ago (loaded
+    // every time so that no path leaves the register waiting on a load)
+    u32x4 rr = load_rowres(p, row_of(n >= 2 ? n - 2 : 0));
+    compiler_fence();
+    if constexpr (VEC) {
+      // after this item's copy came, in the previous item, its eight probs
+      // stores (with probs, from the third item on), its summary store and
+      // this item's row-result load
+      if (n == 0) wait_vm<0>();
+      else if (PROBS != 0 && n >= 3) wait_vm<9>();
+      else wait_vm<1>();
+      lds_read_chunk(cur, buf);
+      compiler_fence();
+      copy_chunk(n + 1);
+      compiler_fence();
+    } else {
+      chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
+    }
+    const Tuple t = reduce_chunk<VEC>(p, row, chunk, cur, false);
+    // row n - 2 first: waiting for its result then does not wait for the
+    // summary store below. The empty statement consumes rr on every path,
+    // so the wait for its load is placed here, exactly.
+    __asm__ volatile("" ::"v"(rr));
+    if (n >= 2) {
+      rr = wait_row_result(p, row_of(n - 2), rr);
+      if constexpr (PROBS != 0)
+        write_probs<PROBS, VEC>(p, row_of(n - 2), chunk, p2,
+                                prob_scale(m2, __uint_as_float(rr[0]), __uint_as_float(rr[2])));
+    }
+    compiler_fence();
+    publish_tuple(tuple_rsrc(p, row), member, t, p.epoch);
+    compiler_fence();
+    if (n >= 1 && mturn == member) merge_row<PROBS>(p, row_of(n - 1));
+    if (n >= 1 && ++mturn == p.C) mturn = 0;
+    if constexpr (PROBS != 0) {
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) {
+        p2[j] = p1[j];
+        p1[j] = cur[j];
+      }
+      m2 = m1;
+      m1 = t.m;
+    }
+  }
+  if (mturn == member) merge_row<PROBS>(p, row_of(nrows - 1));
+  if constexpr (PROBS != 0) {
+    if (nrows >= 2) {
+      const int64_t r2 = row_of(nrows - 2);
+      const u32x4 v = wait_row_result(p, r2, load_rowres(p, r2));
+      write_probs<PROBS, VEC>(p, r2, chunk, p2, prob_scale(m2, __uint_as_float(v[0]), __uint_as_float(v[2])));
+    }
+    const int64_t r1 = row_of(nrows - 1);
+    const u32x4 v = wait_row_result(p, r1, load_rowres(p, r1));
+    write_probs<PROBS, VEC>(p, r1, chunk, p1, prob_scale(m1, __uint_as_float(v[0]), __uint_as_float(v[2])));
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host side: occupancy query and launch (called by the C ABI).
 // ---------------------------------------------------------------------------
-template <int QPT, int PROBS, bool VEC>
+template <int PROBS, bool VEC>
 static const void *kernel_ptr() {
-  return reinterpret_cast<const void *>(&rowstats_kernel<QPT, PROBS, VEC>);
+  return reinterpret_cast<const void *>(&rowstats_kernel<PROBS, VEC>);
 }
 
 static const void *select_kernel(int probs_dtype, bool vec) {
   if (vec) {
     switch (probs_dtype) {
-      case 1: return kernel_ptr<kQPT, 1, true>();
-      case 2: return kernel_ptr<kQPT, 2, true>();
-      default: return kernel_ptr<kQPT, 0, true>();
+      case 1: return kernel_ptr<1, true>();
+      case 2: return kernel_ptr<2, true>();
+      default: return kernel_ptr<0, true>();
     }
   }
   switch (probs_dtype) {
-    case 1: return kernel_ptr<kQPT, 1, false>();
-    case 2: return kernel_ptr<kQPT, 2, false>();
-    default: return kernel_ptr<kQPT, 0, false>();
+    case 1: return kernel_ptr<1, false>();
+    case 2: return kernel_ptr<2, false>();
+    default: return kernel_ptr<0, false>();
   }
 }
 
@@ -560,10 +741,8 @@ hipError_t rowstats_launch(const RowStatsParams &p, int probs_dtype, int grid,
                            hipStream_t stream) {
   RowStatsParams arg = p;
   void *args[] = {&arg};
-  const void *k = select_kernel(probs_dtype, p.vec_ok != 0);
-  if (probs_dtype != 0)
-    return hipLaunchCooperativeKernel(k, dim3(grid), dim3(kThreads), args, 0, stream);
-  return hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, 0, stream);
+  return hipLaunchCooperativeKernel(select_kernel(probs_dtype, p.vec_ok != 0), dim3(grid),
+                                    dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace rowstats

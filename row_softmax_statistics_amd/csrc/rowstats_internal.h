@@ -11,7 +11,7 @@ namespace rowstats {
 // (4 columns) in registers. Workgroups of kRowThreads threads only group
 // waves for launch and LDS; waves exchange results through global scratch.
 constexpr int kWaveQuads = 8;
-constexpr int kRowThreads = 512;
+constexpr int kRowThreads = 256;
 constexpr int kChunkQuads = 64 * kWaveQuads;  // 512
 constexpr int kChunkCols = 4 * kChunkQuads;   // 2048
 

@@ -359,6 +359,16 @@ __device__ __forceinline__ void lds_read_chunk(float4 (&v)[kQ], const float4 *bu
   for (int j = 0; j < kQ; ++j) v[j] = make_float4(r[j][0], r[j][1], r[j][2], r[j][3]);
 }
 
+// cm = 2 cm + (a >= b): the compare writes VCC and the add takes it as the
+// carry in (the compiler would spend a select and a shift instead).
+__device__ __forceinline__ uint32_t push_bit_ge(uint32_t cm, float a, float b) {
+  __asm__("v_cmp_ge_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+          : "+v"(cm)
+          : "v"(a), "v"(b)
+          : "vcc");
+  return cm;
+}
+
 // s_waitcnt vmcnt(n): at most n of this wave's vector memory operations are
 // still outstanding. They complete in issue order, so an operation followed
 // by at least n others has completed.
@@ -418,13 +428,13 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   const float mw = wave_allreduce(mt, MaxF());
 
   // ---- lowest column of the wave attaining its max ----
-  int32_t amk = INT_MAX;
-  if (mt == mw) {
+  // kt: this lane's first element equal to its own maximum (the Gumbel
+  // bound below uses it too)
+  int32_t kt = 0;
 #pragma unroll
-    for (int k = 4 * kQ - 1; k >= 0; --k)
-      if (comp(v[k >> 2], k & 3) == mw) amk = k;
-  }
-  const int32_t amw = wave_allreduce(amk == INT_MAX ? INT_MAX : col_of(amk), MinI());
+  for (int k = 4 * kQ - 1; k >= 0; --k)
+    if (comp(v[k >> 2], k & 3) == mt) kt = k;
+  const int32_t amw = wave_allreduce(mt == mw ? col_of(kt) : INT_MAX, MinI());
 
   // ---- exp values e = 2^32 exp(s - m) in place of s, and their sums ----
   // The 2^32 factor keeps every probability that survives rounding to
@@ -469,53 +479,51 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     if (Sw * 0x1p-32f * a > 8.0f) {
       float zt = -INFINITY;  // relative to m
       if (mt != -INFINITY) {
-        // e is monotone in s, so the first element with e == e(mt) holds mt
-        const float et = __builtin_amdgcn_exp2f(fmaf(fmaxf(mt - mu, -FLT_MAX), kLog2e, 32.0f));
-        int32_t kt = INT_MAX;
-#pragma unroll
-        for (int k = 4 * kQ - 1; k >= 0; --k)
-          if (comp(v[k >> 2], k & 3) == et) kt = k;
-        if (kt != INT_MAX) {
-          const int32_t ct = col_of(kt);
-          const uint4 w = philox4x32_10((uint32_t)(ct >> 2), 0u, r0, r1, k0, k1);
-          zt = (mt - mw) + g32(pick(w, ct & 3)) - 0x1p-10f;
-        }
+        const int32_t ct = col_of(kt);
+        const uint4 w = philox4x32_10((uint32_t)(ct >> 2), 0u, r0, r1, k0, k1);
+        zt = (mt - mw) + g32(pick(w, ct & 3)) - 0x1p-10f;
       }
       zt = wave_allreduce(zt, MaxF());
       a = fminf(a, __builtin_amdgcn_exp2f(-zt * kLog2e) * (1.0f + 0x1p-12f));
     }
     const float kc = a * kTestMargin;
     const float ethr = kQuadSkip / a;
-    // Candidates. In the quads of the wave that hold one (few), every
-    // candidate gets an fp32 score relative to m: s - m read back from its
-    // exp value (log2 e - 32 = (s - m) log2(e), error near 1e-5) plus its
-    // fp32 Gumbel value. Each lane keeps its best two scores.
-    uint32_t cm = 0;  // candidate elements of this lane, bit k = 4 j + i
-    float za1 = -INFINITY, za2 = -INFINITY;
-    int32_t kbest = 0;
+    // Candidate test of a column with word w and exp value e: it can reach
+    // zlb only if 1 - u <= e a 2^-32, i.e. w >= 2^32 - 1/2 - e a. Tested as
+    // fl32(w) >= fl32(2^32 - 512 - e kc): fl32(w) is within 128 of w, the fma
+    // rounds by at most 128 and kc covers the rounding of e and a, so every
+    // such column passes (a few more may). Bit 31 - k of cm is element k.
+    uint32_t cm = 0;
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
       if (max4(v[j]) >= ethr) {
         const uint4 w = philox4x32_10(qb + (uint32_t)(j * kWave), 0u, r0, r1, k0, k1);
-        uint32_t cq = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          cq |= (uint32_t)((float)(~pick(w, i)) <= comp(v[j], i) * kc) << i;
-        if (__ballot(cq != 0) != 0) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (cq & (1u << i)) {
-              const float z = (__builtin_amdgcn_logf(comp(v[j], i)) - 32.0f) * kLn2 + g32(pick(w, i));
-              if (z > za1) {
-                za2 = za1;
-                za1 = z;
-                kbest = 4 * j + i;
-              } else {
-                za2 = fmaxf(za2, z);
-              }
-            }
-          }
-          cm |= cq << (4 * j);
+          cm = push_bit_ge(cm, (float)pick(w, i), fmaf(-comp(v[j], i), kc, 4294966784.0f));
+      } else {
+        cm <<= 4;
+      }
+    }
+    // Every candidate gets an fp32 score relative to m: s - m from its raw
+    // logit (re-read; it was just streamed, so the read normally hits the
+    // cache) plus its fp32 Gumbel value. Each lane keeps its best two.
+    float za1 = -INFINITY, za2 = -INFINITY;
+    int32_t kbest = 0;
+    for (uint32_t c2 = cm; c2 != 0;) {
+      const int k = __builtin_clz(c2);
+      c2 &= ~(0x80000000u >> k);
+      const int32_t c = col_of(k);
+      if (c < V) {
+        const float x = xrow[c];
+        const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, r0, r1, k0, k1);
+        const float z = (scale(x, rtc) - mw) + g32(pick(w, c & 3));
+        if (z > za1) {
+          za2 = za1;
+          za1 = z;
+          kbest = k;
+        } else {
+          za2 = fmaxf(za2, z);
         }
       }
     }
@@ -543,7 +551,11 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
       };
       if (za1 >= zcut) score_exact(kbest);
       if (za2 >= zcut) {
-        for (uint32_t c2 = cm & ~(1u << kbest); c2; c2 &= c2 - 1) score_exact(__builtin_ctz(c2));
+        for (uint32_t c2 = cm & ~(0x80000000u >> kbest); c2 != 0;) {
+          const int k = __builtin_clz(c2);
+          c2 &= ~(0x80000000u >> k);
+          score_exact(k);
+        }
       }
       zb = wave_allreduce(bz, MaxD());
       zc = wave_allreduce(bz == zb ? bc : INT_MAX, MinI());
@@ -620,7 +632,7 @@ __device__ __forceinline__ u32x4 wait_row_result(const RowStatsParams &p, int64_
 // the issue arbiter, would finish early and leave the SIMD half idle).
 // ---------------------------------------------------------------------------
 template <int PROBS, bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void rowstats_kernel(RowStatsParams p) {
+__global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowStatsParams p) {
   // one LDS buffer of one chunk per wave (vector path): the next chunk is
   // copied in as soon as the current one has been read into registers
   __shared__ float4 stage[VEC ? kWaves * kChunkQuads : 1];

@@ -58,6 +58,8 @@ constexpr float kTestMargin = 1.0f + 0x1p-10f;
 // Cache-policy bit sc1: a device-scope coherent load or store (the CU's L1
 // is bypassed and the access is coherent across XCDs).
 constexpr int kDevScope = 16;
+// Rows between publishing a row's summary and reading its result.
+constexpr int kLag = 3;
 
 typedef __attribute__((address_space(3))) void *LdsPtr;
 
@@ -626,10 +628,12 @@ __device__ __forceinline__ u32x4 wait_row_result(const RowStatsParams &p, int64_
 // group reduces rows group, group + n_groups, ..., the member chunk `member`
 // of each. The merger of the group's n-th row is member n % C; it merges
 // row n after reducing row n + 1. Before publishing row n, every member
-// waits for the result of row n - 2 (normally long there): with probs it
-// needs it to write row n - 2's probabilities, and without probs the wait
-// keeps the waves of a SIMD in step (otherwise the older wave, favoured by
-// the issue arbiter, would finish early and leave the SIMD half idle).
+// waits for the result of row n - kLag (normally there for a whole chunk):
+// with probs it needs it to write that row's probabilities, and without
+// probs the wait keeps the waves of a SIMD in step (otherwise the older
+// wave, favoured by the issue arbiter, would finish early and leave the
+// SIMD half idle). With kLag = 2 the merger's result would arrive just as
+// the members look for it.
 // ---------------------------------------------------------------------------
 template <int PROBS, bool VEC>
 __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowStatsParams p) {
@@ -658,22 +662,24 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
   };
 
   float4 cur[kQ];
-  float4 p1[PROBS ? kQ : 1], p2[PROBS ? kQ : 1];  // exp values of rows n - 1, n - 2
-  float m1 = -INFINITY, m2 = -INFINITY;            // and their wave maxima
-  int mturn = 0;                                   // (n - 1) % C
+  // exp values and wave maxima of rows n - 1, n - 2, n - 3 (with probs)
+  float4 p1[PROBS ? kQ : 1], p2[PROBS ? kQ : 1], p3[PROBS ? kQ : 1];
+  float m1 = -INFINITY, m2 = -INFINITY, m3 = -INFINITY;
+  int mturn = 0;  // (n - 1) % C
   if constexpr (VEC) copy_chunk(0);
   for (int64_t n = 0; n < nrows; ++n) {
     const int64_t row = row_of(n);
-    // row result of row n - 2, written by its merger a chunk ago (loaded
-    // every time so that no path leaves the register waiting on a load)
-    u32x4 rr = load_rowres(p, row_of(n >= 2 ? n - 2 : 0));
+    // row result of row n - kLag, written by its merger more than a chunk
+    // ago (loaded every time so that no path leaves the register waiting on
+    // a load)
+    u32x4 rr = load_rowres(p, row_of(n >= kLag ? n - kLag : 0));
     compiler_fence();
     if constexpr (VEC) {
       // after this item's copy came, in the previous item, its eight probs
-      // stores (with probs, from the third item on), its summary store and
-      // this item's row-result load
+      // stores (with probs, once rows are kLag behind), its summary store
+      // and this item's row-result load
       if (n == 0) wait_vm<0>();
-      else if (PROBS != 0 && n >= 3) wait_vm<9>();
+      else if (PROBS != 0 && n > kLag) wait_vm<9>();
       else wait_vm<1>();
       lds_read_chunk(cur, buf);
       compiler_fence();
@@ -683,15 +689,15 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
       chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
     }
     const Tuple t = reduce_chunk<VEC>(p, row, chunk, cur, false);
-    // row n - 2 first: waiting for its result then does not wait for the
+    // row n - kLag first: waiting for its result then does not wait for the
     // summary store below. The empty statement consumes rr on every path,
     // so the wait for its load is placed here, exactly.
     __asm__ volatile("" ::"v"(rr));
-    if (n >= 2) {
-      rr = wait_row_result(p, row_of(n - 2), rr);
+    if (n >= kLag) {
+      rr = wait_row_result(p, row_of(n - kLag), rr);
       if constexpr (PROBS != 0)
-        write_probs<PROBS, VEC>(p, row_of(n - 2), chunk, p2,
-                                prob_scale(m2, __uint_as_float(rr[0]), __uint_as_float(rr[2])));
+        write_probs<PROBS, VEC>(p, row_of(n - kLag), chunk, p3,
+                                prob_scale(m3, __uint_as_float(rr[0]), __uint_as_float(rr[2])));
     }
     compiler_fence();
     publish_tuple(tuple_rsrc(p, row), member, t, p.epoch);
@@ -701,23 +707,27 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
     if constexpr (PROBS != 0) {
 #pragma unroll
       for (int j = 0; j < kQ; ++j) {
+        p3[j] = p2[j];
         p2[j] = p1[j];
         p1[j] = cur[j];
       }
+      m3 = m2;
       m2 = m1;
       m1 = t.m;
     }
   }
   if (mturn == member) merge_row<PROBS>(p, row_of(nrows - 1));
   if constexpr (PROBS != 0) {
-    if (nrows >= 2) {
-      const int64_t r2 = row_of(nrows - 2);
-      const u32x4 v = wait_row_result(p, r2, load_rowres(p, r2));
-      write_probs<PROBS, VEC>(p, r2, chunk, p2, prob_scale(m2, __uint_as_float(v[0]), __uint_as_float(v[2])));
-    }
-    const int64_t r1 = row_of(nrows - 1);
-    const u32x4 v = wait_row_result(p, r1, load_rowres(p, r1));
-    write_probs<PROBS, VEC>(p, r1, chunk, p1, prob_scale(m1, __uint_as_float(v[0]), __uint_as_float(v[2])));
+    // the last kLag rows' probabilities
+    auto finish = [&](int64_t n, const float4 (&e)[kQ], float mw) {
+      if (n < 0) return;
+      const int64_t r = row_of(n);
+      const u32x4 v = wait_row_result(p, r, load_rowres(p, r));
+      write_probs<PROBS, VEC>(p, r, chunk, e, prob_scale(mw, __uint_as_float(v[0]), __uint_as_float(v[2])));
+    };
+    finish(nrows - 3, p3, m3);
+    finish(nrows - 2, p2, m2);
+    finish(nrows - 1, p1, m1);
   }
 }
 

@@ -467,7 +467,11 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   if (!greedy && mw != -INFINITY) {
     const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
     const uint32_t r0 = (uint32_t)(uint64_t)row, r1 = (uint32_t)((uint64_t)row >> 32);
-    const uint32_t qb = (uint32_t)chunk * kChunkQuads + (uint32_t)lane;  // quad of j = 0
+    uint32_t qb = (uint32_t)chunk * kChunkQuads + (uint32_t)lane;  // quad of j = 0
+    // The counters are the same for every row of this wave: without this the
+    // compiler hoists the first Philox round out of the row loop and, short
+    // of registers, reloads its products from scratch memory every row.
+    __asm__ volatile("" : "+v"(qb));
     constexpr float kLn2 = 0.693147180559945309f;
     // fp32 Gumbel value -log(-log u) of a word, error below 2^-12
     auto g32 = [&](uint32_t w) { return -__builtin_amdgcn_logf(neg_log_u_f32(w)) * kLn2; };

@@ -1,0 +1,163 @@
+// Chunk pipeline shared by the row-statistics and top-K kernels (gfx950):
+// a wave owns a chunk of 2048 columns of a row (lane l holds quads
+// j * 64 + l, j < 8), copies the next chunk from HBM into its LDS buffer
+// while it reduces the current one, and exchanges results with the other
+// waves of the row through device-coherent words tagged with the call's
+// epoch.
+#pragma once
+
+#include "device_common.h"
+#include "rowstats_internal.h"
+
+namespace rowstats {
+
+constexpr int kQ = kWaveQuads;
+// Cache-policy bit sc1: a device-scope coherent load or store (the CU's L1
+// is bypassed and the access is coherent across XCDs).
+constexpr int kDevScope = 16;
+// Polls of one wait before it gives up and flags the call (about a second);
+// once any wait has given up, every later wait of the call gives up at once.
+constexpr uint32_t kSpinLimit = 1u << 20;
+// Rows between publishing a row's summaries and reading the row's result.
+constexpr int kLag = 3;
+
+typedef __attribute__((address_space(3))) void *LdsPtr;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Keeps the compiler from moving memory operations across this point, so
+// the counts above hold for the issue order written here.
+__device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  compiler_fence();
+}
+
+
+// ---------------------------------------------------------------------------
+// Chunk transfers. Lane l holds quads j * 64 + l (j < 8) of the chunk, so
+// each load instruction of the wave covers 1 KiB of contiguous logits; the
+// buffer descriptor stops at the row end (loads past it read 0 and are masked
+// to -inf, stores past it are dropped).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ Rsrc chunk_rsrc(const float *xrow, int32_t c0, int32_t V) {
+  // the size is wave-uniform; readfirstlane keeps it (and the descriptor) in
+  // scalar registers even where the compiler clamps it with a vector op
+  const int32_t cols = __builtin_amdgcn_readfirstlane(max(min(V - c0, kChunkCols), 0));
+  return make_rsrc(xrow + c0, 4u * (uint32_t)cols);
+}
+
+// Vector path: asynchronous copy of the chunk into the wave's LDS buffer
+// (quad j * 64 + l at buf[j * 64 + l]).
+__device__ __forceinline__ void chunk_copy_async(float4 *buf, const float *xrow, int32_t c0,
+                                                 int32_t V) {
+  const Rsrc r = chunk_rsrc(xrow, c0, V);
+  const uint32_t voff = 16u * lane_id();
+  // The instruction offset moves both the HBM address and the LDS
+  // destination, so M0 (the LDS base) changes only once per chunk.
+#define ROWSTATS_DMA(J)                                                                          \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(buf + ((J) >> 2) * 4 * kWave), 16, voff, \
+                                           4096 * ((J) >> 2), 1024 * ((J)&3), 0)
+  ROWSTATS_DMA(0);
+  ROWSTATS_DMA(1);
+  ROWSTATS_DMA(2);
+  ROWSTATS_DMA(3);
+  ROWSTATS_DMA(4);
+  ROWSTATS_DMA(5);
+  ROWSTATS_DMA(6);
+  ROWSTATS_DMA(7);
+#undef ROWSTATS_DMA
+}
+
+// Scalar path (unaligned rows or vocab % 4 != 0): four 4-byte loads a quad.
+__device__ __forceinline__ void chunk_load(float4 (&v)[kQ], const float *xrow, int32_t c0,
+                                           int32_t V) {
+  const Rsrc r = chunk_rsrc(xrow, c0, V);
+  const uint32_t voff = 16u * lane_id();
+#pragma unroll
+  for (int j = 0; j < kQ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      set_comp(v[j], i,
+               __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 16 * kWave * j + 4 * i, 0)));
+}
+
+// Read of the wave's LDS buffer, written as inline assembly (ending with its
+// own lgkmcnt wait): the compiler would otherwise wait for every copy still
+// in flight into LDS before the read, including the one it must overlap.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const float4 *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float4 *)p;
+}
+
+// Quads j * 64 + lane (j < 8) of the buffer at `buf`.
+__device__ __forceinline__ void lds_read_chunk(float4 (&v)[kQ], const float4 *buf) {
+  const uint32_t a = lds_addr(buf) + 16u * (uint32_t)lane_id();
+  f32x4 r0, r1, r2, r3, r4, r5, r6, r7;
+  __asm__ volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %8 offset:1024\n"
+      "ds_read_b128 %2, %8 offset:2048\n"
+      "ds_read_b128 %3, %8 offset:3072\n"
+      "ds_read_b128 %4, %8 offset:4096\n"
+      "ds_read_b128 %5, %8 offset:5120\n"
+      "ds_read_b128 %6, %8 offset:6144\n"
+      "ds_read_b128 %7, %8 offset:7168\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(a)
+      : "memory");
+  const f32x4 r[kQ] = {r0, r1, r2, r3, r4, r5, r6, r7};
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) v[j] = make_float4(r[j][0], r[j][1], r[j][2], r[j][3]);
+}
+
+
+// ---------------------------------------------------------------------------
+// Row results: two 64-bit words per row, a 32-bit payload each with the
+// call's epoch in the high half, stored device-coherently by the row's
+// merger and polled by the row's other waves.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ Rsrc row_result_rsrc(uint64_t *rowres, int64_t row) {
+  return make_rsrc(rowres + row * (kRowResultBytes / 8), (uint32_t)kRowResultBytes);
+}
+__device__ __forceinline__ u32x4 load_row_result(uint64_t *rowres, int64_t row) {
+  return __builtin_amdgcn_raw_buffer_load_b128(row_result_rsrc(rowres, row), 0u, 0, kDevScope);
+}
+__device__ __forceinline__ void store_row_result(uint64_t *rowres, int64_t row, uint32_t a,
+                                                 uint32_t b, uint32_t epoch) {
+  const u32x4 v = {a, epoch, b, epoch};
+  __builtin_amdgcn_raw_buffer_store_b128(v, row_result_rsrc(rowres, row), 0u, 0, kDevScope);
+}
+__device__ __forceinline__ bool row_result_ready(const u32x4 &v, uint32_t epoch) {
+  return ((v[1] == epoch) & (v[3] == epoch)) != 0;
+}
+
+// Whether some wait of this call has already given up.
+__device__ __forceinline__ bool call_failed(const uint32_t *err_flag) {
+  return __hip_atomic_load(err_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+}
+
+// Waits until the row result of `row` (pre-loaded in v) shows `epoch`;
+// returns it.
+__device__ __forceinline__ u32x4 wait_row_result(uint64_t *rowres, int64_t row, u32x4 v,
+                                                 uint32_t epoch, uint32_t *err_flag) {
+  // the retry loop sits off the common path: a loop header there would make
+  // the compiler wait for every outstanding copy before the first check
+  if (!row_result_ready(v, epoch)) {
+    uint32_t spins = 0;
+    do {
+      __builtin_amdgcn_s_sleep(1);
+      v = load_row_result(rowres, row);
+    } while (!row_result_ready(v, epoch) && ++spins <= kSpinLimit && !call_failed(err_flag));
+    if (!row_result_ready(v, epoch) && lane_id() == 0) atomicOr(err_flag, 1u);
+  }
+  return v;
+}
+
+}  // namespace rowstats

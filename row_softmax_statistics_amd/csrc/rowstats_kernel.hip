@@ -34,6 +34,7 @@
 // if 1 - u <= exp(s - zlb), which follows from -log u >= 1 - u and reuses
 // the column's exp value. The few columns passing both are scored exactly
 // in fp64 and the best score wins (ties to the lower column).
+#include "chunk_common.h"
 #include "device_common.h"
 #include "device_math.h"
 #include "rowstats_internal.h"
@@ -45,23 +46,12 @@ namespace rowstats {
 
 constexpr int kThreads = kRowThreads;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kQ = kWaveQuads;
-// Polls of one wait before it gives up and flags the call (about a second);
-// once any wait has given up, every later wait of the call gives up at once.
-constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr float kLog2e = 1.44269504088896340736f;
 // 2^32 exp(-22.8739) = 0.49998, lowered for the 2^-13 error of -log u and
 // the rounding of e: a quad whose exp values are all below kQuadSkip / a,
 // a = -log u of the bound's word, cannot reach the bound.
 constexpr float kQuadSkip = 0.4993f;
 constexpr float kTestMargin = 1.0f + 0x1p-10f;
-// Cache-policy bit sc1: a device-scope coherent load or store (the CU's L1
-// is bypassed and the access is coherent across XCDs).
-constexpr int kDevScope = 16;
-// Rows between publishing a row's summary and reading its result.
-constexpr int kLag = 3;
-
-typedef __attribute__((address_space(3))) void *LdsPtr;
 
 // A wave, chunk or row summary relative to its own maximum m.
 struct Tuple {
@@ -73,8 +63,6 @@ struct Tuple {
   int32_t zc;  // its column
   int32_t zx;  // 1: zb is exact (fp64); 0: fp32 estimate, within 2^-9 of exact
 };
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ Tuple empty_tuple() {
   Tuple t;
@@ -138,10 +126,6 @@ __device__ __forceinline__ Rsrc tuple_rsrc(const RowStatsParams &p, int64_t row)
   return make_rsrc(p.tuples + row * p.C * (kTupleBytes / 8), (uint32_t)(p.C * kTupleBytes));
 }
 
-__device__ __forceinline__ Rsrc rowres_rsrc(const RowStatsParams &p, int64_t row) {
-  return make_rsrc(p.rowres + row * (kRowResultBytes / 8), (uint32_t)kRowResultBytes);
-}
-
 __device__ __forceinline__ uint32_t tuple_payload(const Tuple &t, int k) {
   switch (k) {
     case 0: return __float_as_uint(t.m);
@@ -184,19 +168,6 @@ __device__ __forceinline__ bool read_tuple(const Rsrc &r, int member, uint32_t e
           (c[1] == epoch) & (c[3] == epoch) & (d[1] == epoch) & (d[3] == epoch)) != 0;
 }
 
-// The row result read by the probs writers: (m, 1 / S), both tagged.
-__device__ __forceinline__ u32x4 load_rowres(const RowStatsParams &p, int64_t row) {
-  return __builtin_amdgcn_raw_buffer_load_b128(rowres_rsrc(p, row), 0u, 0, kDevScope);
-}
-__device__ __forceinline__ bool rowres_ready(const u32x4 &v, uint32_t epoch) {
-  return ((v[1] == epoch) & (v[3] == epoch)) != 0;
-}
-
-// Whether some wait of this call has already given up.
-__device__ __forceinline__ bool call_failed(const RowStatsParams &p) {
-  return __hip_atomic_load(p.err_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-}
-
 __device__ __forceinline__ void write_row_outputs(const RowStatsParams &p, int64_t row,
                                                   bool greedy, const Tuple &r) {
   // H = log S - W / S, every exp value carrying a 2^32 factor
@@ -235,7 +206,7 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
     uint32_t spins = 0;
     while (!read_tuple(r, i, p.epoch, t)) {
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit || call_failed(p)) {
+      if (++spins > kSpinLimit || call_failed(p.err_flag)) {
         atomicOr(p.err_flag, 1u);
         break;
       }
@@ -287,78 +258,8 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
     write_row_outputs(p, row, greedy, m);
     // the row result: with probs the writers need it, without probs it only
     // paces the members
-    const u32x4 v = {__float_as_uint(m.m), p.epoch, __float_as_uint((float)(1.0 / m.S)), p.epoch};
-    __builtin_amdgcn_raw_buffer_store_b128(v, rowres_rsrc(p, row), 0u, 0, kDevScope);
+    store_row_result(p.rowres, row, __float_as_uint(m.m), __float_as_uint((float)(1.0 / m.S)), p.epoch);
   }
-}
-
-// ---------------------------------------------------------------------------
-// Chunk transfers. Lane l holds quads j * 64 + l (j < 8) of the chunk, so
-// each load instruction of the wave covers 1 KiB of contiguous logits; the
-// buffer descriptor stops at the row end (loads past it read 0 and are masked
-// to -inf, stores past it are dropped).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ Rsrc chunk_rsrc(const float *xrow, int32_t c0, int32_t V) {
-  // the size is wave-uniform; readfirstlane keeps it (and the descriptor) in
-  // scalar registers even where the compiler clamps it with a vector op
-  const int32_t cols = __builtin_amdgcn_readfirstlane(max(min(V - c0, kChunkCols), 0));
-  return make_rsrc(xrow + c0, 4u * (uint32_t)cols);
-}
-
-// Vector path: asynchronous copy of the chunk into the wave's LDS buffer
-// (quad j * 64 + l at buf[j * 64 + l]).
-__device__ __forceinline__ void chunk_copy_async(float4 *buf, const float *xrow, int32_t c0,
-                                                 int32_t V) {
-  const Rsrc r = chunk_rsrc(xrow, c0, V);
-  const uint32_t voff = 16u * lane_id();
-#pragma unroll
-  for (int j = 0; j < kQ; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(buf + j * kWave), 16, voff,
-                                             16 * kWave * j, 0, 0);
-}
-
-// Scalar path (unaligned rows or vocab % 4 != 0): four 4-byte loads a quad.
-__device__ __forceinline__ void chunk_load(float4 (&v)[kQ], const float *xrow, int32_t c0,
-                                           int32_t V) {
-  const Rsrc r = chunk_rsrc(xrow, c0, V);
-  const uint32_t voff = 16u * lane_id();
-#pragma unroll
-  for (int j = 0; j < kQ; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      set_comp(v[j], i,
-               __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 16 * kWave * j + 4 * i, 0)));
-}
-
-// Read of the wave's LDS buffer, written as inline assembly (ending with its
-// own lgkmcnt wait): the compiler would otherwise wait for every copy still
-// in flight into LDS before the read, including the one it must overlap.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t lds_addr(const float4 *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float4 *)p;
-}
-
-// Quads j * 64 + lane (j < 8) of the buffer at `buf`.
-__device__ __forceinline__ void lds_read_chunk(float4 (&v)[kQ], const float4 *buf) {
-  const uint32_t a = lds_addr(buf) + 16u * (uint32_t)lane_id();
-  f32x4 r0, r1, r2, r3, r4, r5, r6, r7;
-  __asm__ volatile(
-      "ds_read_b128 %0, %8\n"
-      "ds_read_b128 %1, %8 offset:1024\n"
-      "ds_read_b128 %2, %8 offset:2048\n"
-      "ds_read_b128 %3, %8 offset:3072\n"
-      "ds_read_b128 %4, %8 offset:4096\n"
-      "ds_read_b128 %5, %8 offset:5120\n"
-      "ds_read_b128 %6, %8 offset:6144\n"
-      "ds_read_b128 %7, %8 offset:7168\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-      : "v"(a)
-      : "memory");
-  const f32x4 r[kQ] = {r0, r1, r2, r3, r4, r5, r6, r7};
-#pragma unroll
-  for (int j = 0; j < kQ; ++j) v[j] = make_float4(r[j][0], r[j][1], r[j][2], r[j][3]);
 }
 
 // cm = 2 cm + (a >= b): the compare writes VCC and the add takes it as the
@@ -369,21 +270,6 @@ __device__ __forceinline__ uint32_t push_bit_ge(uint32_t cm, float a, float b) {
           : "v"(a), "v"(b)
           : "vcc");
   return cm;
-}
-
-// s_waitcnt vmcnt(n): at most n of this wave's vector memory operations are
-// still outstanding. They complete in issue order, so an operation followed
-// by at least n others has completed.
-// Keeps the compiler from moving memory operations across this point, so
-// the counts above hold for the issue order written here.
-__device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  compiler_fence();
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-  compiler_fence();
 }
 
 // ---------------------------------------------------------------------------
@@ -611,22 +497,6 @@ __device__ __forceinline__ void write_probs(const RowStatsParams &p, int64_t row
   }
 }
 
-// Waits until the row result of `row` (pre-loaded in v) shows this call's
-// epoch; returns it.
-__device__ __forceinline__ u32x4 wait_row_result(const RowStatsParams &p, int64_t row, u32x4 v) {
-  // the retry loop sits off the common path: a loop header there would make
-  // the compiler wait for every outstanding copy before the first check
-  if (!rowres_ready(v, p.epoch)) {
-    uint32_t spins = 0;
-    do {
-      __builtin_amdgcn_s_sleep(1);
-      v = load_rowres(p, row);
-    } while (!rowres_ready(v, p.epoch) && ++spins <= kSpinLimit && !call_failed(p));
-    if (!rowres_ready(v, p.epoch) && lane_id() == 0) atomicOr(p.err_flag, 1u);
-  }
-  return v;
-}
-
 // ---------------------------------------------------------------------------
 // The kernel. Global wave gw belongs to group gw / C as member gw % C: the
 // group reduces rows group, group + n_groups, ..., the member chunk `member`
@@ -676,7 +546,7 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
     // row result of row n - kLag, written by its merger more than a chunk
     // ago (loaded every time so that no path leaves the register waiting on
     // a load)
-    u32x4 rr = load_rowres(p, row_of(n >= kLag ? n - kLag : 0));
+    u32x4 rr = load_row_result(p.rowres, row_of(n >= kLag ? n - kLag : 0));
     compiler_fence();
     if constexpr (VEC) {
       // after this item's copy came, in the previous item, its eight probs
@@ -698,7 +568,7 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
     // so the wait for its load is placed here, exactly.
     __asm__ volatile("" ::"v"(rr));
     if (n >= kLag) {
-      rr = wait_row_result(p, row_of(n - kLag), rr);
+      rr = wait_row_result(p.rowres, row_of(n - kLag), rr, p.epoch, p.err_flag);
       if constexpr (PROBS != 0)
         write_probs<PROBS, VEC>(p, row_of(n - kLag), chunk, p3,
                                 prob_scale(m3, __uint_as_float(rr[0]), __uint_as_float(rr[2])));
@@ -726,7 +596,7 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
     auto finish = [&](int64_t n, const float4 (&e)[kQ], float mw) {
       if (n < 0) return;
       const int64_t r = row_of(n);
-      const u32x4 v = wait_row_result(p, r, load_rowres(p, r));
+      const u32x4 v = wait_row_result(p.rowres, r, load_row_result(p.rowres, r), p.epoch, p.err_flag);
       write_probs<PROBS, VEC>(p, r, chunk, e, prob_scale(mw, __uint_as_float(v[0]), __uint_as_float(v[2])));
     };
     finish(nrows - 3, p3, m3);

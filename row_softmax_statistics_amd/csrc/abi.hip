@@ -37,13 +37,11 @@ constexpr int kMaxDevices = 64;
 // the top-K key stores 0x7FFFFFFF - column: keep them all below 2^31.
 constexpr int64_t kMaxVocab = 0x7FFFFFFFLL - 65536;
 
-// Scratch of one device, grow-only.
-//  - row-statistics scratch: tagged member summaries and row results; zeroed
-//    when allocated, after which words are only ever told apart by the call
-//    epoch in their high half (epoch 0 never occurs);
-//  - top-K scratch: slice records and two banks of row counters of
-//    counters_len / 2 words; a call counts in bank `parity` and its kernel
-//    zeroes the other bank, which the next call uses.
+// Scratch of one device, grow-only, shared by both entry points: the
+// waves' tagged summaries (row-statistics tuples or top-K records), row
+// results and, for top-K, the kept-row list. Zeroed when allocated, after
+// which tagged words are only ever told apart by the call epoch in their
+// high half (epoch 0 never occurs; every call takes the next epoch).
 struct DeviceState {
   bool ready = false;
   int cus = 0;
@@ -51,13 +49,8 @@ struct DeviceState {
   int topk_resident[2] = {};
   void *row_scratch = nullptr;
   size_t row_scratch_bytes = 0;
-  uint32_t epoch = 0;            // epoch of the last row-statistics call
-  void *partials = nullptr;
-  size_t partials_bytes = 0;
-  uint32_t *counters = nullptr;
-  size_t counters_len = 0;
+  uint32_t epoch = 0;       // epoch of the last call
   uint32_t *err_flag = nullptr;
-  int parity = 0;                // top-K counter bank of the next call
 };
 
 std::mutex g_mu;
@@ -106,38 +99,6 @@ int device_state(DeviceState **out) {
   return ROWSTATS_OK;
 }
 
-int ensure_scratch(DeviceState &d, size_t partial_bytes, size_t counters, hipStream_t s) {
-  hipError_t e;
-  if (partial_bytes > d.partials_bytes) {
-    if (d.partials) {
-      e = hipFree(d.partials);
-      if (e != hipSuccess) return fail_hip(e, "hipFree(partials)");
-      d.partials = nullptr;
-      d.partials_bytes = 0;
-    }
-    size_t cap = partial_bytes + partial_bytes / 4;
-    e = hipMalloc(&d.partials, cap);
-    if (e != hipSuccess) return fail_hip(e, "hipMalloc(partials)");
-    d.partials_bytes = cap;
-  }
-  if (counters > d.counters_len) {
-    if (d.counters) {
-      e = hipFree(d.counters);
-      if (e != hipSuccess) return fail_hip(e, "hipFree(counters)");
-      d.counters = nullptr;
-      d.counters_len = 0;
-    }
-    size_t cap = counters + counters / 4 + 64;
-    e = hipMalloc(&d.counters, cap * sizeof(uint32_t));
-    if (e != hipSuccess) return fail_hip(e, "hipMalloc(counters)");
-    d.counters_len = cap;
-    e = zero_async(d.counters, cap, s);
-    if (e != hipSuccess) return fail_hip(e, "zeroing counters");
-  }
-  return ROWSTATS_OK;
-}
-
-// Row-statistics scratch of at least `bytes`; a new buffer is zeroed.
 int ensure_row_scratch(DeviceState &d, size_t bytes, hipStream_t s) {
   if (bytes <= d.row_scratch_bytes) return ROWSTATS_OK;
   hipError_t e;
@@ -154,6 +115,18 @@ int ensure_row_scratch(DeviceState &d, size_t bytes, hipStream_t s) {
   d.row_scratch_bytes = cap;
   e = zero_async(reinterpret_cast<uint32_t *>(d.row_scratch), cap / 4, s);
   if (e != hipSuccess) return fail_hip(e, "zeroing row scratch");
+  return ROWSTATS_OK;
+}
+
+// The epoch of a new call (clearing the scratch when the counter wraps).
+int next_epoch(DeviceState &d, hipStream_t s, uint32_t *epoch) {
+  if (++d.epoch == 0) {
+    // the epoch wrapped: clear every tag it could still match
+    hipError_t e = zero_async(reinterpret_cast<uint32_t *>(d.row_scratch), d.row_scratch_bytes / 4, s);
+    if (e != hipSuccess) return fail_hip(e, "zeroing scratch");
+    d.epoch = 1;
+  }
+  *epoch = d.epoch;
   return ROWSTATS_OK;
 }
 
@@ -233,13 +206,7 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
   const size_t tuple_bytes = (size_t)rows * p.C * kTupleBytes;
   const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
   if ((rc = ensure_row_scratch(*d, tuple_bytes + rowres_bytes, s))) return rc;
-  if (++d->epoch == 0) {
-    // the epoch wrapped: clear every tag it could still match
-    hipError_t e = zero_async(reinterpret_cast<uint32_t *>(d->row_scratch), d->row_scratch_bytes / 4, s);
-    if (e != hipSuccess) return fail_hip(e, "zeroing row scratch");
-    d->epoch = 1;
-  }
-  p.epoch = d->epoch;
+  if ((rc = next_epoch(*d, s, &p.epoch))) return rc;
   p.tuples = reinterpret_cast<uint64_t *>(d->row_scratch);
   p.rowres = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(d->row_scratch) + tuple_bytes);
   p.err_flag = d->err_flag;
@@ -272,31 +239,42 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   p.ld = row_stride;
   p.rows = rows;
   p.vocab = (int32_t)vocab;
-  p.nq = (int32_t)((vocab + 3) / 4);
-  p.nq_full = (int32_t)(vocab / 4);
-  p.G = (p.nq + kTopKThreads * kTopKQPT - 1) / (kTopKThreads * kTopKQPT);
+  p.C = (int32_t)((vocab + kChunkCols - 1) / kChunkCols);
   p.vec_ok = ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) && (row_stride % 4 == 0) &&
              (vocab % 4 == 0);
+  p.K = K;
   p.temps = temps;
   p.canvas_len = canvas_len;
   p.keep = keep_mask;
-  p.K = K;
   p.out_vals = out_vals;
   p.out_idx = out_idx;
-  const int64_t resident = (int64_t)d->topk_resident[p.vec_ok] * d->cus;
-  if (resident < 1) return fail(ROWSTATS_ERR_HIP, "top-K kernel cannot be resident");
-  const int64_t items = rows * (int64_t)p.G;
-  const int64_t grid = items < resident ? items : resident;
-  p.xcd_map = (grid % 8 == 0);
-  if ((rc = ensure_scratch(*d, (size_t)rows * p.G * topk_partial_bytes(K), 2 * (size_t)rows, s)))
-    return rc;
-  p.partials = d->partials;
-  p.counters = d->counters;
-  p.counter_stride = (int64_t)(d->counters_len / 2);
-  p.parity = d->parity;
+
+  // As for rowstats_run: every wave resident, a row's C member waves at once.
+  constexpr int kWavesPerBlock = kRowThreads / 64;
+  const int64_t waves = (int64_t)d->topk_resident[p.vec_ok] * d->cus * kWavesPerBlock;
+  if (waves < 1) return fail(ROWSTATS_ERR_HIP, "top-K kernel cannot be resident");
+  if (p.C > waves || p.C > 64 * 64)
+    return fail(ROWSTATS_ERR_COOP,
+                "vocab %lld needs %d co-resident waves per row, the device holds %lld",
+                (long long)vocab, p.C, (long long)waves);
+  int64_t groups = waves / p.C;
+  if (groups > rows) groups = rows;
+  p.n_groups = (int32_t)groups;
+  const int64_t grid = (groups * p.C + kWavesPerBlock - 1) / kWavesPerBlock;
+
+  // records and row results are indexed by kept position (at most rows)
+  const size_t record_bytes = (size_t)rows * p.C * topk_record_bytes(K);
+  const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
+  const size_t kept_bytes = ((size_t)rows + 1) * sizeof(int64_t);
+  if ((rc = ensure_row_scratch(*d, record_bytes + rowres_bytes + kept_bytes, s))) return rc;
+  if ((rc = next_epoch(*d, s, &p.epoch))) return rc;
+  char *base = reinterpret_cast<char *>(d->row_scratch);
+  p.records = reinterpret_cast<uint64_t *>(base);
+  p.rowres = reinterpret_cast<uint64_t *>(base + record_bytes);
+  p.kept = reinterpret_cast<int64_t *>(base + record_bytes + rowres_bytes);
+  p.err_flag = d->err_flag;
   hipError_t e = topk_launch(p, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "top-K kernel launch");
-  d->parity ^= 1;
   return ROWSTATS_OK;
 }
 
@@ -313,14 +291,8 @@ int rowstats_check_device(void *stream) {
   e = hipMemcpy(&flag, d->err_flag, sizeof flag, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpy(error flag)");
   if (flag == 0) return ROWSTATS_OK;
-  // a wait ran out: top-K counters of that call may be left non-zero
   e = hipMemset(d->err_flag, 0, sizeof(uint32_t));
   if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
-  if (d->counters) {
-    e = zero_async(d->counters, d->counters_len, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return fail_hip(e, "zeroing counters");
-  }
   return fail(ROWSTATS_ERR_DEVICE, "a kernel flagged an inter-workgroup wait that ran out (flag %u)",
               flag);
 }
@@ -336,8 +308,6 @@ int rowstats_release(void) {
     if (!d.ready) continue;
     if ((e = hipSetDevice(dev)) != hipSuccess) return fail_hip(e, "hipSetDevice");
     if (d.row_scratch) (void)hipFree(d.row_scratch);
-    if (d.partials) (void)hipFree(d.partials);
-    if (d.counters) (void)hipFree(d.counters);
     if (d.err_flag) (void)hipFree(d.err_flag);
     d = DeviceState();
   }

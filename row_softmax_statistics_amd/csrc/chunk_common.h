@@ -37,7 +37,6 @@ __device__ __forceinline__ void wait_vm() {
   compiler_fence();
 }
 
-
 // ---------------------------------------------------------------------------
 // Chunk transfers. Lane l holds quads j * 64 + l (j < 8) of the chunk, so
 // each load instruction of the wave covers 1 KiB of contiguous logits; the
@@ -117,6 +116,15 @@ __device__ __forceinline__ void lds_read_chunk(float4 (&v)[kQ], const float4 *bu
   for (int j = 0; j < kQ; ++j) v[j] = make_float4(r[j][0], r[j][1], r[j][2], r[j][3]);
 }
 
+// cm = 2 cm + (a >= b): the compare writes VCC and the add takes it as the
+// carry in (the compiler would spend a select and a shift instead).
+__device__ __forceinline__ uint32_t push_bit_ge(uint32_t cm, float a, float b) {
+  __asm__("v_cmp_ge_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+          : "+v"(cm)
+          : "v"(a), "v"(b)
+          : "vcc");
+  return cm;
+}
 
 // ---------------------------------------------------------------------------
 // Row results: two 64-bit words per row, a 32-bit payload each with the

@@ -262,16 +262,6 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
   }
 }
 
-// cm = 2 cm + (a >= b): the compare writes VCC and the add takes it as the
-// carry in (the compiler would spend a select and a shift instead).
-__device__ __forceinline__ uint32_t push_bit_ge(uint32_t cm, float a, float b) {
-  __asm__("v_cmp_ge_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
-          : "+v"(cm)
-          : "v"(a), "v"(b)
-          : "vcc");
-  return cm;
-}
-
 // ---------------------------------------------------------------------------
 // Reduction of one chunk. On entry v holds the chunk's raw logits; on return
 // v holds the exp values 2^32 exp(s - m) of the wave and every lane holds the

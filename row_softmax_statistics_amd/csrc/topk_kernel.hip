@@ -9,18 +9,30 @@
 // distinct elements at or above the K-th largest block maximum, so nothing
 // below it can be in the top-K).
 //
-// Work split. As in the row-statistics kernel, a row is cut into G slices
-// held in registers by one workgroup each (every logit read once). Inside a
-// slice the "blocks" of the threshold rule are the 64 lane-owned column sets
-// of a wave (64 columns each, strided): the K-th largest lane maximum v_K of
-// a wave bounds that wave's top-K from below, so only columns with s >= v_K
-// become candidates. Candidates go to an LDS list and are ranked exactly
-// (rank = number of larger keys); a wave whose list would overflow falls
-// back to K rounds of exact max extraction over its registers. Wave results
-// merge into the slice's top-K, which is published with the slice's
-// (max, sum exp) pair; the last slice of a row to arrive merges the G
-// top-K lists, forms log Z and writes the row.
+// Work split. A small pre-pass writes the list of kept rows. Then, as in
+// the row-statistics kernel, a group of C member waves reduces one kept row
+// at a time, one chunk of 2048 columns per wave, with the next chunk copied
+// into the wave's LDS buffer while the current one is reduced; each logit
+// of a kept row is read from HBM once and rows of other slots not at all.
+//
+// A wave reduces its chunk to a record: (m, S = sum exp(s - m)) and the
+// chunk's K largest keys in rank order. The blocks of the threshold rule
+// are the 64 lanes (32 columns each): with v_K the K-th largest lane
+// maximum, only columns with s >= v_K can be in the chunk's top-K (about
+// K + a few on typical rows). They are listed in LDS and ranked exactly
+// (rank = number of larger keys). A chunk where the rule leaves too many
+// columns (long runs of equal values) takes K rounds of exact extraction.
+//
+// One member per row (the merger, rotating) reads the row's C records one
+// row later: the headers give log Z; the K-th largest of the lanes' largest
+// chunk maxima is again a lower bound of the row's K-th key, and since each
+// record is sorted, a record is read slot by slot only while its keys stay
+// at or above that bound. The keys read are ranked in LDS together with the
+// running top-K. The merger writes the row's logprobs and a row result that
+// keeps the members in step (as in the row-statistics kernel).
+#include "chunk_common.h"
 #include "device_common.h"
+#include "device_math.h"
 #include "topk_internal.h"
 
 #include <float.h>
@@ -29,233 +41,561 @@
 namespace rowstats {
 namespace {
 
-constexpr int kT = kTopKThreads;
-constexpr int kWv = kT / kWave;
-constexpr int kCandCap = 256;    // candidate keys per wave
-constexpr int kMergeCap = 2048;  // keys ranked per round of the row merge
+constexpr int kThreads = kRowThreads;
+constexpr int kWaves = kThreads / kWave;
+constexpr float kLog2e = 1.44269504088896340736f;
+// LDS keys per wave for candidate lists; the last two places of a list are
+// end markers, so a list holds at most kCandCap keys.
+constexpr int kCandKeys = 256;
+constexpr int kCandCap = kCandKeys - 2;
+constexpr uint64_t kSignBit = 0x8000000000000000ull;
 
-struct TopKShared {
-  int64_t buf[kMergeCap];           // per-wave candidate lists, then the row merge
-  int64_t wtop[kWv * kTopKMax];     // top-K of each wave
-  int64_t tops[kTopKMax];           // top-K of the slice / running row top-K
-  double red_d[kWv];
-  float red_f[kWv];
-  int32_t red_i[kWv];
-  int32_t flag;
-};
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
-// Exact top-K of n distinct keys in LDS by rank; writes out[rank] for the
-// keys of rank < K. Threads [first, first + stride) take keys in turn.
-__device__ __forceinline__ void rank_select(const int64_t *keys, int n, int K, int64_t *out,
-                                            int first, int stride) {
-  for (int i = first; i < n; i += stride) {
-    const int64_t ki = keys[i];
-    int r = 0;
-    for (int j = 0; j < n; ++j) r += (keys[j] > ki) ? 1 : 0;
-    if (r < K) out[r] = ki;
+// ---------------------------------------------------------------------------
+// Records: header {m | e, S | e}, then K keys as {high | e, low | e}.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t record_bytes(int K) { return 16u * (uint32_t)(K + 1); }
+
+__device__ __forceinline__ Rsrc records_rsrc(const TopKParams &p, int64_t pos) {
+  const uint32_t rb = record_bytes(p.K);
+  return make_rsrc(reinterpret_cast<const char *>(p.records) + pos * p.C * (int64_t)rb,
+                   (uint32_t)p.C * rb);
+}
+
+__device__ __forceinline__ u32x4 key_words(int64_t k, uint32_t e) {
+  const uint64_t u = (uint64_t)k;
+  return u32x4{(uint32_t)(u >> 32), e, (uint32_t)u, e};
+}
+__device__ __forceinline__ uint64_t words_ukey(const u32x4 &w) {
+  // the key in unsigned order (sign bit flipped): INT64_MIN, "no key", is 0
+  return (((uint64_t)w[0] << 32) | (uint64_t)w[2]) ^ kSignBit;
+}
+__device__ __forceinline__ bool words_ready(const u32x4 &w, uint32_t e) {
+  return ((w[1] == e) & (w[3] == e)) != 0;
+}
+
+__device__ __forceinline__ u32x4 load_words(const Rsrc &r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDevScope);
+}
+
+// Re-polls a pair of tagged words that did not yet show this call's epoch.
+__device__ __forceinline__ u32x4 poll_words(Rsrc r, uint32_t off, uint32_t epoch, uint32_t *err_flag) {
+  u32x4 w;
+  uint32_t spins = 0;
+  do {
+    __builtin_amdgcn_s_sleep(1);
+    w = load_words(r, off);
+  } while (!words_ready(w, epoch) && ++spins <= kSpinLimit && !call_failed(err_flag));
+  if (!words_ready(w, epoch)) atomicOr(err_flag, 1u);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide helpers.
+// ---------------------------------------------------------------------------
+// Exclusive prefix sum over the lanes of cnt (0 <= cnt < 128) and the wave
+// total, one bit of cnt at a time: a ballot of the bit and mbcnt (set bits
+// of lower lanes).
+__device__ __forceinline__ int wave_prefix(int cnt, int &total) {
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 7; ++b) {
+    const uint64_t m = __ballot((cnt >> b) & 1);
+    off += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))
+           << b;
+    tot += __popcll(m) << b;
+    if (__ballot(cnt >> (b + 1)) == 0) break;
+  }
+  total = tot;
+  return off;
+}
+
+// The k-th largest (1 <= k <= 64) over the lanes of u, in unsigned order.
+// Bits are fixed from the top: a bit is set when at least k lanes are at or
+// above the prefix with that bit set.
+template <class U>
+__device__ __forceinline__ U wave_kth_largest(U u, int k) {
+  U res = 0;
+#pragma unroll
+  for (int b = 8 * (int)sizeof(U) - 1; b >= 0; --b) {
+    const U c = res | ((U)1 << b);
+    res = (__popcll(__ballot(u >= c)) >= k) ? c : res;
+  }
+  return res;
+}
+
+// Element k (0..31) of the lane's chunk registers. A per-lane index into
+// registers would go through scratch memory, so this is a tree of selects
+// on the bits of k. The empty statements hand the selects register values:
+// selects between two array elements would otherwise be turned back into
+// one indexed load.
+__device__ __forceinline__ float element_at(const float4 (&v)[kQ], uint32_t k) {
+  const bool b0 = (k & 1u) != 0, b1 = (k & 2u) != 0, b2 = (k & 4u) != 0, b3 = (k & 8u) != 0,
+             b4 = (k & 16u) != 0;
+  float q[kQ];
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) {
+    float x = v[j].x, y = v[j].y, z = v[j].z, w = v[j].w;
+    __asm__("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
+    q[j] = b1 ? (b0 ? w : z) : (b0 ? y : x);
+  }
+  const float a0 = b2 ? q[1] : q[0], a1 = b2 ? q[3] : q[2], a2 = b2 ? q[5] : q[4],
+              a3 = b2 ? q[7] : q[6];
+  const float c0 = b3 ? a1 : a0, c1 = b3 ? a3 : a2;
+  return b4 ? c1 : c0;
+}
+
+// Keeps the compiler's LDS accesses in program order between lanes of a
+// wave (the hardware executes a wave's LDS operations in order).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// Ranks of the keys of an LDS list of n <= 64 NX keys (distinct, except for
+// INT64_MIN): key[x] = list[lane + 64 x], rank[x] = the number of list keys
+// above it (INT_MAX past the list end). list[n] and list[n + 1] must hold
+// INT64_MIN.
+template <int NX>
+__device__ __forceinline__ void rank_keys(const int64_t *list, int n, int64_t (&key)[4],
+                                          int (&rank)[4]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    const int idx = lane + x * kWave;
+    key[x] = idx < n ? list[idx] : INT64_MIN;
+    rank[x] = 0;
+  }
+  for (int j = 0; j < n; j += 2) {
+    const i64x2 pr = *reinterpret_cast<const i64x2 *>(list + j);
+#pragma unroll
+    for (int x = 0; x < NX; ++x) rank[x] += (int)(pr[0] > key[x]) + (int)(pr[1] > key[x]);
+  }
+#pragma unroll
+  for (int x = 0; x < NX; ++x)
+    if (lane + x * kWave >= n) rank[x] = INT_MAX;
+#pragma unroll
+  for (int x = NX; x < 4; ++x) {
+    key[x] = INT64_MIN;
+    rank[x] = INT_MAX;
   }
 }
 
-struct SliceRecord {
-  double S;   // sum over the slice of 2^32 exp(s - m)
-  float m;    // slice max of s
-  int32_t pad;
-  // followed by K int64 keys
-};
-
-__device__ __forceinline__ int64_t *record_keys(SliceRecord *r) {
-  return reinterpret_cast<int64_t *>(reinterpret_cast<char *>(r) + 16);
+__device__ __forceinline__ void rank_list(const int64_t *list, int n, int64_t (&key)[4],
+                                          int (&rank)[4]) {
+  if (n <= kWave) rank_keys<1>(list, n, key, rank);
+  else if (n <= 2 * kWave) rank_keys<2>(list, n, key, rank);
+  else if (n <= 3 * kWave) rank_keys<3>(list, n, key, rank);
+  else rank_keys<4>(list, n, key, rank);
 }
 
-template <int QPT, bool VEC>
-__device__ void topk_slice(const TopKParams &p, int64_t row, int g, TopKShared &sh) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+// ---------------------------------------------------------------------------
+// Reduction of one chunk to its record. On return lanes hold (key[x],
+// rank[x]) pairs: the keys of rank < K are the chunk's top-K (INT64_MIN
+// where the chunk has fewer than K columns); mw and S are the header.
+// ---------------------------------------------------------------------------
+struct ChunkTop {
+  int64_t key[4];
+  int rank[4];
+  float mw;
+  float S;
+};
+
+template <bool VEC>
+__device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, int64_t row, int32_t chunk,
+                                                  float4 (&v)[kQ], int64_t *cand, ChunkTop &out) {
+  const int lane = lane_id();
   const int32_t V = p.vocab;
   const int K = p.K;
-  const float Tc = clamp_temp(p.temps[row / p.canvas_len]);
-  const double rtc = 1.0 / (double)Tc;
-  const float *xrow = p.logits + row * p.ld;
-  const int32_t q0 = g * (kT * QPT);
+  const float T = load_uniform(p.temps + row / p.canvas_len);
+  const double rtc = 1.0 / (double)clamp_temp(T);
+  const int32_t c0 = chunk * kChunkCols;
+  // column of element 0 of this lane. The columns are the same for every
+  // row of this wave: without this the compiler computes the fallback's
+  // keys of all 32 columns once, outside the row loop, and spills them.
+  int32_t cl = c0 + 4 * lane;
+  __asm__ volatile("" : "+v"(cl));
+  auto col_of = [&](uint32_t k) -> int32_t {
+    return cl + 4 * (int32_t)(k >> 2) * kWave + (int32_t)(k & 3u);
+  };
 
-  float4 v[QPT];
-  const float mt = load_scaled_slice<QPT, kT, VEC>(xrow, q0, V, rtc, v);
-  const float ml = block_allreduce<kT>(mt, MaxF(), sh.red_f);
-  const float mu = (ml == -INFINITY) ? 0.0f : ml;
-  constexpr float kLog2e = 1.44269504088896340736f;
+  // ---- mask the row end, scale s = fl32(x / Tc) ----
+  const int32_t left = V - c0;
+  if (left < kChunkCols) {
+#pragma unroll
+    for (int j = 0; j < kQ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        set_comp(v[j], i, (4 * (j * kWave + lane) + i < left) ? comp(v[j], i) : -INFINITY);
+  }
+  float mt = -INFINITY;
+  if (T == 1.0f) {  // x / 1 = x
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) mt = fmaxf(mt, max4(v[j]));
+  } else {
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      v[j].x = scale(v[j].x, rtc);
+      v[j].y = scale(v[j].y, rtc);
+      v[j].z = scale(v[j].z, rtc);
+      v[j].w = scale(v[j].w, rtc);
+      mt = fmaxf(mt, max4(v[j]));
+    }
+  }
+  const float mw = wave_allreduce(mt, MaxF());
+
+  // ---- S = sum exp(s - m) of the chunk (1 <= S <= 2048 unless empty) ----
+  const float mu = (mw == -INFINITY) ? 0.0f : mw;
   float St = 0.0f;
 #pragma unroll
-  for (int j = 0; j < QPT; ++j)
+  for (int j = 0; j < kQ; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      St += __builtin_amdgcn_exp2f(fmaf(fmaxf(comp(v[j], i) - mu, -FLT_MAX), kLog2e, 32.0f));
-  const double Sl = block_allreduce<kT>((double)St, SumD(), sh.red_d);
+    for (int i = 0; i < 4; ++i) St += __builtin_amdgcn_exp2f((comp(v[j], i) - mu) * kLog2e);
+  out.mw = mw;
+  out.S = (float)wave_allreduce((double)St, SumD());
 
-  // ---- wave threshold: K-th largest lane maximum (ties ranked by lane) ----
-  float vK = -INFINITY;
-  if (K <= kWave) {
-    int rank = 0;
+  // ---- threshold: the K-th largest lane maximum ----
+  const uint32_t uk = wave_kth_largest<uint32_t>((uint32_t)key32(mt) ^ 0x80000000u, K);
+  const float vk = key32_value((int32_t)(uk ^ 0x80000000u));
+  // Bit 31 - k of cm: element k is a candidate (s >= v_K). With v_K > -inf
+  // the K lanes whose maxima reach v_K give at least K candidates, all real
+  // columns (masked ones are -inf).
+  uint32_t cm = 0;
 #pragma unroll
-    for (int l = 0; l < kWave; ++l) {
-      const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mt), l));
-      rank += (o > mt || (o == mt && l < lane)) ? 1 : 0;
+  for (int j = 0; j < kQ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cm = push_bit_ge(cm, comp(v[j], i), vk);
+  int total;
+  const int off = wave_prefix(__popc(cm), total);
+
+  if (vk != -INFINITY && total <= kCandCap) {
+    int o = off;
+    for (uint32_t c2 = cm; c2 != 0;) {
+      const uint32_t k = (uint32_t)__builtin_clz(c2);
+      c2 &= ~(0x80000000u >> k);
+      cand[o++] = key64(element_at(v, k), col_of(k));
     }
-    const uint64_t hit = __ballot(rank == K - 1);  // exactly one lane
-    if (hit != 0)
-      vK = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mt), __builtin_ctzll(hit)));
-  }
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < QPT; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cnt += (comp(v[j], i) >= vK) ? 1 : 0;
-  int incl = cnt;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
-  }
-  const int total = __shfl(incl, kWave - 1, kWave);
-  int64_t *cand = sh.buf + wave * kCandCap;
-  int64_t *wtop = sh.wtop + wave * kTopKMax;
-  const bool fits = total <= kCandCap;
-  if (fits) {
-    int off = incl - cnt;
-#pragma unroll
-    for (int k = 0; k < 4 * QPT; ++k) {
-      const float sk = comp(v[k >> 2], k & 3);
-      if (sk >= vK) cand[off++] = key64(sk, slice_col<kT>(q0, k));
+    if (lane == 0) {
+      cand[total] = INT64_MIN;
+      cand[total + 1] = INT64_MIN;
     }
-  }
-  __syncthreads();
-  if (fits) {
-    rank_select(cand, total, K, wtop, lane, kWave);
+    wave_lds_order();
+    rank_list(cand, total, out.key, out.rank);
+    wave_lds_order();
   } else {
-    // exact fallback: K rounds of "largest key below the previous one"
-    int64_t prev = INT64_MAX;
-    for (int k = 0; k < K; ++k) {
+    // exact fallback: K rounds of "largest key below the previous one";
+    // lane k keeps the key of rank k
+    int64_t prev = INT64_MAX, mine = INT64_MIN;
+    for (int r = 0; r < K; ++r) {
       int64_t best = INT64_MIN;
 #pragma unroll
-      for (int k = 0; k < 4 * QPT; ++k) {
-        const int64_t key = key64(comp(v[k >> 2], k & 3), slice_col<kT>(q0, k));
-        if (key < prev && key > best) best = key;
+      for (int k = 0; k < 4 * kQ; ++k) {
+        const int32_t c = col_of((uint32_t)k);
+        const int64_t key = (c < V) ? key64(comp(v[k >> 2], k & 3), c) : INT64_MIN;
+        best = (key < prev && key > best) ? key : best;
       }
       best = wave_allreduce(best, MaxI64());
-      if (lane == 0) wtop[k] = best;
+      if (lane == r) mine = best;
       prev = best;
     }
-  }
-  __syncthreads();
-  // ---- slice top-K from the waves' top-K ----
-  for (int i = tid; i < kWv * K; i += kT) {
-    const int64_t ki = sh.wtop[(i / K) * kTopKMax + (i % K)];
-    int r = 0;
-    for (int w = 0; w < kWv; ++w)
-      for (int k = 0; k < K; ++k) r += (sh.wtop[w * kTopKMax + k] > ki) ? 1 : 0;
-    if (r < K) sh.tops[r] = ki;
-  }
-  __syncthreads();
-
-  // ---- publish the slice record (wave 0 writes, lane 0 releases) ----
-  const size_t rec_bytes = topk_partial_bytes(K);
-  char *base = reinterpret_cast<char *>(p.partials) + (size_t)row * p.G * rec_bytes;
-  uint32_t *ctr = p.counters + (size_t)p.parity * p.counter_stride + row;
-  if (wave == 0) {
-    SliceRecord *rec = reinterpret_cast<SliceRecord *>(base + (size_t)g * rec_bytes);
-    if (lane < K) record_keys(rec)[lane] = sh.tops[lane];
-    if (lane == 0) {
-      rec->S = Sl;
-      rec->m = ml;
-      rec->pad = 0;
-      const uint32_t old =
-          __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      sh.flag = (old == (uint32_t)(p.G - 1));
+    out.key[0] = mine;
+    out.rank[0] = lane;
+#pragma unroll
+    for (int x = 1; x < 4; ++x) {
+      out.key[x] = INT64_MIN;
+      out.rank[x] = INT_MAX;
     }
-  }
-  __syncthreads();
-  const bool last = sh.flag != 0;
-  __syncthreads();
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-  // ---- last slice of the row: merge G records ----
-  float m = -INFINITY;
-  for (int i = tid; i < p.G; i += kT)
-    m = fmaxf(m, reinterpret_cast<const SliceRecord *>(base + (size_t)i * rec_bytes)->m);
-  m = block_allreduce<kT>(m, MaxF(), sh.red_f);
-  double S = 0.0;
-  for (int i = tid; i < p.G; i += kT) {
-    const SliceRecord *rec = reinterpret_cast<const SliceRecord *>(base + (size_t)i * rec_bytes);
-    if (rec->S > 0.0) S += rec->S * exp((double)rec->m - (double)m);
-  }
-  S = block_allreduce<kT>(S, SumD(), sh.red_d);
-  // log Z - m, with the 2^32 factor of every exp value removed; the
-  // logprob is then (s - m) - logS, whose first difference is exact
-  const double logS = log(S) - 32.0 * 0.69314718055994530942;
-
-  const int total_keys = p.G * K;
-  int have = 0;
-  for (int pos = 0; pos < total_keys;) {
-    const int chunk = min(kMergeCap - have, total_keys - pos);
-    for (int i = tid; i < have; i += kT) sh.buf[i] = sh.tops[i];
-    for (int i = tid; i < chunk; i += kT) {
-      const int t = pos + i;
-      const SliceRecord *rec =
-          reinterpret_cast<const SliceRecord *>(base + (size_t)(t / K) * rec_bytes);
-      sh.buf[have + i] = reinterpret_cast<const int64_t *>(reinterpret_cast<const char *>(rec) + 16)[t % K];
-    }
-    __syncthreads();
-    rank_select(sh.buf, have + chunk, K, sh.tops, tid, kT);
-    __syncthreads();
-    have = K;
-    pos += chunk;
-  }
-  if (tid < K) {
-    const int64_t key = sh.tops[tid];
-    const float s = key32_value((int32_t)(key >> 32));
-    p.out_idx[row * K + tid] = key64_col(key);
-    p.out_vals[row * K + tid] = (float)(((double)s - (double)m) - logS);
   }
 }
 
-template <int QPT, bool VEC>
-__global__ __launch_bounds__(kT, 4) void topk_kernel(TopKParams p) {
-  __shared__ TopKShared sh;
-  const int nwg = gridDim.x;
-  int L = blockIdx.x;
-  if (p.xcd_map) L = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
-  // this call counts in bank `parity`; zero the other bank for the next call
-  {
-    uint32_t *other = p.counters + (size_t)(p.parity ^ 1) * p.counter_stride;
-    for (int64_t i = (int64_t)blockIdx.x * kT + threadIdx.x; i < p.counter_stride;
-         i += (int64_t)nwg * kT)
-      other[i] = 0u;
+__device__ __forceinline__ void publish_record(const TopKParams &p, int64_t pos, int32_t chunk,
+                                               const ChunkTop &t) {
+  const Rsrc r = records_rsrc(p, pos);
+  const uint32_t base = (uint32_t)chunk * record_bytes(p.K);
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    if (t.rank[x] < p.K)
+      __builtin_amdgcn_raw_buffer_store_b128(key_words(t.key[x], p.epoch), r,
+                                             base + 16u * (uint32_t)(t.rank[x] + 1), 0, kDevScope);
+  if (lane_id() == 0) {
+    const u32x4 h = {__float_as_uint(t.mw), p.epoch, __float_as_uint(t.S), p.epoch};
+    __builtin_amdgcn_raw_buffer_store_b128(h, r, base, 0, kDevScope);
   }
-  const int64_t items = p.rows * (int64_t)p.G;
-  for (int64_t it = L; it < items; it += nwg) {
-    const int64_t row = it / p.G;
-    const int g = (int)(it - row * p.G);
-    if (!p.keep[row / p.canvas_len]) continue;
-    topk_slice<QPT, VEC>(p, row, g, sh);
+}
+
+// ---------------------------------------------------------------------------
+// The merger's work for the kept row at position pos (row index `row`).
+// buf is the wave's LDS list area: the running top-K in [0, K), the keys
+// waiting to be ranked in [K, K + nb).
+// ---------------------------------------------------------------------------
+__device__ void merge_row_topk(const TopKParams &p, int64_t pos, int64_t row, int64_t *buf) {
+  const int lane = lane_id();
+  const int K = p.K, C = p.C;
+  const uint32_t rb = record_bytes(K);
+  const Rsrc r = records_rsrc(p, pos);
+
+  // ---- headers and chunk maxima of records q = lane + 64 i ----
+  float ml = -INFINITY;
+  double Sl = 0.0;
+  uint64_t umax = 0;  // largest chunk maximum of the lane, unsigned order
+  for (int q = lane; q < C; q += kWave) {
+    u32x4 h = load_words(r, (uint32_t)q * rb);
+    u32x4 k0 = load_words(r, (uint32_t)q * rb + 16u);
+    if (!words_ready(h, p.epoch)) h = poll_words(r, (uint32_t)q * rb, p.epoch, p.err_flag);
+    if (!words_ready(k0, p.epoch)) k0 = poll_words(r, (uint32_t)q * rb + 16u, p.epoch, p.err_flag);
+    const float mq = __uint_as_float(h[0]);
+    const float Sq = __uint_as_float(h[2]);
+    if (Sq > 0.0f) {
+      if (mq > ml) {
+        Sl = Sl * (double)__builtin_amdgcn_exp2f((ml - mq) * kLog2e) + (double)Sq;
+        ml = mq;
+      } else {
+        Sl += (double)Sq * (double)__builtin_amdgcn_exp2f((mq - ml) * kLog2e);
+      }
+    }
+    umax = max(umax, words_ukey(k0));
   }
+  const float M = wave_allreduce(ml, MaxF());
+  const double S = wave_allreduce(
+      Sl > 0.0 ? Sl * (double)__builtin_amdgcn_exp2f((ml - M) * kLog2e) : 0.0, SumD());
+  const double logS = log_d(S);  // log Z = M + logS
+
+  // ---- lower bound of the row's K-th key ----
+  // With at least K lanes holding records, the K-th largest of the lanes'
+  // maxima is (K distinct keys reach it). Otherwise every key is read.
+  uint64_t t = 1;  // unsigned order; 0 is "no key"
+  if (min(C, kWave) >= K) t = wave_kth_largest<uint64_t>(umax, K);
+
+  // ---- records slot by slot, keys at or above t ----
+  if (lane < K) buf[lane] = INT64_MIN;
+  int nb = 0;
+  const int B = kCandCap - K;
+  auto flush = [&]() {
+    const int n = K + nb;
+    if (lane == 0) {
+      buf[n] = INT64_MIN;
+      buf[n + 1] = INT64_MIN;
+    }
+    wave_lds_order();
+    int64_t key[4];
+    int rank[4];
+    rank_list(buf, n, key, rank);
+    wave_lds_order();
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      if (rank[x] < K) buf[rank[x]] = key[x];
+    wave_lds_order();
+    nb = 0;
+    // keys below the current K-th can no longer enter
+    const int64_t kth = buf[K - 1];
+    t = max(t, (uint64_t)kth ^ kSignBit);
+  };
+  const int nq = (C - 1 - lane) / kWave + 1;  // records of this lane (lane < C)
+  const int nqmax = (C + kWave - 1) / kWave;
+  // active: records of this lane whose last key read reached t
+  uint64_t act = lane < C ? (nq >= 64 ? ~0ull : (1ull << nq) - 1ull) : 0ull;
+  for (int s = 0; s < K && __ballot(act != 0) != 0; ++s) {
+    const uint32_t soff = 16u * (uint32_t)(s + 1);
+    for (int q0 = 0; q0 < nqmax; q0 += 4) {
+      u32x4 w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t q = (uint32_t)(lane + (q0 + x) * kWave);
+        w[x] = ((act >> (q0 + x)) & 1) ? load_words(r, q * rb + soff) : u32x4{0u, 0u, 0u, 0u};
+      }
+      int64_t kk[4];
+      uint32_t fl = 0;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if ((act >> (q0 + x)) & 1) {
+          const uint32_t q = (uint32_t)(lane + (q0 + x) * kWave);
+          if (!words_ready(w[x], p.epoch)) w[x] = poll_words(r, q * rb + soff, p.epoch, p.err_flag);
+          const uint64_t u = words_ukey(w[x]);
+          if (u >= t) {
+            kk[x] = (int64_t)(u ^ kSignBit);
+            fl |= 1u << x;
+          } else {
+            act &= ~(1ull << (q0 + x));
+          }
+        } else {
+          kk[x] = INT64_MIN;
+        }
+      }
+      // append the flagged keys, ranking whenever the list is full
+      int total;
+      const int off = wave_prefix(__popc(fl), total);
+      for (int done = 0; done < total;) {
+        if (nb == B) flush();
+        const int room = B - nb;
+        int o = off;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          if ((fl >> x) & 1) {
+            const int g = o - done;
+            if (g >= 0 && g < room) buf[K + nb + g] = kk[x];
+            ++o;
+          }
+        }
+        const int took = min(room, total - done);
+        nb += took;
+        done += took;
+      }
+    }
+    if (s + 1 == K) act = 0;
+  }
+  flush();
+
+  if (lane < K) {
+    const int64_t key = buf[lane];
+    const float s = key32_value((int32_t)(key >> 32));
+    p.out_idx[row * K + lane] = key64_col(key);
+    p.out_vals[row * K + lane] = (float)(((double)s - (double)M) - logS);
+  }
+  wave_lds_order();
+  if (lane == 0) store_row_result(p.rowres, pos, __float_as_uint(M), 0u, p.epoch);
+}
+
+__device__ __forceinline__ int64_t load_uniform_i64(const int64_t *p) {
+  return *(const __attribute__((address_space(4))) int64_t *)p;
+}
+
+// ---------------------------------------------------------------------------
+// The kernel. Global wave gw belongs to group gw / C as member gw % C: the
+// group reduces kept positions group, group + n_groups, ..., the member
+// chunk `member` of each. The merger of the group's n-th kept row is member
+// n % C; it merges row n after reducing row n + 1. Every member waits for
+// the row result of row n - kLag before merging, which keeps the waves of
+// a SIMD in step.
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
+  __shared__ float4 stage[VEC ? kWaves * kChunkQuads : 1];
+  __shared__ __attribute__((aligned(16))) int64_t lists[kWaves * kCandKeys];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int gw = (int)blockIdx.x * kWaves + wave;
+  const int group = gw / p.C;
+  const int member = gw - group * p.C;
+  if (group >= p.n_groups) return;
+  const int64_t n_kept = load_uniform_i64(p.kept + p.rows);
+  const int64_t nrows = (n_kept - group + p.n_groups - 1) / p.n_groups;
+  if (nrows <= 0) return;
+  const int32_t chunk = member;
+  auto pos_of = [&](int64_t n) -> int64_t { return group + n * p.n_groups; };
+  auto row_at = [&](int64_t n) -> int64_t {
+    return load_uniform_i64(p.kept + pos_of(n < nrows ? n : nrows - 1));
+  };
+  float4 *const buf = stage + (VEC ? wave * kChunkQuads : 0);
+  int64_t *const list = lists + wave * kCandKeys;
+  // as in the row-statistics kernel, the copy past the last row still
+  // issues (through a zero-size descriptor) so that every path issues the
+  // same operations
+  auto copy_chunk = [&](int64_t n, int64_t row) {
+    if (n < nrows)
+      chunk_copy_async(buf, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
+    else
+      chunk_copy_async(buf, p.logits, 0, 0);
+  };
+
+  int64_t row = row_at(0), next_row = row_at(1), prev_row = row;
+  int mturn = 0;  // (n - 1) % C
+  if constexpr (VEC) copy_chunk(0, row);
+  for (int64_t n = 0; n < nrows; ++n) {
+    const int64_t after_row = row_at(n + 2);
+    u32x4 rr = load_row_result(p.rowres, pos_of(n >= kLag ? n - kLag : 0));
+    compiler_fence();
+    float4 cur[kQ];
+    if constexpr (VEC) {
+      // after this row's copy came, in the previous row, its record stores,
+      // the merger's work and this row's row-result load
+      wait_vm<1>();
+      lds_read_chunk(cur, buf);
+      compiler_fence();
+      copy_chunk(n + 1, next_row);
+      compiler_fence();
+    } else {
+      chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
+    }
+    ChunkTop t;
+    reduce_chunk_topk<VEC>(p, row, chunk, cur, list, t);
+    // consume rr before the record stores, so that its wait does not wait
+    // for the copy above
+    __asm__ volatile("" ::"v"(rr));
+    compiler_fence();
+    publish_record(p, pos_of(n), chunk, t);
+    compiler_fence();
+    if (n >= kLag) rr = wait_row_result(p.rowres, pos_of(n - kLag), rr, p.epoch, p.err_flag);
+    if (n >= 1 && mturn == member) merge_row_topk(p, pos_of(n - 1), prev_row, list);
+    if (n >= 1 && ++mturn == p.C) mturn = 0;
+    prev_row = row;
+    row = next_row;
+    next_row = after_row;
+  }
+  if (mturn == member) merge_row_topk(p, pos_of(nrows - 1), prev_row, list);
+}
+
+// ---------------------------------------------------------------------------
+// Kept-row list: kept[0 .. n) = the rows of kept slots in order, kept[rows]
+// = n. One workgroup; thread t handles a contiguous range of rows.
+// ---------------------------------------------------------------------------
+constexpr int kListThreads = 1024;
+
+__global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *keep, int64_t rows,
+                                                               int64_t canvas_len, int64_t *kept) {
+  __shared__ int64_t wave_tot[kListThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int64_t per = (rows + kListThreads - 1) / kListThreads;
+  const int64_t r0 = min(rows, (int64_t)tid * per), r1 = min(rows, r0 + per);
+  int64_t cnt = 0;
+  for (int64_t r = r0; r < r1;) {
+    const int64_t slot = r / canvas_len;
+    const int64_t end = min(r1, (slot + 1) * canvas_len);
+    if (keep[slot]) cnt += end - r;
+    r = end;
+  }
+  // exclusive prefix over the workgroup
+  int64_t incl = cnt;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int64_t o = __shfl_up(incl, (unsigned)d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int64_t off = incl - cnt;
+  for (int w = 0; w < wave; ++w) off += wave_tot[w];
+  for (int64_t r = r0; r < r1;) {
+    const int64_t slot = r / canvas_len;
+    const int64_t end = min(r1, (slot + 1) * canvas_len);
+    if (keep[slot])
+      for (; r < end; ++r) kept[off++] = r;
+    r = end;
+  }
+  if (tid == kListThreads - 1) kept[rows] = off;
 }
 
 }  // namespace
 
 static const void *topk_kernel_ptr(bool vec) {
-  return vec ? reinterpret_cast<const void *>(&topk_kernel<kTopKQPT, true>)
-             : reinterpret_cast<const void *>(&topk_kernel<kTopKQPT, false>);
+  return vec ? reinterpret_cast<const void *>(&topk_kernel<true>)
+             : reinterpret_cast<const void *>(&topk_kernel<false>);
 }
 
 hipError_t topk_resident_blocks(bool vec, int *blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, topk_kernel_ptr(vec), kT, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, topk_kernel_ptr(vec), kThreads,
+                                                      0);
 }
 
 hipError_t topk_launch(const TopKParams &p, int grid, hipStream_t stream) {
+  kept_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(p.keep, p.rows, p.canvas_len,
+                                                                 p.kept);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   TopKParams arg = p;
   void *args[] = {&arg};
-  return hipLaunchKernel(topk_kernel_ptr(p.vec_ok != 0), dim3(grid), dim3(kT), args, 0, stream);
+  return hipLaunchCooperativeKernel(topk_kernel_ptr(p.vec_ok != 0), dim3(grid), dim3(kThreads), args,
+                                    0, stream);
 }
 
 }  // namespace rowstats

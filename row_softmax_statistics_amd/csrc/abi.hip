@@ -266,12 +266,15 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   const size_t record_bytes = (size_t)rows * p.C * topk_record_bytes(K);
   const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
   const size_t kept_bytes = ((size_t)rows + 1) * sizeof(int64_t);
-  if ((rc = ensure_row_scratch(*d, record_bytes + rowres_bytes + kept_bytes, s))) return rc;
+  const size_t temp_bytes = ((size_t)rows * sizeof(float) + 15) & ~(size_t)15;
+  if ((rc = ensure_row_scratch(*d, record_bytes + rowres_bytes + kept_bytes + temp_bytes, s)))
+    return rc;
   if ((rc = next_epoch(*d, s, &p.epoch))) return rc;
   char *base = reinterpret_cast<char *>(d->row_scratch);
   p.records = reinterpret_cast<uint64_t *>(base);
   p.rowres = reinterpret_cast<uint64_t *>(base + record_bytes);
-  p.kept = reinterpret_cast<int64_t *>(base + record_bytes + rowres_bytes);
+  p.kept_temp = reinterpret_cast<float *>(base + record_bytes + rowres_bytes);
+  p.kept = reinterpret_cast<int64_t *>(base + record_bytes + rowres_bytes + temp_bytes);
   p.err_flag = d->err_flag;
   hipError_t e = topk_launch(p, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "top-K kernel launch");

@@ -23,7 +23,22 @@ constexpr int kLag = 3;
 
 typedef __attribute__((address_space(3))) void *LdsPtr;
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+// Lane within the wave, from mbcnt (bits of an all-ones mask below the
+// lane): it needs no input register, so the compiler can recompute it
+// instead of keeping threadIdx.x alive through the kernel.
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// The same, computed where it is written: the compiler cannot move volatile
+// inline assembly out of a loop, so values derived from it inside a row loop
+// are recomputed there instead of being kept (and spilled to scratch
+// memory, whose reloads wait for the chunk copy in flight) across the loop.
+__device__ __forceinline__ int lane_here() {
+  uint32_t l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return (int)l;
+}
 
 // Keeps the compiler from moving memory operations across this point, so
 // the counts above hold for the issue order written here.
@@ -50,11 +65,16 @@ __device__ __forceinline__ Rsrc chunk_rsrc(const float *xrow, int32_t c0, int32_
   return make_rsrc(xrow + c0, 4u * (uint32_t)cols);
 }
 
-// Vector path: asynchronous copy of the chunk into the wave's LDS buffer
-// (quad j * 64 + l at buf[j * 64 + l]).
-__device__ __forceinline__ void chunk_copy_async(float4 *buf, const float *xrow, int32_t c0,
-                                                 int32_t V) {
-  const Rsrc r = chunk_rsrc(xrow, c0, V);
+// Bytes of the chunk at column c0 of a row of V columns (wave-uniform).
+__device__ __forceinline__ uint32_t chunk_bytes(int32_t c0, int32_t V) {
+  return 4u * (uint32_t)__builtin_amdgcn_readfirstlane(max(min(V - c0, kChunkCols), 0));
+}
+
+// Vector path: asynchronous copy of `bytes` bytes at src (a chunk) into the
+// wave's LDS buffer (quad j * 64 + l at buf[j * 64 + l]); the rest of the
+// buffer gets zeros.
+__device__ __forceinline__ void chunk_copy_bytes(float4 *buf, const float *src, uint32_t bytes) {
+  const Rsrc r = make_rsrc(src, bytes);
   const uint32_t voff = 16u * lane_id();
   // The instruction offset moves both the HBM address and the LDS
   // destination, so M0 (the LDS base) changes only once per chunk.
@@ -70,6 +90,11 @@ __device__ __forceinline__ void chunk_copy_async(float4 *buf, const float *xrow,
   ROWSTATS_DMA(6);
   ROWSTATS_DMA(7);
 #undef ROWSTATS_DMA
+}
+
+__device__ __forceinline__ void chunk_copy_async(float4 *buf, const float *xrow, int32_t c0,
+                                                 int32_t V) {
+  chunk_copy_bytes(buf, xrow + c0, chunk_bytes(c0, V));
 }
 
 // Scalar path (unaligned rows or vocab % 4 != 0): four 4-byte loads a quad.
@@ -124,6 +149,27 @@ __device__ __forceinline__ uint32_t push_bit_ge(uint32_t cm, float a, float b) {
           : "v"(a), "v"(b)
           : "vcc");
   return cm;
+}
+
+// Element k (0..31) of the lane's chunk registers. A per-lane index into
+// registers would go through scratch memory, so this is a tree of selects
+// on the bits of k. The empty statements hand the selects register values:
+// selects between two array elements would otherwise be turned back into
+// one indexed load.
+__device__ __forceinline__ float element_at(const float4 (&v)[kQ], uint32_t k) {
+  const bool b0 = (k & 1u) != 0, b1 = (k & 2u) != 0, b2 = (k & 4u) != 0, b3 = (k & 8u) != 0,
+             b4 = (k & 16u) != 0;
+  float q[kQ];
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) {
+    float x = v[j].x, y = v[j].y, z = v[j].z, w = v[j].w;
+    __asm__("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
+    q[j] = b1 ? (b0 ? w : z) : (b0 ? y : x);
+  }
+  const float a0 = b2 ? q[1] : q[0], a1 = b2 ? q[3] : q[2], a2 = b2 ? q[5] : q[4],
+              a3 = b2 ? q[7] : q[6];
+  const float c0 = b3 ? a1 : a0, c1 = b3 ? a3 : a2;
+  return b4 ? c1 : c0;
 }
 
 // ---------------------------------------------------------------------------

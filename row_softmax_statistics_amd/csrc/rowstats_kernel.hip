@@ -275,7 +275,6 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   const float T = load_uniform(p.temps + row / p.canvas_len);
   const bool greedy = !(T > 0.0f);
   const double rtc = 1.0 / (double)clamp_temp(T);
-  const float *xrow = p.logits + row * p.ld;
   const int32_t c0 = chunk * kChunkCols;
   // column of element k = 4 j + i of this lane
   auto col_of = [&](int k) -> int32_t { return c0 + 4 * ((k >> 2) * kWave + lane) + (k & 3); };
@@ -343,11 +342,12 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   if (!greedy && mw != -INFINITY) {
     const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
     const uint32_t r0 = (uint32_t)(uint64_t)row, r1 = (uint32_t)((uint64_t)row >> 32);
-    uint32_t qb = (uint32_t)chunk * kChunkQuads + (uint32_t)lane;  // quad of j = 0
-    // The counters are the same for every row of this wave: without this the
-    // compiler hoists the first Philox round out of the row loop and, short
-    // of registers, reloads its products from scratch memory every row.
-    __asm__ volatile("" : "+v"(qb));
+    // quad of j = 0. The counters are the same for every row of this wave:
+    // with lane_id() the compiler keeps them (or the first Philox round's
+    // products) across the row loop and, short of registers, reloads them
+    // from scratch memory, and each such reload waits for the chunk copy in
+    // flight.
+    const uint32_t qb = (uint32_t)chunk * kChunkQuads + (uint32_t)lane_here();
     constexpr float kLn2 = 0.693147180559945309f;
     // fp32 Gumbel value -log(-log u) of a word, error below 2^-12
     auto g32 = [&](uint32_t w) { return -__builtin_amdgcn_logf(neg_log_u_f32(w)) * kLn2; };
@@ -389,7 +389,10 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     }
     // Every candidate gets an fp32 score relative to m: s - m from its raw
     // logit (re-read; it was just streamed, so the read normally hits the
-    // cache) plus its fp32 Gumbel value. Each lane keeps its best two.
+    // cache) plus its fp32 Gumbel value. Each lane keeps its best two. (The
+    // wait for the re-read also waits for the chunk copy in flight; scoring
+    // from the exp values in registers avoids that but costs more vector
+    // instructions, and measures slower.)
     float za1 = -INFINITY, za2 = -INFINITY;
     int32_t kbest = 0;
     for (uint32_t c2 = cm; c2 != 0;) {
@@ -397,7 +400,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
       c2 &= ~(0x80000000u >> k);
       const int32_t c = col_of(k);
       if (c < V) {
-        const float x = xrow[c];
+        const float x = p.logits[row * p.ld + c];
         const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, r0, r1, k0, k1);
         const float z = (scale(x, rtc) - mw) + g32(pick(w, c & 3));
         if (z > za1) {

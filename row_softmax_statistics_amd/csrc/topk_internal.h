@@ -32,6 +32,7 @@ struct TopKParams {
   float *out_vals;
   int64_t *out_idx;
   int64_t *kept;      // [rows + 1]: kept rows in order, then their count (written by the pre-pass)
+  float *kept_temp;   // [rows]: temperature of kept row i (written by the pre-pass)
   uint64_t *records;  // [rows, C] records of topk_record_bytes(K), indexed by kept position
   uint64_t *rowres;   // [rows] row results of kRowResultBytes, indexed by kept position
   uint32_t *err_flag;

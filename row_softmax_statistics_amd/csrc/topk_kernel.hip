@@ -126,27 +126,6 @@ __device__ __forceinline__ U wave_kth_largest(U u, int k) {
   return res;
 }
 
-// Element k (0..31) of the lane's chunk registers. A per-lane index into
-// registers would go through scratch memory, so this is a tree of selects
-// on the bits of k. The empty statements hand the selects register values:
-// selects between two array elements would otherwise be turned back into
-// one indexed load.
-__device__ __forceinline__ float element_at(const float4 (&v)[kQ], uint32_t k) {
-  const bool b0 = (k & 1u) != 0, b1 = (k & 2u) != 0, b2 = (k & 4u) != 0, b3 = (k & 8u) != 0,
-             b4 = (k & 16u) != 0;
-  float q[kQ];
-#pragma unroll
-  for (int j = 0; j < kQ; ++j) {
-    float x = v[j].x, y = v[j].y, z = v[j].z, w = v[j].w;
-    __asm__("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
-    q[j] = b1 ? (b0 ? w : z) : (b0 ? y : x);
-  }
-  const float a0 = b2 ? q[1] : q[0], a1 = b2 ? q[3] : q[2], a2 = b2 ? q[5] : q[4],
-              a3 = b2 ? q[7] : q[6];
-  const float c0 = b3 ? a1 : a0, c1 = b3 ? a3 : a2;
-  return b4 ? c1 : c0;
-}
-
 // Keeps the compiler's LDS accesses in program order between lanes of a
 // wave (the hardware executes a wave's LDS operations in order).
 __device__ __forceinline__ void wave_lds_order() {
@@ -160,7 +139,7 @@ __device__ __forceinline__ void wave_lds_order() {
 template <int NX>
 __device__ __forceinline__ void rank_keys(const int64_t *list, int n, int64_t (&key)[4],
                                           int (&rank)[4]) {
-  const int lane = lane_id();
+  const int lane = lane_here();
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
     const int idx = lane + x * kWave;
@@ -203,12 +182,11 @@ struct ChunkTop {
 };
 
 template <bool VEC>
-__device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, int64_t row, int32_t chunk,
+__device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, int32_t chunk,
                                                   float4 (&v)[kQ], int64_t *cand, ChunkTop &out) {
   const int lane = lane_id();
   const int32_t V = p.vocab;
   const int K = p.K;
-  const float T = load_uniform(p.temps + row / p.canvas_len);
   const double rtc = 1.0 / (double)clamp_temp(T);
   const int32_t c0 = chunk * kChunkCols;
   // column of element 0 of this lane. The columns are the same for every
@@ -330,7 +308,7 @@ __device__ __forceinline__ void publish_record(const TopKParams &p, int64_t pos,
 // waiting to be ranked in [K, K + nb).
 // ---------------------------------------------------------------------------
 __device__ void merge_row_topk(const TopKParams &p, int64_t pos, int64_t row, int64_t *buf) {
-  const int lane = lane_id();
+  const int lane = lane_here();
   const int K = p.K, C = p.C;
   const uint32_t rb = record_bytes(K);
   const Rsrc r = records_rsrc(p, pos);
@@ -463,7 +441,7 @@ __device__ __forceinline__ int64_t load_uniform_i64(const int64_t *p) {
 // ---------------------------------------------------------------------------
 // The kernel. Global wave gw belongs to group gw / C as member gw % C: the
 // group reduces kept positions group, group + n_groups, ..., the member
-// chunk `member` of each. The merger of the group's n-th kept row is member
+// chunk `member` of each. The merger of the group's n-th row is member
 // n % C; it merges row n after reducing row n + 1. Every member waits for
 // the row result of row n - kLag before merging, which keeps the waves of
 // a SIMD in step.
@@ -478,31 +456,33 @@ __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
   const int member = gw - group * p.C;
   if (group >= p.n_groups) return;
   const int64_t n_kept = load_uniform_i64(p.kept + p.rows);
-  const int64_t nrows = (n_kept - group + p.n_groups - 1) / p.n_groups;
-  if (nrows <= 0) return;
+  if (group >= n_kept) return;
   const int32_t chunk = member;
-  auto pos_of = [&](int64_t n) -> int64_t { return group + n * p.n_groups; };
-  auto row_at = [&](int64_t n) -> int64_t {
-    return load_uniform_i64(p.kept + pos_of(n < nrows ? n : nrows - 1));
+  const int64_t G = p.n_groups;
+  // The group's rows are at kept positions group, group + G, ... below
+  // n_kept (all bounds are kept in positions: a row count would come from a
+  // 64-bit division, which leaves its result in vector registers).
+  auto row_at = [&](int64_t pos) -> int64_t {
+    return load_uniform_i64(p.kept + (pos < n_kept ? pos : (int64_t)group));
   };
   float4 *const buf = stage + (VEC ? wave * kChunkQuads : 0);
   int64_t *const list = lists + wave * kCandKeys;
   // as in the row-statistics kernel, the copy past the last row still
   // issues (through a zero-size descriptor) so that every path issues the
   // same operations
-  auto copy_chunk = [&](int64_t n, int64_t row) {
-    if (n < nrows)
-      chunk_copy_async(buf, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
-    else
-      chunk_copy_async(buf, p.logits, 0, 0);
+  const uint32_t bytes = chunk_bytes(chunk * kChunkCols, p.vocab);
+  auto copy_chunk = [&](int64_t pos, int64_t row) {
+    chunk_copy_bytes(buf, pos < n_kept ? p.logits + row * p.ld + chunk * kChunkCols : p.logits,
+                     pos < n_kept ? bytes : 0u);
   };
 
-  int64_t row = row_at(0), next_row = row_at(1), prev_row = row;
+  int64_t pos = group;
+  int64_t row = row_at(pos), next_row = row_at(pos + G), prev_row = row;
   int mturn = 0;  // (n - 1) % C
-  if constexpr (VEC) copy_chunk(0, row);
-  for (int64_t n = 0; n < nrows; ++n) {
-    const int64_t after_row = row_at(n + 2);
-    u32x4 rr = load_row_result(p.rowres, pos_of(n >= kLag ? n - kLag : 0));
+  if constexpr (VEC) copy_chunk(pos, row);
+  for (int n = 0; pos < n_kept; ++n, pos += G) {
+    const int64_t after_row = row_at(pos + 2 * G);
+    u32x4 rr = load_row_result(p.rowres, n >= kLag ? pos - kLag * G : pos);
     compiler_fence();
     float4 cur[kQ];
     if constexpr (VEC) {
@@ -511,37 +491,40 @@ __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
       wait_vm<1>();
       lds_read_chunk(cur, buf);
       compiler_fence();
-      copy_chunk(n + 1, next_row);
+      copy_chunk(pos + G, next_row);
       compiler_fence();
     } else {
       chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
     }
     ChunkTop t;
-    reduce_chunk_topk<VEC>(p, row, chunk, cur, list, t);
+    reduce_chunk_topk<VEC>(p, load_uniform(p.kept_temp + pos), chunk, cur, list, t);
     // consume rr before the record stores, so that its wait does not wait
     // for the copy above
     __asm__ volatile("" ::"v"(rr));
     compiler_fence();
-    publish_record(p, pos_of(n), chunk, t);
+    publish_record(p, pos, chunk, t);
     compiler_fence();
-    if (n >= kLag) rr = wait_row_result(p.rowres, pos_of(n - kLag), rr, p.epoch, p.err_flag);
-    if (n >= 1 && mturn == member) merge_row_topk(p, pos_of(n - 1), prev_row, list);
+    if (n >= kLag) rr = wait_row_result(p.rowres, pos - kLag * G, rr, p.epoch, p.err_flag);
+    if (n >= 1 && mturn == member) merge_row_topk(p, pos - G, prev_row, list);
     if (n >= 1 && ++mturn == p.C) mturn = 0;
     prev_row = row;
     row = next_row;
     next_row = after_row;
   }
-  if (mturn == member) merge_row_topk(p, pos_of(nrows - 1), prev_row, list);
+  if (mturn == member) merge_row_topk(p, pos - G, prev_row, list);
 }
 
 // ---------------------------------------------------------------------------
 // Kept-row list: kept[0 .. n) = the rows of kept slots in order, kept[rows]
-// = n. One workgroup; thread t handles a contiguous range of rows.
+// = n, and kept_temp[i] = the temperature of row kept[i]. One workgroup;
+// thread t handles a contiguous range of rows.
 // ---------------------------------------------------------------------------
 constexpr int kListThreads = 1024;
 
-__global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *keep, int64_t rows,
-                                                               int64_t canvas_len, int64_t *kept) {
+__global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *keep,
+                                                               const float *temps, int64_t rows,
+                                                               int64_t canvas_len, int64_t *kept,
+                                                               float *kept_temp) {
   __shared__ int64_t wave_tot[kListThreads / kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -568,8 +551,13 @@ __global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *
   for (int64_t r = r0; r < r1;) {
     const int64_t slot = r / canvas_len;
     const int64_t end = min(r1, (slot + 1) * canvas_len);
-    if (keep[slot])
-      for (; r < end; ++r) kept[off++] = r;
+    if (keep[slot]) {
+      const float T = temps[slot];
+      for (; r < end; ++r) {
+        kept_temp[off] = T;
+        kept[off++] = r;
+      }
+    }
     r = end;
   }
   if (tid == kListThreads - 1) kept[rows] = off;
@@ -588,8 +576,8 @@ hipError_t topk_resident_blocks(bool vec, int *blocks_per_cu) {
 }
 
 hipError_t topk_launch(const TopKParams &p, int grid, hipStream_t stream) {
-  kept_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(p.keep, p.rows, p.canvas_len,
-                                                                 p.kept);
+  kept_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(p.keep, p.temps, p.rows,
+                                                                 p.canvas_len, p.kept, p.kept_temp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   TopKParams arg = p;

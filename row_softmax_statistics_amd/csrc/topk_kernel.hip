@@ -44,10 +44,12 @@ namespace {
 constexpr int kThreads = kRowThreads;
 constexpr int kWaves = kThreads / kWave;
 constexpr float kLog2e = 1.44269504088896340736f;
-// LDS keys per wave for candidate lists; the last two places of a list are
-// end markers, so a list holds at most kCandCap keys.
+// LDS keys per wave for candidate lists. Ranking reads a list 8 keys at a
+// time, so the 8 places after a list hold end markers (INT64_MIN), and a
+// list holds at most kCandCap keys.
 constexpr int kCandKeys = 256;
-constexpr int kCandCap = kCandKeys - 2;
+constexpr int kListPad = 8;
+constexpr int kCandCap = kCandKeys - kListPad;
 constexpr uint64_t kSignBit = 0x8000000000000000ull;
 
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
@@ -134,8 +136,8 @@ __device__ __forceinline__ void wave_lds_order() {
 
 // Ranks of the keys of an LDS list of n <= 64 NX keys (distinct, except for
 // INT64_MIN): key[x] = list[lane + 64 x], rank[x] = the number of list keys
-// above it (INT_MAX past the list end). list[n] and list[n + 1] must hold
-// INT64_MIN.
+// above it (INT_MAX past the list end). list[n .. n + 8) must hold INT64_MIN
+// (the list is read 8 keys per wait).
 template <int NX>
 __device__ __forceinline__ void rank_keys(const int64_t *list, int n, int64_t (&key)[4],
                                           int (&rank)[4]) {
@@ -146,10 +148,14 @@ __device__ __forceinline__ void rank_keys(const int64_t *list, int n, int64_t (&
     key[x] = idx < n ? list[idx] : INT64_MIN;
     rank[x] = 0;
   }
-  for (int j = 0; j < n; j += 2) {
-    const i64x2 pr = *reinterpret_cast<const i64x2 *>(list + j);
+  for (int j = 0; j < n; j += kListPad) {
+    const i64x2 *l2 = reinterpret_cast<const i64x2 *>(list + j);
+    const i64x2 a = l2[0], b = l2[1], c = l2[2], d = l2[3];
 #pragma unroll
-    for (int x = 0; x < NX; ++x) rank[x] += (int)(pr[0] > key[x]) + (int)(pr[1] > key[x]);
+    for (int x = 0; x < NX; ++x)
+      rank[x] += (int)(a[0] > key[x]) + (int)(a[1] > key[x]) + (int)(b[0] > key[x]) +
+                 (int)(b[1] > key[x]) + (int)(c[0] > key[x]) + (int)(c[1] > key[x]) +
+                 (int)(d[0] > key[x]) + (int)(d[1] > key[x]);
   }
 #pragma unroll
   for (int x = 0; x < NX; ++x)
@@ -254,10 +260,7 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, 
       c2 &= ~(0x80000000u >> k);
       cand[o++] = key64(element_at(v, k), col_of(k));
     }
-    if (lane == 0) {
-      cand[total] = INT64_MIN;
-      cand[total + 1] = INT64_MIN;
-    }
+    if (lane < kListPad) cand[total + lane] = INT64_MIN;
     wave_lds_order();
     rank_list(cand, total, out.key, out.rank);
     wave_lds_order();
@@ -313,15 +316,14 @@ __device__ void merge_row_topk(const TopKParams &p, int64_t pos, int64_t row, in
   const uint32_t rb = record_bytes(K);
   const Rsrc r = records_rsrc(p, pos);
 
-  // ---- headers and chunk maxima of records q = lane + 64 i ----
+  // ---- headers, chunk maxima and second keys ----
+  // Records q = lane + 64 i. Their header and first two keys are read at
+  // once; the keys of records 0 and 1 of the lane stay in registers, since
+  // on typical rows few keys past the second of a record reach the bound.
   float ml = -INFINITY;
   double Sl = 0.0;
   uint64_t umax = 0;  // largest chunk maximum of the lane, unsigned order
-  for (int q = lane; q < C; q += kWave) {
-    u32x4 h = load_words(r, (uint32_t)q * rb);
-    u32x4 k0 = load_words(r, (uint32_t)q * rb + 16u);
-    if (!words_ready(h, p.epoch)) h = poll_words(r, (uint32_t)q * rb, p.epoch, p.err_flag);
-    if (!words_ready(k0, p.epoch)) k0 = poll_words(r, (uint32_t)q * rb + 16u, p.epoch, p.err_flag);
+  auto add_header = [&](const u32x4 &h) {
     const float mq = __uint_as_float(h[0]);
     const float Sq = __uint_as_float(h[2]);
     if (Sq > 0.0f) {
@@ -332,7 +334,43 @@ __device__ void merge_row_topk(const TopKParams &p, int64_t pos, int64_t row, in
         Sl += (double)Sq * (double)__builtin_amdgcn_exp2f((mq - ml) * kLog2e);
       }
     }
-    umax = max(umax, words_ukey(k0));
+  };
+  auto ready = [&](u32x4 w, uint32_t off) {
+    return words_ready(w, p.epoch) ? w : poll_words(r, off, p.epoch, p.err_flag);
+  };
+  const u32x4 none = {0u, 0u, 0u, 0u};
+  const bool has0 = lane < C, has1 = lane + kWave < C, two = K > 1;
+  const uint32_t o0 = (uint32_t)lane * rb, o1 = (uint32_t)(lane + kWave) * rb;
+  u32x4 h0 = none, w00 = none, w01 = none, h1 = none, w10 = none, w11 = none;
+  if (has0) {
+    h0 = load_words(r, o0);
+    w00 = load_words(r, o0 + 16u);
+    if (two) w01 = load_words(r, o0 + 32u);
+  }
+  if (has1) {
+    h1 = load_words(r, o1);
+    w10 = load_words(r, o1 + 16u);
+    if (two) w11 = load_words(r, o1 + 32u);
+  }
+  if (has0) {
+    h0 = ready(h0, o0);
+    w00 = ready(w00, o0 + 16u);
+    if (two) w01 = ready(w01, o0 + 32u);
+    add_header(h0);
+    umax = words_ukey(w00);
+  }
+  if (has1) {
+    h1 = ready(h1, o1);
+    w10 = ready(w10, o1 + 16u);
+    if (two) w11 = ready(w11, o1 + 32u);
+    add_header(h1);
+    umax = max(umax, words_ukey(w10));
+  }
+  for (int q = lane + 2 * kWave; q < C; q += kWave) {
+    const uint32_t o = (uint32_t)q * rb;
+    u32x4 h = load_words(r, o), w0 = load_words(r, o + 16u);
+    add_header(ready(h, o));
+    umax = max(umax, words_ukey(ready(w0, o + 16u)));
   }
   const float M = wave_allreduce(ml, MaxF());
   const double S = wave_allreduce(
@@ -341,20 +379,20 @@ __device__ void merge_row_topk(const TopKParams &p, int64_t pos, int64_t row, in
 
   // ---- lower bound of the row's K-th key ----
   // With at least K lanes holding records, the K-th largest of the lanes'
-  // maxima is (K distinct keys reach it). Otherwise every key is read.
+  // maxima is one (K distinct keys reach it), and so is that key with its
+  // low word cleared, whose high word is the K-th largest high word.
+  // Otherwise every key is read.
   uint64_t t = 1;  // unsigned order; 0 is "no key"
-  if (min(C, kWave) >= K) t = wave_kth_largest<uint64_t>(umax, K);
+  if (min(C, kWave) >= K)
+    t = max((uint64_t)wave_kth_largest<uint32_t>((uint32_t)(umax >> 32), K) << 32, (uint64_t)1);
 
-  // ---- records slot by slot, keys at or above t ----
+  // ---- keys at or above t, ranked with the running top-K ----
   if (lane < K) buf[lane] = INT64_MIN;
   int nb = 0;
   const int B = kCandCap - K;
   auto flush = [&]() {
     const int n = K + nb;
-    if (lane == 0) {
-      buf[n] = INT64_MIN;
-      buf[n + 1] = INT64_MIN;
-    }
+    if (lane < kListPad) buf[n + lane] = INT64_MIN;
     wave_lds_order();
     int64_t key[4];
     int rank[4];
@@ -369,56 +407,80 @@ __device__ void merge_row_topk(const TopKParams &p, int64_t pos, int64_t row, in
     const int64_t kth = buf[K - 1];
     t = max(t, (uint64_t)kth ^ kSignBit);
   };
-  const int nq = (C - 1 - lane) / kWave + 1;  // records of this lane (lane < C)
+  // Appends the keys kk[x] with bit x of fl set, ranking whenever the list
+  // is full.
+  auto append = [&](const int64_t (&kk)[4], uint32_t fl) {
+    int total;
+    const int off = wave_prefix(__popc(fl), total);
+    for (int done = 0; done < total;) {
+      if (nb == B) flush();
+      const int room = B - nb;
+      int o = off;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if ((fl >> x) & 1) {
+          const int g = o - done;
+          if (g >= 0 && g < room) buf[K + nb + g] = kk[x];
+          ++o;
+        }
+      }
+      const int took = min(room, total - done);
+      nb += took;
+      done += took;
+    }
+  };
+  // the first two keys of records 0 and 1 of the lane
+  uint64_t later = 0;  // records 0 and 1 still to be read from slot 2 on
+  {
+    const uint64_t u[4] = {words_ukey(w00), words_ukey(w01), words_ukey(w10), words_ukey(w11)};
+    const bool in[4] = {has0, has0 && two, has1, has1 && two};
+    int64_t kk[4];
+    uint32_t fl = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      kk[x] = (int64_t)(u[x] ^ kSignBit);
+      if (in[x] && u[x] >= t) fl |= 1u << x;
+    }
+    if (K > 2) later = (uint64_t)((fl >> 1) & 1) | ((uint64_t)((fl >> 3) & 1) << 1);
+    append(kk, fl);
+  }
+  // the other records from slot 0, records 0 and 1 from slot 2, each while
+  // its keys reach t (a record is sorted)
+  const int nq = lane < C ? (C - 1 - lane) / kWave + 1 : 0;  // records of this lane
   const int nqmax = (C + kWave - 1) / kWave;
-  // active: records of this lane whose last key read reached t
-  uint64_t act = lane < C ? (nq >= 64 ? ~0ull : (1ull << nq) - 1ull) : 0ull;
-  for (int s = 0; s < K && __ballot(act != 0) != 0; ++s) {
+  uint64_t act = nq > 2 ? (nq >= 64 ? ~0ull : (1ull << nq) - 1ull) & ~3ull : 0ull;
+  for (int s = 0; s < K; ++s) {
+    if (s == 2) {
+      act |= later;
+      later = 0;
+    }
+    if (__ballot((act | later) != 0) == 0) break;
+    if (__ballot(act != 0) == 0) continue;
     const uint32_t soff = 16u * (uint32_t)(s + 1);
     for (int q0 = 0; q0 < nqmax; q0 += 4) {
       u32x4 w[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const uint32_t q = (uint32_t)(lane + (q0 + x) * kWave);
-        w[x] = ((act >> (q0 + x)) & 1) ? load_words(r, q * rb + soff) : u32x4{0u, 0u, 0u, 0u};
+        w[x] = ((act >> (q0 + x)) & 1) ? load_words(r, q * rb + soff) : none;
       }
       int64_t kk[4];
       uint32_t fl = 0;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
+        kk[x] = INT64_MIN;
         if ((act >> (q0 + x)) & 1) {
           const uint32_t q = (uint32_t)(lane + (q0 + x) * kWave);
-          if (!words_ready(w[x], p.epoch)) w[x] = poll_words(r, q * rb + soff, p.epoch, p.err_flag);
-          const uint64_t u = words_ukey(w[x]);
+          const uint64_t u = words_ukey(ready(w[x], q * rb + soff));
           if (u >= t) {
             kk[x] = (int64_t)(u ^ kSignBit);
             fl |= 1u << x;
           } else {
             act &= ~(1ull << (q0 + x));
           }
-        } else {
-          kk[x] = INT64_MIN;
         }
       }
-      // append the flagged keys, ranking whenever the list is full
-      int total;
-      const int off = wave_prefix(__popc(fl), total);
-      for (int done = 0; done < total;) {
-        if (nb == B) flush();
-        const int room = B - nb;
-        int o = off;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          if ((fl >> x) & 1) {
-            const int g = o - done;
-            if (g >= 0 && g < room) buf[K + nb + g] = kk[x];
-            ++o;
-          }
-        }
-        const int took = min(room, total - done);
-        nb += took;
-        done += took;
-      }
+      append(kk, fl);
     }
     if (s + 1 == K) act = 0;
   }

@@ -18,8 +18,6 @@ constexpr int kDevScope = 16;
 // Polls of one wait before it gives up and flags the call (about a second);
 // once any wait has given up, every later wait of the call gives up at once.
 constexpr uint32_t kSpinLimit = 1u << 20;
-// Rows between publishing a row's summaries and reading the row's result.
-constexpr int kLag = 3;
 
 typedef __attribute__((address_space(3))) void *LdsPtr;
 

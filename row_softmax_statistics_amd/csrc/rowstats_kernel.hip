@@ -494,16 +494,20 @@ __device__ __forceinline__ void write_probs(const RowStatsParams &p, int64_t row
 // The kernel. Global wave gw belongs to group gw / C as member gw % C: the
 // group reduces rows group, group + n_groups, ..., the member chunk `member`
 // of each. The merger of the group's n-th row is member n % C; it merges
-// row n after reducing row n + 1. Before publishing row n, every member
-// waits for the result of row n - kLag (normally there for a whole chunk):
-// with probs it needs it to write that row's probabilities, and without
-// probs the wait keeps the waves of a SIMD in step (otherwise the older
-// wave, favoured by the issue arbiter, would finish early and leave the
-// SIMD half idle). With kLag = 2 the merger's result would arrive just as
-// the members look for it.
+// row n after reducing row n + kMergeLag. Before publishing row n, every
+// member waits for the result of row n - kLag (normally there for a whole
+// chunk): with probs it needs it to write that row's probabilities, and
+// without probs the wait keeps the waves of a SIMD in step (otherwise the
+// older wave, favoured by the issue arbiter, would finish early and leave
+// the SIMD half idle). A merge delays its merger's next chunks; the merger
+// of a later row waits for such a late chunk only when the delay exceeds
+// kMergeLag chunk periods. With probs, each row of lag keeps the row's exp
+// values in registers, so the lags stay short there.
 // ---------------------------------------------------------------------------
 template <int PROBS, bool VEC>
 __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowStatsParams p) {
+  constexpr int kMergeLag = PROBS ? 1 : 2;
+  constexpr int kLag = kMergeLag + 2;
   // one LDS buffer of one chunk per wave (vector path): the next chunk is
   // copied in as soon as the current one has been read into registers
   __shared__ float4 stage[VEC ? kWaves * kChunkQuads : 1];
@@ -532,7 +536,7 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
   // exp values and wave maxima of rows n - 1, n - 2, n - 3 (with probs)
   float4 p1[PROBS ? kQ : 1], p2[PROBS ? kQ : 1], p3[PROBS ? kQ : 1];
   float m1 = -INFINITY, m2 = -INFINITY, m3 = -INFINITY;
-  int mturn = 0;  // (n - 1) % C
+  int mturn = 0;  // (n - kMergeLag) % C
   if constexpr (VEC) copy_chunk(0);
   for (int64_t n = 0; n < nrows; ++n) {
     const int64_t row = row_of(n);
@@ -569,8 +573,10 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
     compiler_fence();
     publish_tuple(tuple_rsrc(p, row), member, t, p.epoch);
     compiler_fence();
-    if (n >= 1 && mturn == member) merge_row<PROBS>(p, row_of(n - 1));
-    if (n >= 1 && ++mturn == p.C) mturn = 0;
+    if (n >= kMergeLag) {
+      if (mturn == member) merge_row<PROBS>(p, row_of(n - kMergeLag));
+      if (++mturn == p.C) mturn = 0;
+    }
     if constexpr (PROBS != 0) {
 #pragma unroll
       for (int j = 0; j < kQ; ++j) {
@@ -583,9 +589,14 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
       m1 = t.m;
     }
   }
-  if (mturn == member) merge_row<PROBS>(p, row_of(nrows - 1));
+  // the last kMergeLag rows (fewer if the group has fewer rows)
+  for (int64_t n = max(nrows - kMergeLag, (int64_t)0); n < nrows; ++n) {
+    if (mturn == member) merge_row<PROBS>(p, row_of(n));
+    if (++mturn == p.C) mturn = 0;
+  }
   if constexpr (PROBS != 0) {
-    // the last kLag rows' probabilities
+    // the last kLag rows' probabilities (kLag = 3 with probs)
+    static_assert(PROBS == 0 || kLag == 3, "three rows of exp values are kept");
     auto finish = [&](int64_t n, const float4 (&e)[kQ], float mw) {
       if (n < 0) return;
       const int64_t r = row_of(n);

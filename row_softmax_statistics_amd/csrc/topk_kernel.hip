@@ -504,10 +504,15 @@ __device__ __forceinline__ int64_t load_uniform_i64(const int64_t *p) {
 // The kernel. Global wave gw belongs to group gw / C as member gw % C: the
 // group reduces kept positions group, group + n_groups, ..., the member
 // chunk `member` of each. The merger of the group's n-th row is member
-// n % C; it merges row n after reducing row n + 1. Every member waits for
-// the row result of row n - kLag before merging, which keeps the waves of
-// a SIMD in step.
+// n % C; it merges row n after reducing row n + kMergeLag. Before merging,
+// every member waits for the row result of row n - kPaceLag, which keeps
+// the waves of a SIMD in step. A merge delays its merger's next chunks;
+// the merger of a later row waits for such a late chunk only when the
+// delay exceeds kMergeLag chunk periods.
 // ---------------------------------------------------------------------------
+constexpr int kMergeLag = 2;
+constexpr int kPaceLag = kMergeLag + 2;
+
 template <bool VEC>
 __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
   __shared__ float4 stage[VEC ? kWaves * kChunkQuads : 1];
@@ -539,12 +544,12 @@ __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
   };
 
   int64_t pos = group;
-  int64_t row = row_at(pos), next_row = row_at(pos + G), prev_row = row;
-  int mturn = 0;  // (n - 1) % C
+  int64_t row = row_at(pos), next_row = row_at(pos + G);
+  int mturn = 0;  // (n - kMergeLag) % C
   if constexpr (VEC) copy_chunk(pos, row);
   for (int n = 0; pos < n_kept; ++n, pos += G) {
     const int64_t after_row = row_at(pos + 2 * G);
-    u32x4 rr = load_row_result(p.rowres, n >= kLag ? pos - kLag * G : pos);
+    u32x4 rr = load_row_result(p.rowres, n >= kPaceLag ? pos - kPaceLag * G : pos);
     compiler_fence();
     float4 cur[kQ];
     if constexpr (VEC) {
@@ -566,14 +571,23 @@ __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
     compiler_fence();
     publish_record(p, pos, chunk, t);
     compiler_fence();
-    if (n >= kLag) rr = wait_row_result(p.rowres, pos - kLag * G, rr, p.epoch, p.err_flag);
-    if (n >= 1 && mturn == member) merge_row_topk(p, pos - G, prev_row, list);
-    if (n >= 1 && ++mturn == p.C) mturn = 0;
-    prev_row = row;
+    if (n >= kPaceLag)
+      rr = wait_row_result(p.rowres, pos - kPaceLag * G, rr, p.epoch, p.err_flag);
+    if (n >= kMergeLag) {
+      if (mturn == member) {
+        const int64_t mpos = pos - kMergeLag * G;
+        merge_row_topk(p, mpos, load_uniform_i64(p.kept + mpos), list);
+      }
+      if (++mturn == p.C) mturn = 0;
+    }
     row = next_row;
     next_row = after_row;
   }
-  if (mturn == member) merge_row_topk(p, pos - G, prev_row, list);
+  // the last kMergeLag rows (fewer if the group has fewer rows)
+  for (int64_t mpos = max(pos - kMergeLag * G, (int64_t)group); mpos < pos; mpos += G) {
+    if (mturn == member) merge_row_topk(p, mpos, load_uniform_i64(p.kept + mpos), list);
+    if (++mturn == p.C) mturn = 0;
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -12,6 +12,10 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
     # no packed fp32 instructions (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # atomics stay single instructions: the atomic optimizer would turn a
+    # one-lane counter claim into a wave reduction that waits for its result
+    # (and so for every memory operation in flight) right where it is issued
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-result", "-Wno-unknown-pragmas",
 ]
 

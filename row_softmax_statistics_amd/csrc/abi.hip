@@ -226,6 +226,8 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   if (K < 1 || (int64_t)K > vocab)
     return fail(ROWSTATS_ERR_K, "K must be in [1, vocab=%lld], got %d", (long long)vocab, K);
   if (K > kTopKMax) return fail(ROWSTATS_ERR_K, "K must be <= %d, got %d", kTopKMax, K);
+  if (rows > 0x7FFFFFFFLL)
+    return fail(ROWSTATS_ERR_SHAPE, "top-K takes at most 2^31 - 1 rows, got %lld", (long long)rows);
   if (!keep_mask) return fail(ROWSTATS_ERR_NULL, "keep_mask is NULL");
   if (!out_vals || !out_idx) return fail(ROWSTATS_ERR_NULL, "an output pointer is NULL");
 
@@ -263,14 +265,18 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   const int64_t grid = (groups * p.C + kWavesPerBlock - 1) / kWavesPerBlock;
 
   // records and row results are indexed by kept position (at most rows)
+  const size_t head_bytes = 256 + (size_t)groups * kRingBytes;  // claim counter, row rings
   const size_t record_bytes = (size_t)rows * p.C * topk_record_bytes(K);
   const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
   const size_t kept_bytes = ((size_t)rows + 1) * sizeof(int64_t);
   const size_t temp_bytes = ((size_t)rows * sizeof(float) + 15) & ~(size_t)15;
-  if ((rc = ensure_row_scratch(*d, record_bytes + rowres_bytes + kept_bytes + temp_bytes, s)))
+  if ((rc = ensure_row_scratch(*d, head_bytes + record_bytes + rowres_bytes + kept_bytes + temp_bytes, s)))
     return rc;
   if ((rc = next_epoch(*d, s, &p.epoch))) return rc;
   char *base = reinterpret_cast<char *>(d->row_scratch);
+  p.counter = reinterpret_cast<uint32_t *>(base);
+  p.rings = reinterpret_cast<uint64_t *>(base + 256);
+  base += head_bytes;
   p.records = reinterpret_cast<uint64_t *>(base);
   p.rowres = reinterpret_cast<uint64_t *>(base + record_bytes);
   p.kept_temp = reinterpret_cast<float *>(base + record_bytes + rowres_bytes);

@@ -212,4 +212,71 @@ __device__ __forceinline__ u32x4 wait_row_result(uint64_t *rowres, int64_t row, 
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Dynamic row assignment. Waves of different groups share a SIMD, and the
+// issue arbiter favours the oldest wave, so with a fixed share of rows per
+// group the groups finish at very different times and the last part of a
+// launch runs with few waves. Instead, the first kDealAhead rows of group
+// g are positions g + k G (G groups); after that, member 0 of the group
+// claims each next position from a call-wide counter kDealAhead rows before
+// the group needs it and posts it in the group's ring of kRingSlots slots.
+// A slot holds two tagged words {position | epoch, iteration | epoch}; a
+// position of -1 ends the group's rows. Claims only grow, so every position
+// below the limit is taken by exactly one group.
+// ---------------------------------------------------------------------------
+struct RowDealer {
+  uint64_t *ring;     // this group's ring
+  uint32_t *counter;  // this call's claim counter (zero at the start of the call)
+  int64_t limit;      // positions below it exist
+  int64_t first;      // first position handed out by claims: kDealAhead G
+  int64_t group, G;
+  uint32_t epoch;
+
+  __device__ __forceinline__ int64_t static_pos(int n) const {
+    const int64_t q = group + (int64_t)n * G;
+    return q < limit ? q : -1;
+  }
+  __device__ __forceinline__ Rsrc ring_rsrc() const { return make_rsrc(ring, (uint32_t)kRingBytes); }
+  __device__ __forceinline__ u32x4 load_slot(int n) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(ring_rsrc(), 16u * (uint32_t)(n % kRingSlots), 0,
+                                                 kDevScope);
+  }
+  __device__ __forceinline__ bool slot_ready(const u32x4 &w, int n) const {
+    return ((w[1] == epoch) & (w[3] == epoch) & (w[2] == (uint32_t)n)) != 0;
+  }
+  // Position of iteration n from its slot w (loaded earlier), waiting for
+  // the post if it is not there yet.
+  __device__ __forceinline__ int64_t slot_pos(u32x4 w, int n, uint32_t *err_flag) const {
+    if (!slot_ready(w, n)) {
+      uint32_t spins = 0;
+      do {
+        __builtin_amdgcn_s_sleep(1);
+        w = load_slot(n);
+      } while (!slot_ready(w, n) && ++spins <= kSpinLimit && !call_failed(err_flag));
+      if (!slot_ready(w, n)) {
+        if (lane_id() == 0) atomicOr(err_flag, 1u);
+        return -1;
+      }
+    }
+    return (int64_t)(int32_t)__builtin_amdgcn_readfirstlane((int)w[0]);
+  }
+  // Member 0: claims one position (lane 0 holds the counter value).
+  __device__ __forceinline__ uint32_t claim() const {
+    uint32_t v = 0;
+    if (lane_id() == 0) v = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+  }
+  __device__ __forceinline__ int64_t claimed_pos(uint32_t v) const {
+    const int64_t q = first + (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+    return q < limit ? q : -1;
+  }
+  __device__ __forceinline__ void post(int n, int64_t q) const {
+    if (lane_id() == 0) {
+      const u32x4 w = {(uint32_t)q, epoch, (uint32_t)n, epoch};
+      __builtin_amdgcn_raw_buffer_store_b128(w, ring_rsrc(), 16u * (uint32_t)(n % kRingSlots), 0,
+                                             kDevScope);
+    }
+  }
+};
+
 }  // namespace rowstats

@@ -20,6 +20,12 @@ constexpr int kTupleBytes = 64;
 // Per row: two tagged words (row maximum, 1 / sum) read by the probs writers.
 constexpr int kRowResultBytes = 16;
 
+// Dynamic row assignment (RowDealer): rows claimed this many rows ahead,
+// and a ring of this many 16-byte slots per group.
+constexpr int kDealAhead = 8;
+constexpr int kRingSlots = 16;
+constexpr int kRingBytes = 16 * kRingSlots;
+
 struct RowStatsParams {
   const float *logits;
   int64_t ld;

@@ -35,6 +35,8 @@ struct TopKParams {
   float *kept_temp;   // [rows]: temperature of kept row i (written by the pre-pass)
   uint64_t *records;  // [rows, C] records of topk_record_bytes(K), indexed by kept position
   uint64_t *rowres;   // [rows] row results of kRowResultBytes, indexed by kept position
+  uint64_t *rings;    // [n_groups] rings of kept positions (RowDealer)
+  uint32_t *counter;  // row-claim counter (zeroed by the pre-pass)
   uint32_t *err_flag;
 };
 

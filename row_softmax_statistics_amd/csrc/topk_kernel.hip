@@ -502,9 +502,9 @@ __device__ __forceinline__ int64_t load_uniform_i64(const int64_t *p) {
 
 // ---------------------------------------------------------------------------
 // The kernel. Global wave gw belongs to group gw / C as member gw % C: the
-// group reduces kept positions group, group + n_groups, ..., the member
-// chunk `member` of each. The merger of the group's n-th row is member
-// n % C; it merges row n after reducing row n + kMergeLag. Before merging,
+// group reduces one kept row at a time (positions from a RowDealer), the
+// member chunk `member` of each. The merger of the group's n-th row is
+// member n % C; it merges row n after reducing row n + kMergeLag. Before merging,
 // every member waits for the row result of row n - kPaceLag, which keeps
 // the waves of a SIMD in step. A merge delays its merger's next chunks;
 // the merger of a later row waits for such a late chunk only when the
@@ -526,12 +526,16 @@ __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
   if (group >= n_kept) return;
   const int32_t chunk = member;
   const int64_t G = p.n_groups;
-  // The group's rows are at kept positions group, group + G, ... below
-  // n_kept (all bounds are kept in positions: a row count would come from a
-  // 64-bit division, which leaves its result in vector registers).
-  auto row_at = [&](int64_t pos) -> int64_t {
-    return load_uniform_i64(p.kept + (pos < n_kept ? pos : (int64_t)group));
-  };
+  const bool leader = member == 0;
+  RowDealer d;
+  d.ring = p.rings + (int64_t)group * (kRingBytes / 8);
+  d.counter = p.counter;
+  d.limit = n_kept;
+  d.first = kDealAhead * G;
+  d.group = group;
+  d.G = G;
+  d.epoch = p.epoch;
+  auto row_at = [&](int64_t pos) -> int64_t { return load_uniform_i64(p.kept + (pos >= 0 ? pos : 0)); };
   float4 *const buf = stage + (VEC ? wave * kChunkQuads : 0);
   int64_t *const list = lists + wave * kCandKeys;
   // as in the row-statistics kernel, the copy past the last row still
@@ -539,68 +543,96 @@ __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
   // same operations
   const uint32_t bytes = chunk_bytes(chunk * kChunkCols, p.vocab);
   auto copy_chunk = [&](int64_t pos, int64_t row) {
-    chunk_copy_bytes(buf, pos < n_kept ? p.logits + row * p.ld + chunk * kChunkCols : p.logits,
-                     pos < n_kept ? bytes : 0u);
+    chunk_copy_bytes(buf, pos >= 0 ? p.logits + row * p.ld + chunk * kChunkCols : p.logits,
+                     pos >= 0 ? bytes : 0u);
   };
 
-  int64_t pos = group;
-  int64_t row = row_at(pos), next_row = row_at(pos + G);
+  // positions of iterations n (pos), n + 1 and n - 1 .. n - kPaceLag (hist)
+  int64_t pos = group, pos_next = d.static_pos(1);
+  int64_t row = row_at(pos), row_next = row_at(pos_next);
+  int64_t hist[kPaceLag];
+#pragma unroll
+  for (int i = 0; i < kPaceLag; ++i) hist[i] = -1;
+  bool claiming = leader;
   int mturn = 0;  // (n - kMergeLag) % C
   if constexpr (VEC) copy_chunk(pos, row);
-  for (int n = 0; pos < n_kept; ++n, pos += G) {
-    const int64_t after_row = row_at(pos + 2 * G);
-    u32x4 rr = load_row_result(p.rowres, n >= kPaceLag ? pos - kPaceLag * G : pos);
+  for (int n = 0; pos >= 0; ++n) {
+    const int64_t pace_pos = hist[kPaceLag - 1];
+    u32x4 rr = load_row_result(p.rowres, pace_pos >= 0 ? pace_pos : pos);
+    u32x4 slot = d.load_slot(n + 2);
+    uint32_t claim = 0;
+    if (claiming) claim = d.claim();
     compiler_fence();
     float4 cur[kQ];
     if constexpr (VEC) {
-      // after this row's copy came, in the previous row, its record stores,
-      // the merger's work and this row's row-result load
-      wait_vm<1>();
+      // after this row's copy came, in the previous row, at least its record
+      // header store, then this row's row-result and slot loads and (member
+      // 0) its claim
+      if (leader) wait_vm<3>();
+      else wait_vm<2>();
       lds_read_chunk(cur, buf);
       compiler_fence();
-      copy_chunk(pos + G, next_row);
+      copy_chunk(pos_next, row_next);
       compiler_fence();
     } else {
       chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
     }
     ChunkTop t;
     reduce_chunk_topk<VEC>(p, load_uniform(p.kept_temp + pos), chunk, cur, list, t);
-    // consume rr before the record stores, so that its wait does not wait
-    // for the copy above
-    __asm__ volatile("" ::"v"(rr));
+    // consume the loads issued before the copy here, before the record
+    // stores, so that their wait does not wait for the copy above
+    __asm__ volatile("" ::"v"(rr), "v"(slot), "v"(claim));
     compiler_fence();
+    const int64_t pos_after = n + 2 < kDealAhead ? d.static_pos(n + 2) : d.slot_pos(slot, n + 2, p.err_flag);
+    const int64_t row_after = row_at(pos_after);
+    if (leader) {
+      int64_t q = -1;
+      if (claiming) {
+        q = d.claimed_pos(claim);
+        claiming = q >= 0;
+      }
+      d.post(n + kDealAhead, q);
+    }
     publish_record(p, pos, chunk, t);
     compiler_fence();
-    if (n >= kPaceLag)
-      rr = wait_row_result(p.rowres, pos - kPaceLag * G, rr, p.epoch, p.err_flag);
+    if (pace_pos >= 0) rr = wait_row_result(p.rowres, pace_pos, rr, p.epoch, p.err_flag);
     if (n >= kMergeLag) {
       if (mturn == member) {
-        const int64_t mpos = pos - kMergeLag * G;
-        merge_row_topk(p, mpos, load_uniform_i64(p.kept + mpos), list);
+        const int64_t mpos = hist[kMergeLag - 1];
+        merge_row_topk(p, mpos, row_at(mpos), list);
       }
       if (++mturn == p.C) mturn = 0;
     }
-    row = next_row;
-    next_row = after_row;
+#pragma unroll
+    for (int i = kPaceLag - 1; i > 0; --i) hist[i] = hist[i - 1];
+    hist[0] = pos;
+    pos = pos_next;
+    pos_next = pos_after;
+    row = row_next;
+    row_next = row_after;
   }
   // the last kMergeLag rows (fewer if the group has fewer rows)
-  for (int64_t mpos = max(pos - kMergeLag * G, (int64_t)group); mpos < pos; mpos += G) {
-    if (mturn == member) merge_row_topk(p, mpos, load_uniform_i64(p.kept + mpos), list);
+#pragma unroll
+  for (int i = kMergeLag - 1; i >= 0; --i) {
+    if (hist[i] < 0) continue;
+    if (mturn == member) merge_row_topk(p, hist[i], row_at(hist[i]), list);
     if (++mturn == p.C) mturn = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Kept-row list: kept[0 .. n) = the rows of kept slots in order, kept[rows]
-// = n, and kept_temp[i] = the temperature of row kept[i]. One workgroup;
-// thread t handles a contiguous range of rows.
+// = n, and kept_temp[i] = the temperature of row kept[i]; also zeroes the
+// row-claim counter. One workgroup; thread t handles a contiguous range of
+// rows.
 // ---------------------------------------------------------------------------
 constexpr int kListThreads = 1024;
 
 __global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *keep,
                                                                const float *temps, int64_t rows,
                                                                int64_t canvas_len, int64_t *kept,
-                                                               float *kept_temp) {
+                                                               float *kept_temp,
+                                                               uint32_t *counter) {
   __shared__ int64_t wave_tot[kListThreads / kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -636,7 +668,10 @@ __global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *
     }
     r = end;
   }
-  if (tid == kListThreads - 1) kept[rows] = off;
+  if (tid == kListThreads - 1) {
+    kept[rows] = off;
+    *counter = 0u;  // the row claims of the kernel that follows
+  }
 }
 
 }  // namespace
@@ -652,8 +687,8 @@ hipError_t topk_resident_blocks(bool vec, int *blocks_per_cu) {
 }
 
 hipError_t topk_launch(const TopKParams &p, int grid, hipStream_t stream) {
-  kept_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(p.keep, p.temps, p.rows,
-                                                                 p.canvas_len, p.kept, p.kept_temp);
+  kept_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(
+      p.keep, p.temps, p.rows, p.canvas_len, p.kept, p.kept_temp, p.counter);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   TopKParams arg = p;

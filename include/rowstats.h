@@ -28,9 +28,9 @@ extern "C" {
 typedef enum rowstats_status {
   ROWSTATS_OK = 0,
   ROWSTATS_ERR_NULL = -1,   /* a required pointer is NULL */
-  ROWSTATS_ERR_SHAPE = -2,  /* rows < 0, or (rows > 0 and: vocab < 1,
-                               vocab > 2^31 - 1 - 65536, row_stride < vocab,
-                               canvas_len < 1) */
+  ROWSTATS_ERR_SHAPE = -2,  /* rows < 0, or (rows > 0 and: rows > 2^31 - 1,
+                               vocab < 1, vocab > 2^31 - 1 - 65536,
+                               row_stride < vocab, canvas_len < 1) */
   ROWSTATS_ERR_K = -3,      /* K < 1, K > vocab or K > 64 */
   ROWSTATS_ERR_DTYPE = -4,  /* probs_dtype is not one of rowstats_probs_dtype */
   ROWSTATS_ERR_HIP = -5,    /* a HIP call failed (allocation, launch); see last_error */
@@ -61,7 +61,7 @@ typedef enum rowstats_probs_dtype {
  *               Values are finite or -inf; no row is all -inf; x / T stays
  *               finite in fp32 (not checked on the device).
  *   rows, vocab matrix shape; rows == 0 returns at once;
- *               1 <= vocab <= 2^31 - 1 - 65536.
+ *               rows <= 2^31 - 1; 1 <= vocab <= 2^31 - 1 - 65536.
  *   temps       fp32, at least ceil(rows / canvas_len) entries; row r uses
  *               T = temps[r / canvas_len]. T > 0 samples with Gumbel noise;
  *               T <= 0 is greedy (sample = argmax). The scaled logits are

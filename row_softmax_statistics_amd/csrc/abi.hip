@@ -33,6 +33,10 @@ int fail_hip(hipError_t e, const char *what) {
 }
 
 constexpr int kMaxDevices = 64;
+// Start of the scratch buffer, for both entry points: the two row-claim
+// counters (at the same place for every call, since each call zeroes the
+// counter of the next one); the groups' row rings follow.
+constexpr size_t kScratchHead = 256;
 // Columns (and the padding columns of a row's last slice) index as int32 and
 // the top-K key stores 0x7FFFFFFF - column: keep them all below 2^31.
 constexpr int64_t kMaxVocab = 0x7FFFFFFFLL - 65536;
@@ -142,7 +146,9 @@ int check_common(const float *logits, int64_t row_stride, int64_t rows, int64_t 
     return fail(ROWSTATS_ERR_SHAPE, "canvas_len must be >= 1, got %lld", (long long)canvas_len);
   if (!logits) return fail(ROWSTATS_ERR_NULL, "logits is NULL");
   if (!temps) return fail(ROWSTATS_ERR_NULL, "temps is NULL");
-  (void)rows;
+  // rows are handed out as 32-bit positions
+  if (rows > 0x7FFFFFFFLL)
+    return fail(ROWSTATS_ERR_SHAPE, "rows must be <= 2^31 - 1, got %lld", (long long)rows);
   return ROWSTATS_OK;
 }
 
@@ -182,6 +188,7 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
              (vocab % 4 == 0) && ((reinterpret_cast<uintptr_t>(probs) & 7) == 0);
   p.temps = temps;
   p.canvas_len = canvas_len;
+  slot_divider(canvas_len, &p.slot_mul, &p.slot_shift);
   p.seed = seed;
   p.argmax = argmax;
   p.sample = sample;
@@ -203,12 +210,16 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
   p.n_groups = (int32_t)groups;
   const int64_t grid = (groups * p.C + kWavesPerBlock - 1) / kWavesPerBlock;
 
+  const size_t head_bytes = kScratchHead + (size_t)groups * kRingBytes;
   const size_t tuple_bytes = (size_t)rows * p.C * kTupleBytes;
   const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
-  if ((rc = ensure_row_scratch(*d, tuple_bytes + rowres_bytes, s))) return rc;
+  if ((rc = ensure_row_scratch(*d, head_bytes + tuple_bytes + rowres_bytes, s))) return rc;
   if ((rc = next_epoch(*d, s, &p.epoch))) return rc;
-  p.tuples = reinterpret_cast<uint64_t *>(d->row_scratch);
-  p.rowres = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(d->row_scratch) + tuple_bytes);
+  char *base = reinterpret_cast<char *>(d->row_scratch);
+  p.counters = reinterpret_cast<uint32_t *>(base);
+  p.rings = reinterpret_cast<uint64_t *>(base + kScratchHead);
+  p.tuples = reinterpret_cast<uint64_t *>(base + head_bytes);
+  p.rowres = reinterpret_cast<uint64_t *>(base + head_bytes + tuple_bytes);
   p.err_flag = d->err_flag;
   hipError_t e = rowstats_launch(p, probs_dtype, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
@@ -226,8 +237,6 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   if (K < 1 || (int64_t)K > vocab)
     return fail(ROWSTATS_ERR_K, "K must be in [1, vocab=%lld], got %d", (long long)vocab, K);
   if (K > kTopKMax) return fail(ROWSTATS_ERR_K, "K must be <= %d, got %d", kTopKMax, K);
-  if (rows > 0x7FFFFFFFLL)
-    return fail(ROWSTATS_ERR_SHAPE, "top-K takes at most 2^31 - 1 rows, got %lld", (long long)rows);
   if (!keep_mask) return fail(ROWSTATS_ERR_NULL, "keep_mask is NULL");
   if (!out_vals || !out_idx) return fail(ROWSTATS_ERR_NULL, "an output pointer is NULL");
 
@@ -265,7 +274,7 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   const int64_t grid = (groups * p.C + kWavesPerBlock - 1) / kWavesPerBlock;
 
   // records and row results are indexed by kept position (at most rows)
-  const size_t head_bytes = 256 + (size_t)groups * kRingBytes;  // claim counter, row rings
+  const size_t head_bytes = kScratchHead + (size_t)groups * kRingBytes;
   const size_t record_bytes = (size_t)rows * p.C * topk_record_bytes(K);
   const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
   const size_t kept_bytes = ((size_t)rows + 1) * sizeof(int64_t);
@@ -274,8 +283,8 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
     return rc;
   if ((rc = next_epoch(*d, s, &p.epoch))) return rc;
   char *base = reinterpret_cast<char *>(d->row_scratch);
-  p.counter = reinterpret_cast<uint32_t *>(base);
-  p.rings = reinterpret_cast<uint64_t *>(base + 256);
+  p.counters = reinterpret_cast<uint32_t *>(base);
+  p.rings = reinterpret_cast<uint64_t *>(base + kScratchHead);
   base += head_bytes;
   p.records = reinterpret_cast<uint64_t *>(base);
   p.rowres = reinterpret_cast<uint64_t *>(base + record_bytes);

@@ -37,6 +37,8 @@ struct RowStatsParams {
   uint32_t epoch;     // tag of this call's scratch words (never 0)
   const float *temps;
   int64_t canvas_len;
+  uint32_t slot_mul;  // row / canvas_len = (row * slot_mul) >> slot_shift for 0 <= row < 2^31
+  uint32_t slot_shift;
   uint64_t seed;
   int64_t *argmax;
   int64_t *sample;
@@ -44,8 +46,29 @@ struct RowStatsParams {
   void *probs;
   uint64_t *tuples;   // [rows, C] tuples of kTupleBytes
   uint64_t *rowres;   // [rows] row results of kRowResultBytes
+  uint64_t *rings;    // [n_groups] rings of rows (RowDealer)
+  uint32_t *counters; // two row-claim counters: a call uses counters[epoch & 1]
+                      // and zeroes counters[(epoch + 1) & 1] for the next call
   uint32_t *err_flag;
 };
+
+// Multiplier and shift with floor(n / d) = (n * mul) >> shift for every
+// 0 <= n < 2^31 (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", 1994, with the multiplier rounded up): for
+// 2^(l-1) < d <= 2^l, mul = ceil(2^(31 + l) / d) < 2^32 and shift = 31 + l.
+// d >= 2^31 maps every such n to 0.
+inline void slot_divider(int64_t d, uint32_t *mul, uint32_t *shift) {
+  if (d >= 0x80000000LL) {
+    *mul = 0;
+    *shift = 0;
+    return;
+  }
+  int l = 0;
+  while ((int64_t(1) << l) < d) ++l;
+  const uint64_t two = uint64_t(1) << (31 + l);
+  *mul = (uint32_t)((two + (uint64_t)d - 1) / (uint64_t)d);
+  *shift = (uint32_t)(31 + l);
+}
 
 hipError_t rowstats_resident_blocks(int probs_dtype, bool vec, int *blocks_per_cu);
 hipError_t rowstats_launch(const RowStatsParams &p, int probs_dtype, int grid,

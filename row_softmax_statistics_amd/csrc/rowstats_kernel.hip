@@ -87,6 +87,13 @@ __device__ __forceinline__ void add_rescaled(const Tuple &t, float m, double &S,
   }
 }
 
+// Temperature slot of a row, row / canvas_len, as (row * slot_mul) >> slot_shift
+// (exact for every row below 2^31): scalar arithmetic, where a 64-bit
+// division would go through vector registers.
+__device__ __forceinline__ int64_t slot_of(const RowStatsParams &p, int64_t row) {
+  return (int64_t)(((uint64_t)(uint32_t)row * p.slot_mul) >> p.slot_shift);
+}
+
 // Merge of two summaries.
 __device__ __forceinline__ Tuple combine(const Tuple &a, const Tuple &b) {
   Tuple r;
@@ -142,7 +149,7 @@ __device__ __forceinline__ uint32_t tuple_payload(const Tuple &t, int k) {
 // Lanes 0..3 store two tagged words each (one 16-byte store instruction).
 __device__ __forceinline__ void publish_tuple(const Rsrc &r, int member, const Tuple &t,
                                               uint32_t epoch) {
-  const int lane = lane_id();
+  const int lane = lane_here();
   if (lane < 4) {
     const u32x4 v = {tuple_payload(t, 2 * lane), epoch, tuple_payload(t, 2 * lane + 1), epoch};
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (uint32_t)(member * kTupleBytes + 16 * lane), 0,
@@ -222,7 +229,7 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
     }
   }
   Tuple m = wave_merge(acc);
-  const float T = load_uniform(p.temps + row / p.canvas_len);
+  const float T = load_uniform(p.temps + slot_of(p, row));
   const bool greedy = !(T > 0.0f);
   const double zmax = wave_allreduce(b1, MaxD());
   if (!greedy && zmax != -INFINITY) {
@@ -272,7 +279,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
                                               float4 (&v)[kQ], bool exact) {
   const int lane = lane_id();
   const int32_t V = p.vocab;
-  const float T = load_uniform(p.temps + row / p.canvas_len);
+  const float T = load_uniform(p.temps + slot_of(p, row));
   const bool greedy = !(T > 0.0f);
   const double rtc = 1.0 / (double)clamp_temp(T);
   const int32_t c0 = chunk * kChunkCols;
@@ -492,8 +499,8 @@ __device__ __forceinline__ void write_probs(const RowStatsParams &p, int64_t row
 
 // ---------------------------------------------------------------------------
 // The kernel. Global wave gw belongs to group gw / C as member gw % C: the
-// group reduces rows group, group + n_groups, ..., the member chunk `member`
-// of each. The merger of the group's n-th row is member n % C; it merges
+// group reduces one row at a time (rows from a RowDealer), the member chunk
+// `member` of each. The merger of the group's n-th row is member n % C; it merges
 // row n after reducing row n + kMergeLag. Before publishing row n, every
 // member waits for the result of row n - kLag (normally there for a whole
 // chunk): with probs it needs it to write that row's probabilities, and
@@ -513,68 +520,95 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
   __shared__ float4 stage[VEC ? kWaves * kChunkQuads : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int gw = (int)blockIdx.x * kWaves + wave;
+  // the next call's row-claim counter starts at zero
+  if (gw == 0 && lane_id() == 0) p.counters[(p.epoch + 1) & 1] = 0u;
   const int group = gw / p.C;
   const int member = gw - group * p.C;
-  if (group >= p.n_groups) return;
-  const int64_t nrows = (p.rows - group + p.n_groups - 1) / p.n_groups;
-  if (nrows <= 0) return;
+  if (group >= p.n_groups || group >= p.rows) return;
   const int32_t chunk = member;
-  auto row_of = [&](int64_t n) -> int64_t { return group + n * p.n_groups; };
+  const bool leader = member == 0;
+  RowDealer d;
+  d.ring = p.rings + (int64_t)group * (kRingBytes / 8);
+  d.counter = p.counters + (p.epoch & 1);
+  d.limit = p.rows;
+  d.first = (int64_t)kDealAhead * p.n_groups;
+  d.group = group;
+  d.G = p.n_groups;
+  d.epoch = p.epoch;
   float4 *const buf = stage + (VEC ? wave * kChunkQuads : 0);
-  // Copies the chunk of the group's row n into the wave's buffer. Past the
-  // last row the copy still issues (through a zero-size descriptor: nothing
+  // Copies the chunk of row `row` into the wave's buffer. Past the last row
+  // (row < 0) the copy still issues (through a zero-size descriptor: nothing
   // is read, the buffer gets zeros), so every path issues the same
   // operations and the compiler can count them exactly.
-  auto copy_chunk = [&](int64_t n) {
-    if (n < nrows)
-      chunk_copy_async(buf, p.logits + row_of(n) * p.ld, chunk * kChunkCols, p.vocab);
-    else
-      chunk_copy_async(buf, p.logits, 0, 0);
+  const uint32_t bytes = chunk_bytes(chunk * kChunkCols, p.vocab);
+  auto copy_chunk = [&](int64_t row) {
+    chunk_copy_bytes(buf, row >= 0 ? p.logits + row * p.ld + chunk * kChunkCols : p.logits,
+                     row >= 0 ? bytes : 0u);
   };
 
   float4 cur[kQ];
   // exp values and wave maxima of rows n - 1, n - 2, n - 3 (with probs)
   float4 p1[PROBS ? kQ : 1], p2[PROBS ? kQ : 1], p3[PROBS ? kQ : 1];
   float m1 = -INFINITY, m2 = -INFINITY, m3 = -INFINITY;
+  // rows of iterations n (row), n + 1 and n - 1 .. n - kLag (hist)
+  int64_t row = group, row_next = d.static_pos(1);
+  int64_t hist[kLag];
+#pragma unroll
+  for (int i = 0; i < kLag; ++i) hist[i] = -1;
   int mturn = 0;  // (n - kMergeLag) % C
-  if constexpr (VEC) copy_chunk(0);
-  for (int64_t n = 0; n < nrows; ++n) {
-    const int64_t row = row_of(n);
+  if constexpr (VEC) copy_chunk(row);
+  for (int n = 0; row >= 0; ++n) {
+    const int64_t pace_row = hist[kLag - 1];
     // row result of row n - kLag, written by its merger more than a chunk
     // ago (loaded every time so that no path leaves the register waiting on
-    // a load)
-    u32x4 rr = load_row_result(p.rowres, row_of(n >= kLag ? n - kLag : 0));
+    // a load), the ring slot of row n + 2 and (member 0) a claim
+    u32x4 rr = load_row_result(p.rowres, pace_row >= 0 ? pace_row : row);
+    u32x4 slot = d.load_slot(n + 2);
+    uint32_t claim = 0;
+    if (leader) claim = d.claim();
     compiler_fence();
     if constexpr (VEC) {
-      // after this item's copy came, in the previous item, its eight probs
-      // stores (with probs, once rows are kLag behind), its summary store
-      // and this item's row-result load
+      // The copy of this row's chunk was followed, in the previous row, by
+      // (member 0) a ring post, with probs (once rows are kLag behind) eight
+      // probs stores, the summary store, and in this row by the row-result
+      // and slot loads; at most that many operations may still be pending.
       if (n == 0) wait_vm<0>();
-      else if (PROBS != 0 && n > kLag) wait_vm<9>();
-      else wait_vm<1>();
+      else if (PROBS != 0 && n > kLag) {
+        if (leader) wait_vm<12>();
+        else wait_vm<11>();
+      } else {
+        if (leader) wait_vm<4>();
+        else wait_vm<3>();
+      }
       lds_read_chunk(cur, buf);
       compiler_fence();
-      copy_chunk(n + 1);
+      copy_chunk(row_next);
       compiler_fence();
     } else {
       chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
     }
     const Tuple t = reduce_chunk<VEC>(p, row, chunk, cur, false);
+    // The empty statement consumes the loads issued before the copy on
+    // every path, so the wait for them is placed here, exactly, and does not
+    // wait for the copy.
+    __asm__ volatile("" ::"v"(rr), "v"(slot), "v"(claim));
+    compiler_fence();
+    const int64_t row_after =
+        n + 2 < kDealAhead ? d.static_pos(n + 2) : d.slot_pos(slot, n + 2, p.err_flag);
+    if (leader) d.post(n + kDealAhead, d.claimed_pos(claim));
     // row n - kLag first: waiting for its result then does not wait for the
-    // summary store below. The empty statement consumes rr on every path,
-    // so the wait for its load is placed here, exactly.
-    __asm__ volatile("" ::"v"(rr));
-    if (n >= kLag) {
-      rr = wait_row_result(p.rowres, row_of(n - kLag), rr, p.epoch, p.err_flag);
+    // summary store below
+    if (pace_row >= 0) {
+      rr = wait_row_result(p.rowres, pace_row, rr, p.epoch, p.err_flag);
       if constexpr (PROBS != 0)
-        write_probs<PROBS, VEC>(p, row_of(n - kLag), chunk, p3,
+        write_probs<PROBS, VEC>(p, pace_row, chunk, p3,
                                 prob_scale(m3, __uint_as_float(rr[0]), __uint_as_float(rr[2])));
     }
     compiler_fence();
     publish_tuple(tuple_rsrc(p, row), member, t, p.epoch);
     compiler_fence();
     if (n >= kMergeLag) {
-      if (mturn == member) merge_row<PROBS>(p, row_of(n - kMergeLag));
+      if (mturn == member) merge_row<PROBS>(p, hist[kMergeLag - 1]);
       if (++mturn == p.C) mturn = 0;
     }
     if constexpr (PROBS != 0) {
@@ -588,24 +622,30 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
       m2 = m1;
       m1 = t.m;
     }
+#pragma unroll
+    for (int i = kLag - 1; i > 0; --i) hist[i] = hist[i - 1];
+    hist[0] = row;
+    row = row_next;
+    row_next = row_after;
   }
   // the last kMergeLag rows (fewer if the group has fewer rows)
-  for (int64_t n = max(nrows - kMergeLag, (int64_t)0); n < nrows; ++n) {
-    if (mturn == member) merge_row<PROBS>(p, row_of(n));
+#pragma unroll
+  for (int i = kMergeLag - 1; i >= 0; --i) {
+    if (hist[i] < 0) continue;
+    if (mturn == member) merge_row<PROBS>(p, hist[i]);
     if (++mturn == p.C) mturn = 0;
   }
   if constexpr (PROBS != 0) {
     // the last kLag rows' probabilities (kLag = 3 with probs)
     static_assert(PROBS == 0 || kLag == 3, "three rows of exp values are kept");
-    auto finish = [&](int64_t n, const float4 (&e)[kQ], float mw) {
-      if (n < 0) return;
-      const int64_t r = row_of(n);
+    auto finish = [&](int64_t r, const float4 (&e)[kQ], float mw) {
+      if (r < 0) return;
       const u32x4 v = wait_row_result(p.rowres, r, load_row_result(p.rowres, r), p.epoch, p.err_flag);
       write_probs<PROBS, VEC>(p, r, chunk, e, prob_scale(mw, __uint_as_float(v[0]), __uint_as_float(v[2])));
     };
-    finish(nrows - 3, p3, m3);
-    finish(nrows - 2, p2, m2);
-    finish(nrows - 1, p1, m1);
+    finish(hist[2], p3, m3);
+    finish(hist[1], p2, m2);
+    finish(hist[0], p1, m1);
   }
 }
 

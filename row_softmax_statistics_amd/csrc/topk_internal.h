@@ -36,7 +36,8 @@ struct TopKParams {
   uint64_t *records;  // [rows, C] records of topk_record_bytes(K), indexed by kept position
   uint64_t *rowres;   // [rows] row results of kRowResultBytes, indexed by kept position
   uint64_t *rings;    // [n_groups] rings of kept positions (RowDealer)
-  uint32_t *counter;  // row-claim counter (zeroed by the pre-pass)
+  uint32_t *counters; // two row-claim counters: a call uses counters[epoch & 1]
+                      // (the pre-pass zeroes both)
   uint32_t *err_flag;
 };
 

@@ -529,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
   const bool leader = member == 0;
   RowDealer d;
   d.ring = p.rings + (int64_t)group * (kRingBytes / 8);
-  d.counter = p.counter;
+  d.counter = p.counters + (p.epoch & 1);
   d.limit = n_kept;
   d.first = kDealAhead * G;
   d.group = group;
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
 // ---------------------------------------------------------------------------
 // Kept-row list: kept[0 .. n) = the rows of kept slots in order, kept[rows]
 // = n, and kept_temp[i] = the temperature of row kept[i]; also zeroes the
-// row-claim counter. One workgroup; thread t handles a contiguous range of
+// row-claim counters. One workgroup; thread t handles a contiguous range of
 // rows.
 // ---------------------------------------------------------------------------
 constexpr int kListThreads = 1024;
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *
                                                                const float *temps, int64_t rows,
                                                                int64_t canvas_len, int64_t *kept,
                                                                float *kept_temp,
-                                                               uint32_t *counter) {
+                                                               uint32_t *counters) {
   __shared__ int64_t wave_tot[kListThreads / kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -670,7 +670,9 @@ __global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *
   }
   if (tid == kListThreads - 1) {
     kept[rows] = off;
-    *counter = 0u;  // the row claims of the kernel that follows
+    // row-claim counters of the kernel that follows and of the next call
+    counters[0] = 0u;
+    counters[1] = 0u;
   }
 }
 
@@ -688,7 +690,7 @@ hipError_t topk_resident_blocks(bool vec, int *blocks_per_cu) {
 
 hipError_t topk_launch(const TopKParams &p, int grid, hipStream_t stream) {
   kept_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(
-      p.keep, p.temps, p.rows, p.canvas_len, p.kept, p.kept_temp, p.counter);
+      p.keep, p.temps, p.rows, p.canvas_len, p.kept, p.kept_temp, p.counters);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   TopKParams arg = p;

@@ -55,6 +55,7 @@ def topk(logits=FAKE, stride=8, rows=4, vocab=8, temps=FAKE, canvas=2, keep=FAKE
     (dict(dtype=3), ERR_DTYPE),
     (dict(dtype=-1), ERR_DTYPE),
     (dict(rows=-1), ERR_SHAPE),
+    (dict(rows=2**31), ERR_SHAPE),
     (dict(vocab=0), ERR_SHAPE),
     (dict(vocab=2**31), ERR_SHAPE),
     (dict(stride=7), ERR_SHAPE),
@@ -82,6 +83,7 @@ def test_rowstats_run_zero_rows_is_a_no_op():
     (dict(K=9), ERR_K),
     (dict(K=65, vocab=100, stride=100), ERR_K),
     (dict(rows=-2), ERR_SHAPE),
+    (dict(rows=2**31), ERR_SHAPE),
     (dict(vocab=0), ERR_SHAPE),
     (dict(stride=3), ERR_SHAPE),
     (dict(canvas=0), ERR_SHAPE),

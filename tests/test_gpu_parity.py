@@ -57,6 +57,27 @@ def test_small_shapes(vocab, pad, probs_dtype):
     done()
 
 
+@pytest.mark.parametrize("canvas", [1, 7, 13, 39, 40, 41, 1000003, 2**31 + 5])
+def test_temperature_slots(canvas):
+    # row r takes temps[r // canvas]; the kernel divides by a multiplier
+    w = syn.random_case(DEV, rows=40, vocab=300, canvas_len=canvas, seed=canvas % 997,
+                        t_choices=(0.0, 0.3, 0.7, 1.0, 1.9))
+    out = gpu_rowstats(w)
+    compare_rowstats(w, out, range(w.rows), f"canvas={canvas}")
+    done()
+
+
+@pytest.mark.parametrize("probs_dtype", [None, torch.bfloat16], ids=["none", "bf16"])
+def test_many_rows_per_group(probs_dtype):
+    # more rows than the statically assigned first rows of every group, so
+    # most rows are handed out through the groups' rings
+    w = syn.random_case(DEV, rows=333, vocab=200003, canvas_len=10, seed=17,
+                        t_choices=(0.0, 0.6, 1.0), probs_dtype=probs_dtype)
+    out = gpu_rowstats(w)
+    compare_rowstats(w, out, range(w.rows), "rows=333")
+    done()
+
+
 @pytest.mark.parametrize("vocab", [37, 20000, 49153])
 def test_quantised_ties(vocab):
     # logits on a 0.5 grid: exact duplicates everywhere, including the max
@@ -194,6 +215,15 @@ def test_topk_adversarial_rows():
     w.logits[4] = torch.linspace(-1, 1, vocab, device=DEV)
     vals, idx = _run_topk(w)
     compare_topk(w, vals, idx, range(w.rows), "topk adversarial")
+    done()
+
+
+def test_topk_many_rows_per_group():
+    # kept rows handed out through the groups' rings (see test_many_rows_per_group)
+    w = _topk_case(rows=500, vocab=200003, canvas=5, K=17, seed=23)
+    vals, idx = _run_topk(w)
+    _check_untouched(w, vals, idx)
+    compare_topk(w, vals, idx, range(w.rows), "topk rows=500")
     done()
 
 

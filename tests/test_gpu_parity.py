@@ -218,6 +218,37 @@ def test_topk_adversarial_rows():
     done()
 
 
+def _magnitude_rows(rows, vocab, seed):
+    """Rows whose values span the fp32 range: ordinary, tiny (below 2^-100),
+    subnormal, zero, huge and -inf, so that chunks fall on both sides of the
+    fp32 scaling's range check."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn(rows, vocab, generator=g) * 2.0
+    kinds = torch.arange(rows) % 6
+    x[kinds == 1] *= 1e-32                           # tiny
+    x[kinds == 2] *= 1e-39                           # subnormal
+    x[kinds == 3, ::7] = 0.0                         # zeros
+    x[kinds == 4] *= 1e22                            # huge (x / T stays finite)
+    x[kinds == 5, 100:2000] = float("-inf")          # a -inf span
+    return x
+
+
+@pytest.mark.parametrize("temp", [0.0, 1e-3, 0.37, 1.0, 3.7, 1000.0])
+def test_scaling_ranges(temp):
+    # s = fl32(x / max(T, 1e-10)) must be the IEEE quotient on every path
+    rows, vocab = 12, 6000
+    x = _magnitude_rows(rows, vocab, seed=int(temp * 1000) % 9973)
+    w = syn.Workload(f"mag{temp}", x.to(DEV), torch.full((rows,), temp, device=DEV), 1, 4242,
+                     torch.bfloat16)
+    out = gpu_rowstats(w)
+    compare_rowstats(w, out, range(rows), f"magnitudes T={temp}")
+    w.keep_mask = torch.ones(rows, dtype=torch.uint8, device=DEV)
+    w.K = 9
+    vals, idx = _run_topk(w)
+    compare_topk(w, vals, idx, range(rows), f"topk magnitudes T={temp}")
+    done()
+
+
 def test_topk_many_rows_per_group():
     # kept rows handed out through the groups' rings (see test_many_rows_per_group)
     w = _topk_case(rows=500, vocab=200003, canvas=5, K=17, seed=23)

@@ -78,6 +78,35 @@ def test_many_rows_per_group(probs_dtype):
     done()
 
 
+@pytest.mark.parametrize("probs_dtype", [None, torch.float16], ids=["none", "fp16"])
+def test_one_wave_groups(probs_dtype):
+    # vocab <= 2048: a group is one wave, which claims, posts and reads its
+    # own rows; many more rows than groups
+    w = syn.random_case(DEV, rows=20000, vocab=37, canvas_len=7, seed=29,
+                        t_choices=(0.0, 0.6, 1.0, 1.4), probs_dtype=probs_dtype)
+    out = gpu_rowstats(w)
+    rows = sample_rows(w.rows, 3000, 6, extra=[0, 1, w.rows - 2, w.rows - 1])
+    compare_rowstats(w, out, rows, "one-wave groups")
+    check_properties(w, out)
+    done()
+
+
+def test_alternating_entry_points():
+    # row-stats and top-K calls share the row-claim counters; each call must
+    # find its counter at zero whatever the previous call was
+    w = syn.random_case(DEV, rows=600, vocab=200003, canvas_len=6, seed=31,
+                        t_choices=(0.0, 0.5, 1.0), probs_dtype=torch.bfloat16)
+    w.keep_mask = (torch.arange(w.temps.numel(), device=DEV) % 4 != 2).to(torch.uint8)
+    w.K = 11
+    for it in range(3):
+        out = gpu_rowstats(w)
+        compare_rowstats(w, out, sample_rows(w.rows, 60, it), f"alternating rowstats {it}")
+        vals, idx = _run_topk(w)
+        _check_untouched(w, vals, idx)
+        compare_topk(w, vals, idx, sample_rows(w.rows, 60, 10 + it), f"alternating topk {it}")
+    done()
+
+
 @pytest.mark.parametrize("vocab", [37, 20000, 49153])
 def test_quantised_ties(vocab):
     # logits on a 0.5 grid: exact duplicates everywhere, including the max
@@ -255,6 +284,14 @@ def test_topk_many_rows_per_group():
     vals, idx = _run_topk(w)
     _check_untouched(w, vals, idx)
     compare_topk(w, vals, idx, range(w.rows), "topk rows=500")
+    done()
+
+
+def test_topk_one_wave_groups():
+    w = _topk_case(rows=20000, vocab=300, canvas=5, K=5, seed=37)
+    vals, idx = _run_topk(w)
+    _check_untouched(w, vals, idx)
+    compare_topk(w, vals, idx, sample_rows(w.rows, 3000, 7, extra=[w.rows - 1]), "topk one-wave")
     done()
 
 

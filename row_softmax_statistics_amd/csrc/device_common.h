@@ -28,6 +28,11 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     if (round > 0) {
       k0 += Philox::W0;
       k1 += Philox::W1;
+      // Each call steps its own copy of the key in scalar registers. Without
+      // the empty statement the compiler hoists all 18 round keys out of the
+      // calling loop and, short of scalar registers, keeps most of them in
+      // vector-register lanes, paying a vector read-lane per use.
+      __asm__ volatile("" : "+s"(k0), "+s"(k1));
     }
     const uint64_t p0 = (uint64_t)Philox::M0 * c0;
     const uint64_t p1 = (uint64_t)Philox::M1 * c2;
@@ -35,6 +40,42 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
     const uint32_t n1 = (uint32_t)p1;
     const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+    const uint32_t n3 = (uint32_t)p0;
+    c0 = n0;
+    c1 = n1;
+    c2 = n2;
+    c3 = n3;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+// The same generator with the keys of rounds 1..9 given in vector registers
+// (computed once per kernel): no scalar work per call.
+struct PhiloxRoundKeys {
+  uint32_t a[10], b[10];
+};
+__device__ __forceinline__ PhiloxRoundKeys philox_round_keys_v(uint32_t k0, uint32_t k1) {
+  PhiloxRoundKeys r;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t x = k0 + (uint32_t)i * Philox::W0, y = k1 + (uint32_t)i * Philox::W1;
+    __asm__("v_mov_b32 %0, %1" : "=v"(r.a[i]) : "s"(x));
+    __asm__("v_mov_b32 %0, %1" : "=v"(r.b[i]) : "s"(y));
+  }
+  return r;
+}
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1,
+                                               const PhiloxRoundKeys &rk) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t ka = round == 0 ? k0 : rk.a[round];
+    const uint32_t kb = round == 0 ? k1 : rk.b[round];
+    const uint64_t p0 = (uint64_t)Philox::M0 * c0;
+    const uint64_t p1 = (uint64_t)Philox::M1 * c2;
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, ka, 0x96);
+    const uint32_t n1 = (uint32_t)p1;
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, kb, 0x96);
     const uint32_t n3 = (uint32_t)p0;
     c0 = n0;
     c1 = n1;
@@ -83,6 +124,13 @@ __device__ __forceinline__ int32_t key64_col(int64_t k) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float max4(const float4 &a) {
   return fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+}
+// Largest of four values that are all >= 0 (no NaN): the order of such fp32
+// values is the order of their bit patterns.
+__device__ __forceinline__ float max4_nonneg(const float4 &a) {
+  const uint32_t m = max(max(__float_as_uint(a.x), __float_as_uint(a.y)),
+                         max(__float_as_uint(a.z), __float_as_uint(a.w)));
+  return __uint_as_float(m);
 }
 __device__ __forceinline__ float comp(const float4 &a, int i) {
   return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : a.w;

@@ -274,9 +274,10 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
 // v holds the exp values 2^32 exp(s - m) of the wave and every lane holds the
 // wave's summary (its best score exact when `exact` is set).
 // ---------------------------------------------------------------------------
-template <bool VEC>
+template <bool VEC, bool VKEYS>
 __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t row, int32_t chunk,
-                                              float4 (&v)[kQ], bool exact) {
+                                              float4 (&v)[kQ], bool exact,
+                                              const PhiloxRoundKeys &rk) {
   const int lane = lane_id();
   const int32_t V = p.vocab;
   const float T = load_uniform(p.temps + slot_of(p, row));
@@ -382,14 +383,24 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     // fl32(w) >= fl32(2^32 - 512 - e kc): fl32(w) is within 128 of w, the fma
     // rounds by at most 128 and kc covers the rounding of e and a, so every
     // such column passes (a few more may). Bit 31 - k of cm is element k.
+    // A quad first takes the test with its largest word and exp value: as
+    // rounding is monotone, a quad that fails it holds no passing column,
+    // and only the lanes of a quad that passes (rare) test its four columns.
     uint32_t cm = 0;
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
-      if (max4(v[j]) >= ethr) {
-        const uint4 w = philox4x32_10(qb + (uint32_t)(j * kWave), 0u, r0, r1, k0, k1);
+      const float ej = max4_nonneg(v[j]);
+      if (ej >= ethr) {
+        const uint4 w = VKEYS ? philox4x32_10(qb + (uint32_t)(j * kWave), 0u, r0, r1, k0, k1, rk)
+                              : philox4x32_10(qb + (uint32_t)(j * kWave), 0u, r0, r1, k0, k1);
+        const uint32_t wm = max(max(w.x, w.y), max(w.z, w.w));
+        if ((float)wm >= fmaf(-ej, kc, 4294966784.0f)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          cm = push_bit_ge(cm, (float)pick(w, i), fmaf(-comp(v[j], i), kc, 4294966784.0f));
+          for (int i = 0; i < 4; ++i)
+            cm = push_bit_ge(cm, (float)pick(w, i), fmaf(-comp(v[j], i), kc, 4294966784.0f));
+        } else {
+          cm <<= 4;
+        }
       } else {
         cm <<= 4;
       }
@@ -527,6 +538,10 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
   if (group >= p.n_groups || group >= p.rows) return;
   const int32_t chunk = member;
   const bool leader = member == 0;
+  // with probs, the Philox round keys live in vector registers (there are
+  // free ones there); without, each call steps them in scalar registers
+  const PhiloxRoundKeys rk =
+      philox_round_keys_v(PROBS ? (uint32_t)p.seed : 0u, PROBS ? (uint32_t)(p.seed >> 32) : 0u);
   RowDealer d;
   d.ring = p.rings + (int64_t)group * (kRingBytes / 8);
   d.counter = p.counters + (p.epoch & 1);
@@ -587,7 +602,7 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
     } else {
       chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
     }
-    const Tuple t = reduce_chunk<VEC>(p, row, chunk, cur, false);
+    const Tuple t = reduce_chunk<VEC, PROBS != 0>(p, row, chunk, cur, false, rk);
     // The empty statement consumes the loads issued before the copy on
     // every path, so the wait for them is placed here, exactly, and does not
     // wait for the copy.

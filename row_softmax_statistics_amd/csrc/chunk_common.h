@@ -140,12 +140,37 @@ __device__ __forceinline__ void lds_read_chunk(float4 (&v)[kQ], const float4 *bu
 }
 
 // cm = 2 cm + (a >= b): the compare writes VCC and the add takes it as the
-// carry in (the compiler would spend a select and a shift instead).
+// carry in (the compiler would spend a select and a shift instead). A carry
+// or mask read of a compare's result needs two wait states after the
+// compare on gfx950; the compiler adds them to its own code but not inside
+// inline assembly, hence the s_nop.
 __device__ __forceinline__ uint32_t push_bit_ge(uint32_t cm, float a, float b) {
-  __asm__("v_cmp_ge_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+  __asm__("v_cmp_ge_f32 vcc, %1, %2\n\ts_nop 1\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
           : "+v"(cm)
           : "v"(a), "v"(b)
           : "vcc");
+  return cm;
+}
+
+// Four such pushes (a0 first). The compares write VCC and two scalar
+// register pairs in turn, so that every add reads a result written at least
+// two instructions before it: no wait states are needed.
+__device__ __forceinline__ uint32_t push4_bits_ge(uint32_t cm, float a0, float a1, float a2,
+                                                  float a3, float b0, float b1, float b2,
+                                                  float b3) {
+  uint64_t sb, sc;
+  __asm__(
+      "v_cmp_ge_f32_e64 vcc, %3, %7\n\t"
+      "v_cmp_ge_f32_e64 %1, %4, %8\n\t"
+      "v_cmp_ge_f32_e64 %2, %5, %9\n\t"
+      "v_addc_co_u32_e64 %0, vcc, %0, %0, vcc\n\t"
+      "v_cmp_ge_f32_e64 vcc, %6, %10\n\t"
+      "v_addc_co_u32_e64 %0, %1, %0, %0, %1\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %2\n\t"
+      "v_addc_co_u32_e64 %0, vcc, %0, %0, vcc"
+      : "+v"(cm), "=&s"(sb), "=&s"(sc)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1), "v"(b2), "v"(b3)
+      : "vcc");
   return cm;
 }
 

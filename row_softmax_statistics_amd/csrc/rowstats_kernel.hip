@@ -395,9 +395,9 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
                               : philox4x32_10(qb + (uint32_t)(j * kWave), 0u, r0, r1, k0, k1);
         const uint32_t wm = max(max(w.x, w.y), max(w.z, w.w));
         if ((float)wm >= fmaf(-ej, kc, 4294966784.0f)) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            cm = push_bit_ge(cm, (float)pick(w, i), fmaf(-comp(v[j], i), kc, 4294966784.0f));
+          cm = push4_bits_ge(cm, (float)w.x, (float)w.y, (float)w.z, (float)w.w,
+                             fmaf(-v[j].x, kc, 4294966784.0f), fmaf(-v[j].y, kc, 4294966784.0f),
+                             fmaf(-v[j].z, kc, 4294966784.0f), fmaf(-v[j].w, kc, 4294966784.0f));
         } else {
           cm <<= 4;
         }

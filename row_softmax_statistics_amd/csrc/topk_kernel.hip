@@ -247,9 +247,7 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, 
   // columns (masked ones are -inf).
   uint32_t cm = 0;
 #pragma unroll
-  for (int j = 0; j < kQ; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cm = push_bit_ge(cm, comp(v[j], i), vk);
+  for (int j = 0; j < kQ; ++j) cm = push4_bits_ge(cm, v[j].x, v[j].y, v[j].z, v[j].w, vk, vk, vk, vk);
   int total;
   const int off = wave_prefix(__popc(cm), total);
 

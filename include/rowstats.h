@@ -31,14 +31,15 @@ typedef enum rowstats_status {
   ROWSTATS_ERR_SHAPE = -2,  /* rows < 0, or (rows > 0 and: rows > 2^31 - 1,
                                vocab < 1, vocab > 2^31 - 1 - 65536,
                                row_stride < vocab, canvas_len < 1) */
-  ROWSTATS_ERR_K = -3,      /* K < 1, K > vocab or K > 64 */
+  ROWSTATS_ERR_K = -3,      /* K < 1 (num_topk < 0), K > vocab or K > 64 */
   ROWSTATS_ERR_DTYPE = -4,  /* probs_dtype is not one of rowstats_probs_dtype */
   ROWSTATS_ERR_HIP = -5,    /* a HIP call failed (allocation, launch); see last_error */
   ROWSTATS_ERR_COOP = -6,   /* rowstats_run keeps the ceil(vocab / 2048) chunks of a
                                row in co-resident waves at once and the device
                                cannot hold them (vocab above about 4.2 million on
                                one MI355X) */
-  ROWSTATS_ERR_DEVICE = -7  /* a kernel flagged a failure (a bounded wait ran out);
+  ROWSTATS_ERR_DEVICE = -7  /* a kernel flagged a failure (a bounded wait ran out,
+                               or a stash index argument was out of range);
                                reported by rowstats_check_device */
 } rowstats_status;
 
@@ -109,14 +110,75 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows,
                   const uint8_t *keep_mask, int32_t K, float *out_vals,
                   int64_t *out_idx, void *stream);
 
+/*
+ * The converged-logprob stash: for the rows of the kept requests, one stash
+ * row each of the argmax, then the request's token ids or the num_topk
+ * largest, then padding.
+ * Defined by: diffusion_gemma_sampler page, stash_converged_logprobs
+ * (docstring: request j owns rows src[j] * canvas_len + p for p < valid[j],
+ * divided by temps[j]; kept requests go to out_*[slots[j], p], laid out as
+ * the argmax, then the request's token ids if it has any, else the num_topk
+ * largest with ties to the lower id, padded with token 0 at -inf; requests
+ * not kept are skipped; launcher: num_topk + 1 <= width) and the
+ * _lp_topk_kernel docstring (the key order). Where the page shows no body
+ * this library reads it as stated below.
+ *
+ *   logits, row_stride, vocab  as for rowstats_run; logits_rows = rows of
+ *               the matrix (>= 1).
+ *   canvas_len  positions per request, >= 1; m * canvas_len <= 2^31 - 1.
+ *   m           requests; m == 0 returns at once.
+ *   src, slots, valid  int32 [m]. Request j with keep[j] != 0 owns the rows
+ *               src[j] * canvas_len + p for 0 <= p < min(valid[j], canvas_len)
+ *               (valid[j] <= 0: none); they go to stash slot slots[j],
+ *               position p. A kept request with a row outside
+ *               [0, logits_rows) or a slot outside [0, stash_slots) is
+ *               skipped and flagged (rowstats_check_device).
+ *   keep        uint8 [m]: nonzero = converged, written.
+ *   temps       fp32 [m]: s = x / max(temps[j], 1e-10f) (IEEE fp32 division;
+ *               T <= 0 uses 1e-10 as in rowstats_run's entropy).
+ *   num_topk    0 <= num_topk <= min(vocab, 64).
+ *   num_token_ids, token_ids, token_ids_stride  NULL token_ids: no request
+ *               has ids. Otherwise int32 num_token_ids [m] and token_ids
+ *               [m, token_ids_stride] (row j at token_ids + j * stride):
+ *               request j lists min(num_token_ids[j], stash_width - 1,
+ *               token_ids_stride) ids when num_token_ids[j] > 0, else its
+ *               num_topk largest. An id outside [0, vocab) is written as given
+ *               with value -inf and flagged.
+ *   stash_slots, stash_positions, stash_width  stash shape:
+ *               stash_positions >= canvas_len, stash_width >= num_topk + 1.
+ *   out_ids     int32 [stash_slots, stash_positions, stash_width] contiguous.
+ *               Column 0: the argmax (lowest column attaining max s); then
+ *               the ids, or the num_topk largest in descending key order
+ *               (value, then lower column); the rest 0.
+ *   out_logprobs fp32, same shape: s - log Z at each listed column (log Z =
+ *               log sum_c exp(s_c)); with logits_mode != 0 the scaled logit s
+ *               itself; -inf on padding.
+ *   out_ranks   int32 [stash_slots, stash_positions]: the number of columns
+ *               whose s is at least the argmax's (1 unless the maximum ties).
+ *   Cells of requests not kept, and positions at or past valid[j], are not
+ *   written.
+ */
+int stash_converged_logprobs(const float *logits, int64_t row_stride,
+                             int64_t logits_rows, int64_t vocab,
+                             int64_t canvas_len, int64_t m, const int32_t *src,
+                             const int32_t *slots, const uint8_t *keep,
+                             const int32_t *valid, const float *temps,
+                             int32_t num_topk, const int32_t *num_token_ids,
+                             const int32_t *token_ids, int64_t token_ids_stride,
+                             int64_t stash_slots, int64_t stash_positions,
+                             int32_t stash_width, int32_t *out_ids,
+                             float *out_logprobs, int32_t *out_ranks,
+                             int logits_mode, void *stream);
+
 /* Text of the calling thread's last failure ("" if none). */
 const char *rowstats_last_error(void);
 
 /*
  * Synchronises `stream` and reports ROWSTATS_ERR_DEVICE if any kernel of
  * this library flagged a failure on the current device since the last
- * check (a bounded inter-workgroup wait that ran out; the outputs of that
- * call are then undefined). Clears the flag.
+ * check: a bounded inter-workgroup wait that ran out (the outputs of that
+ * call are then undefined), or a stash request or token id out of range
+ * (that request or id was skipped, the rest is written). Clears the flag.
  */
 int rowstats_check_device(void *stream);
 

@@ -36,6 +36,12 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p]),
+    "stash_converged_logprobs": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
     "rowstats_last_error": (ctypes.c_char_p, []),
     "rowstats_check_device": (ctypes.c_int, [ctypes.c_void_p]),
     "rowstats_release": (ctypes.c_int, []),
@@ -155,6 +161,69 @@ def topk_logprobs(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int,
         canvas_len, _ptr(keep_mask), int(K), _ptr(out_vals), _ptr(out_idx), _stream_ptr(dev))
     _check(rc, "topk_logprobs")
     return out_vals, out_idx
+
+
+def _gpu_vec(t: torch.Tensor, dtype, name: str, m: int):
+    if t.dtype != dtype or not t.is_cuda or t.dim() != 1 or t.numel() < m:
+        raise ValueError(f"{name} must be a 1-D {dtype} GPU tensor of at least {m} entries")
+    return t.contiguous()
+
+
+def stash_converged_logprobs(logits: torch.Tensor, canvas_len: int, src: torch.Tensor,
+                             slots: torch.Tensor, keep: torch.Tensor, valid: torch.Tensor,
+                             temps: torch.Tensor, num_topk: int,
+                             num_token_ids: torch.Tensor | None,
+                             token_ids: torch.Tensor | None, out_ids: torch.Tensor,
+                             out_logprobs: torch.Tensor, out_ranks: torch.Tensor,
+                             logits_mode: bool) -> None:
+    """Write the stash rows of the kept requests (arguments as on the page).
+
+    Request ``j`` owns logits rows ``src[j] * canvas_len + p`` for
+    ``p < valid[j]``, divided by ``temps[j]``; where ``keep[j]`` they go to
+    ``out_*[slots[j], p]``: the argmax, then the request's token ids if it
+    has any (``num_token_ids[j] > 0``), else the ``num_topk`` largest, padded
+    with token 0 at -inf. ``src``, ``slots``, ``valid``, ``num_token_ids``,
+    ``token_ids``, ``out_ids`` and ``out_ranks`` are int32; ``out_ids`` and
+    ``out_logprobs`` are ``[slots, positions, width]``, ``out_ranks``
+    ``[slots, positions]``, all contiguous.
+    """
+    _check_logits(logits)
+    m = int(slots.numel())
+    src = _gpu_vec(src, torch.int32, "src", m)
+    slots = _gpu_vec(slots, torch.int32, "slots", m)
+    valid = _gpu_vec(valid, torch.int32, "valid", m)
+    temps = _gpu_vec(temps, torch.float32, "temps", m)
+    if keep.dtype not in (torch.uint8, torch.bool) or not keep.is_cuda or keep.numel() < m:
+        raise ValueError("keep must be a uint8/bool GPU tensor of m entries")
+    keep = keep.contiguous()
+    ids_stride = 0
+    if token_ids is not None:
+        num_token_ids = _gpu_vec(num_token_ids, torch.int32, "num_token_ids", m)
+        if token_ids.dtype != torch.int32 or not token_ids.is_cuda or token_ids.dim() != 2:
+            raise ValueError("token_ids must be a 2-D int32 GPU tensor")
+        if token_ids.stride(1) != 1:
+            token_ids = token_ids.contiguous()
+        ids_stride = token_ids.stride(0) if token_ids.shape[0] > 1 else token_ids.shape[1]
+    if out_logprobs.dim() != 3 or out_ids.shape != out_logprobs.shape:
+        raise ValueError("out_ids and out_logprobs must be [slots, positions, width]")
+    if out_ranks.shape != out_logprobs.shape[:2]:
+        raise ValueError("out_ranks must be [slots, positions]")
+    if (out_ids.dtype != torch.int32 or out_logprobs.dtype != torch.float32
+            or out_ranks.dtype != torch.int32):
+        raise ValueError("out_ids / out_ranks must be int32 and out_logprobs float32")
+    if not (out_ids.is_contiguous() and out_logprobs.is_contiguous()
+            and out_ranks.is_contiguous()):
+        raise ValueError("stash outputs must be contiguous")
+    rows, vocab = logits.shape
+    n_slots, positions, width = out_logprobs.shape
+    dev = logits.device
+    rc = lib().stash_converged_logprobs(
+        _ptr(logits), logits.stride(0) if rows > 1 else vocab, rows, vocab, canvas_len, m,
+        _ptr(src), _ptr(slots), _ptr(keep), _ptr(valid), _ptr(temps), int(num_topk),
+        _ptr(num_token_ids if token_ids is not None else None), _ptr(token_ids), ids_stride,
+        n_slots, positions, width, _ptr(out_ids), _ptr(out_logprobs), _ptr(out_ranks),
+        1 if logits_mode else 0, _stream_ptr(dev))
+    _check(rc, "stash_converged_logprobs")
 
 
 def check_device(stream=None):

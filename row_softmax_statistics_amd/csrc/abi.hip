@@ -152,6 +152,57 @@ int check_common(const float *logits, int64_t row_stride, int64_t rows, int64_t 
   return ROWSTATS_OK;
 }
 
+// Groups, scratch layout and launch of the top-K kernel (both entry
+// points); p.rows is the most rows the call can keep.
+int plan_and_launch_topk(DeviceState &d, TopKParams &p, hipStream_t s) {
+  // As for rowstats_run: every wave resident, a row's C member waves at once.
+  constexpr int kWavesPerBlock = kRowThreads / 64;
+  const int64_t rows = p.rows;
+  const int64_t waves = (int64_t)d.topk_resident[p.vec_ok] * d.cus * kWavesPerBlock;
+  if (waves < 1) return fail(ROWSTATS_ERR_HIP, "top-K kernel cannot be resident");
+  if (p.C > waves || p.C > 64 * 64)
+    return fail(ROWSTATS_ERR_COOP,
+                "vocab %d needs %d co-resident waves per row, the device holds %lld", p.vocab,
+                p.C, (long long)waves);
+  int64_t groups = waves / p.C;
+  if (groups > rows) groups = rows;
+  p.n_groups = (int32_t)groups;
+  const int64_t grid = (groups * p.C + kWavesPerBlock - 1) / kWavesPerBlock;
+
+  // records and row results are indexed by kept position (at most rows)
+  auto align16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
+  const size_t head_bytes = kScratchHead + (size_t)groups * kRingBytes;
+  const size_t record_bytes = (size_t)rows * p.C * topk_record_bytes(p.K);
+  const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
+  const size_t temp_bytes = align16((size_t)rows * sizeof(float));
+  const size_t kept_bytes = align16(((size_t)rows + 1) * sizeof(int64_t));
+  const size_t dst_bytes = p.stash ? (size_t)rows * sizeof(int64_t) : 0;
+  const size_t req_bytes = p.stash ? align16((size_t)rows * sizeof(int32_t)) : 0;
+  int rc = ensure_row_scratch(d, head_bytes + record_bytes + rowres_bytes + temp_bytes +
+                                     kept_bytes + dst_bytes + req_bytes, s);
+  if (rc) return rc;
+  if ((rc = next_epoch(d, s, &p.epoch))) return rc;
+  char *base = reinterpret_cast<char *>(d.row_scratch);
+  p.counters = reinterpret_cast<uint32_t *>(base);
+  p.rings = reinterpret_cast<uint64_t *>(base + kScratchHead);
+  base += head_bytes;
+  p.records = reinterpret_cast<uint64_t *>(base);
+  base += record_bytes;
+  p.rowres = reinterpret_cast<uint64_t *>(base);
+  base += rowres_bytes;
+  p.kept_temp = reinterpret_cast<float *>(base);
+  base += temp_bytes;
+  p.kept = reinterpret_cast<int64_t *>(base);
+  base += kept_bytes;
+  p.kept_dst = p.stash ? reinterpret_cast<int64_t *>(base) : nullptr;
+  base += dst_bytes;
+  p.kept_req = p.stash ? reinterpret_cast<int32_t *>(base) : nullptr;
+  p.err_flag = d.err_flag;
+  hipError_t e = topk_launch(p, (int)grid, s);
+  if (e != hipSuccess) return fail_hip(e, "top-K kernel launch");
+  return ROWSTATS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -260,40 +311,86 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   p.out_vals = out_vals;
   p.out_idx = out_idx;
 
-  // As for rowstats_run: every wave resident, a row's C member waves at once.
-  constexpr int kWavesPerBlock = kRowThreads / 64;
-  const int64_t waves = (int64_t)d->topk_resident[p.vec_ok] * d->cus * kWavesPerBlock;
-  if (waves < 1) return fail(ROWSTATS_ERR_HIP, "top-K kernel cannot be resident");
-  if (p.C > waves || p.C > 64 * 64)
-    return fail(ROWSTATS_ERR_COOP,
-                "vocab %lld needs %d co-resident waves per row, the device holds %lld",
-                (long long)vocab, p.C, (long long)waves);
-  int64_t groups = waves / p.C;
-  if (groups > rows) groups = rows;
-  p.n_groups = (int32_t)groups;
-  const int64_t grid = (groups * p.C + kWavesPerBlock - 1) / kWavesPerBlock;
+  return plan_and_launch_topk(*d, p, s);
+}
 
-  // records and row results are indexed by kept position (at most rows)
-  const size_t head_bytes = kScratchHead + (size_t)groups * kRingBytes;
-  const size_t record_bytes = (size_t)rows * p.C * topk_record_bytes(K);
-  const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
-  const size_t kept_bytes = ((size_t)rows + 1) * sizeof(int64_t);
-  const size_t temp_bytes = ((size_t)rows * sizeof(float) + 15) & ~(size_t)15;
-  if ((rc = ensure_row_scratch(*d, head_bytes + record_bytes + rowres_bytes + kept_bytes + temp_bytes, s)))
-    return rc;
-  if ((rc = next_epoch(*d, s, &p.epoch))) return rc;
-  char *base = reinterpret_cast<char *>(d->row_scratch);
-  p.counters = reinterpret_cast<uint32_t *>(base);
-  p.rings = reinterpret_cast<uint64_t *>(base + kScratchHead);
-  base += head_bytes;
-  p.records = reinterpret_cast<uint64_t *>(base);
-  p.rowres = reinterpret_cast<uint64_t *>(base + record_bytes);
-  p.kept_temp = reinterpret_cast<float *>(base + record_bytes + rowres_bytes);
-  p.kept = reinterpret_cast<int64_t *>(base + record_bytes + rowres_bytes + temp_bytes);
-  p.err_flag = d->err_flag;
-  hipError_t e = topk_launch(p, (int)grid, s);
-  if (e != hipSuccess) return fail_hip(e, "top-K kernel launch");
-  return ROWSTATS_OK;
+int stash_converged_logprobs(const float *logits, int64_t row_stride, int64_t logits_rows,
+                             int64_t vocab, int64_t canvas_len, int64_t m, const int32_t *src,
+                             const int32_t *slots, const uint8_t *keep, const int32_t *valid,
+                             const float *temps, int32_t num_topk, const int32_t *num_token_ids,
+                             const int32_t *token_ids, int64_t token_ids_stride,
+                             int64_t stash_slots, int64_t stash_positions, int32_t stash_width,
+                             int32_t *out_ids, float *out_logprobs, int32_t *out_ranks,
+                             int logits_mode, void *stream) {
+  g_last_error.clear();
+  if (m < 0) return fail(ROWSTATS_ERR_SHAPE, "m must be >= 0, got %lld", (long long)m);
+  if (m == 0) return ROWSTATS_OK;
+  if (logits_rows < 1)
+    return fail(ROWSTATS_ERR_SHAPE, "logits_rows must be >= 1, got %lld", (long long)logits_rows);
+  int rc = check_common(logits, row_stride, logits_rows, vocab, temps, canvas_len);
+  if (rc) return rc;
+  if (canvas_len > 0x7FFFFFFFLL / m)
+    return fail(ROWSTATS_ERR_SHAPE, "m * canvas_len must be <= 2^31 - 1, got %lld * %lld",
+                (long long)m, (long long)canvas_len);
+  if (num_topk < 0 || (int64_t)num_topk > vocab || num_topk > kTopKMax)
+    return fail(ROWSTATS_ERR_K, "num_topk must be in [0, min(vocab=%lld, %d)], got %d",
+                (long long)vocab, kTopKMax, num_topk);
+  if ((int64_t)stash_width < (int64_t)num_topk + 1)
+    return fail(ROWSTATS_ERR_SHAPE, "stash_width %d < num_topk + 1 = %d", stash_width,
+                num_topk + 1);
+  if (stash_slots < 1)
+    return fail(ROWSTATS_ERR_SHAPE, "stash_slots must be >= 1, got %lld", (long long)stash_slots);
+  if (stash_positions < canvas_len)
+    return fail(ROWSTATS_ERR_SHAPE, "stash_positions %lld < canvas_len %lld",
+                (long long)stash_positions, (long long)canvas_len);
+  if (!src || !slots || !keep || !valid)
+    return fail(ROWSTATS_ERR_NULL, "src, slots, keep or valid is NULL");
+  if (!out_ids || !out_logprobs || !out_ranks)
+    return fail(ROWSTATS_ERR_NULL, "an output pointer is NULL");
+  if (token_ids) {
+    if (!num_token_ids) return fail(ROWSTATS_ERR_NULL, "token_ids given without num_token_ids");
+    if (token_ids_stride < 1)
+      return fail(ROWSTATS_ERR_SHAPE, "token_ids_stride must be >= 1, got %lld",
+                  (long long)token_ids_stride);
+  }
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState *d = nullptr;
+  if ((rc = device_state(&d))) return rc;
+
+  TopKParams p = {};
+  p.logits = logits;
+  p.ld = row_stride;
+  p.rows = m * canvas_len;  // most rows the kept requests can own
+  p.vocab = (int32_t)vocab;
+  p.C = (int32_t)((vocab + kChunkCols - 1) / kChunkCols);
+  p.vec_ok = ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) && (row_stride % 4 == 0) &&
+             (vocab % 4 == 0);
+  // two keys at least, so that the ties at the maximum are known without a
+  // recount unless the two largest tie
+  p.K = (int32_t)(vocab < 2 ? vocab : (num_topk < 2 ? 2 : num_topk));
+  p.temps = temps;
+  p.canvas_len = canvas_len;
+  p.keep = keep;
+  p.stash = 1;
+  p.K_out = num_topk;
+  p.logits_mode = logits_mode != 0;
+  p.width = stash_width;
+  p.m = m;
+  p.logits_rows = logits_rows;
+  p.stash_slots = stash_slots;
+  p.positions = stash_positions;
+  p.src = src;
+  p.slots = slots;
+  p.valid = valid;
+  p.num_ids = token_ids ? num_token_ids : nullptr;
+  p.ids = token_ids;
+  p.ids_stride = token_ids ? token_ids_stride : 0;
+  p.out_ids32 = out_ids;
+  p.out_lp = out_logprobs;
+  p.out_ranks = out_ranks;
+  return plan_and_launch_topk(*d, p, s);
 }
 
 int rowstats_check_device(void *stream) {
@@ -311,7 +408,9 @@ int rowstats_check_device(void *stream) {
   if (flag == 0) return ROWSTATS_OK;
   e = hipMemset(d->err_flag, 0, sizeof(uint32_t));
   if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
-  return fail(ROWSTATS_ERR_DEVICE, "a kernel flagged an inter-workgroup wait that ran out (flag %u)",
+  return fail(ROWSTATS_ERR_DEVICE, "a kernel flagged %s (flag %u)",
+              (flag & kErrWait) ? "an inter-workgroup wait that ran out"
+                                : "a stash index out of range (request or token id skipped)",
               flag);
 }
 

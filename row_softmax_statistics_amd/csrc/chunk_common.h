@@ -215,9 +215,10 @@ __device__ __forceinline__ bool row_result_ready(const u32x4 &v, uint32_t epoch)
   return ((v[1] == epoch) & (v[3] == epoch)) != 0;
 }
 
-// Whether some wait of this call has already given up.
+// Whether some wait of this call has already given up (bit 0 of the error
+// flag; other bits report bad arguments and do not stop the waits).
 __device__ __forceinline__ bool call_failed(const uint32_t *err_flag) {
-  return __hip_atomic_load(err_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+  return (__hip_atomic_load(err_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u) != 0u;
 }
 
 // Waits until the row result of `row` (pre-loaded in v) shows `epoch`;

@@ -389,6 +389,7 @@ struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf
 struct MinI { __device__ int32_t operator()(int32_t a, int32_t b) const { return a < b ? a : b; } };
 struct SumF { __device__ float operator()(float a, float b) const { return a + b; } };
 struct SumD { __device__ double operator()(double a, double b) const { return a + b; } };
+struct SumI { __device__ int32_t operator()(int32_t a, int32_t b) const { return a + b; } };
 struct MaxD { __device__ double operator()(double a, double b) const { return fmax(a, b); } };
 struct MaxI64 { __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; } };
 

@@ -39,7 +39,35 @@ struct TopKParams {
   uint32_t *counters; // two row-claim counters: a call uses counters[epoch & 1]
                       // (the pre-pass zeroes both)
   uint32_t *err_flag;
+
+  // Stash mode (stash != 0): rows come from requests instead of slots and
+  // each kept row is written as one stash row.
+  int32_t stash;
+  int32_t K_out;         // top-K columns of a stash row (K above is max(K_out, 2), capped at vocab)
+  int32_t logits_mode;   // write s instead of s - log Z
+  int32_t width;         // stash row width, >= K_out + 1
+  int64_t m;             // requests
+  int64_t logits_rows;   // rows of the logits matrix
+  int64_t stash_slots;   // first dimension of the stash
+  int64_t positions;     // second dimension of the stash (>= canvas_len)
+  const int32_t *src;    // [m] canvas of request j
+  const int32_t *slots;  // [m] stash slot of request j
+  const int32_t *valid;  // [m] positions of request j
+  const int32_t *num_ids;  // [m] token ids of request j (null: none)
+  const int32_t *ids;      // [m, ids_stride]
+  int64_t ids_stride;
+  int32_t *out_ids32;    // [stash_slots, positions, width]
+  float *out_lp;         // [stash_slots, positions, width]
+  int32_t *out_ranks;    // [stash_slots, positions]
+  int64_t *kept_dst;     // [rows]: stash row slots[j] * positions + p of kept row i
+  int32_t *kept_req;     // [rows]: request j of kept row i
 };
+
+// Bits of the error flag: a bounded wait ran out (the call's waits then give
+// up), and an index argument of the stash was out of range (that request or
+// token id is skipped).
+constexpr uint32_t kErrWait = 1u;
+constexpr uint32_t kErrIndex = 2u;
 
 hipError_t topk_resident_blocks(bool vec, int *blocks_per_cu);
 // Queues the kept-row pre-pass and the top-K kernel (cooperative) on `stream`.

@@ -303,6 +303,79 @@ __device__ __forceinline__ void publish_record(const TopKParams &p, int64_t pos,
   }
 }
 
+__device__ __forceinline__ int64_t load_uniform_i64(const int64_t *p) {
+  return *(const __attribute__((address_space(4))) int64_t *)p;
+}
+__device__ __forceinline__ int32_t load_uniform_i32(const int32_t *p) {
+  return *(const __attribute__((address_space(4))) int32_t *)p;
+}
+
+// Columns of the row whose scaled value reaches M (its maximum): one pass
+// over the row by the merger, for rows whose K largest keys all tie at M.
+__device__ __forceinline__ int count_at_max(const TopKParams &p, int64_t row, float T, float M) {
+  const double rtc = 1.0 / (double)clamp_temp(T);
+  const float *x = p.logits + row * p.ld;
+  int cnt = 0;
+  for (int32_t c = lane_here(); c < p.vocab; c += kWave) cnt += scale(x[c], rtc) >= M ? 1 : 0;
+  return wave_allreduce(cnt, SumI());
+}
+
+// One stash row: the argmax, then the request's token ids or the K_out
+// largest keys, then token 0 at -inf up to the width; and the argmax's rank
+// (the columns at or above its value). buf holds the row's K largest keys
+// in rank order, M its maximum and logS = log sum exp(s - M).
+__device__ __forceinline__ void write_stash_row(const TopKParams &p, int64_t pos, int64_t row,
+                                             const int64_t *buf, float M, double logS) {
+  const int lane = lane_here();
+  const int K = p.K;
+  const float T = load_uniform(p.kept_temp + pos);
+  const int64_t dst = load_uniform_i64(p.kept_dst + pos);
+  const int32_t j = load_uniform_i32(p.kept_req + pos);
+  const int32_t W = p.width;
+  int32_t *oid = p.out_ids32 + dst * W;
+  float *olp = p.out_lp + dst * W;
+  auto value = [&](float s) -> float {
+    return p.logits_mode ? s : (float)(((double)s - (double)M) - logS);
+  };
+  // ties at the maximum among the K keys; when all K tie, count the row
+  const int64_t mine = lane < K ? buf[lane] : INT64_MIN;
+  int ties = __popcll(__ballot(lane < K && (int32_t)(mine >> 32) == key32(M)));
+  if (ties == K) ties = count_at_max(p, row, T, M);
+  int n = p.K_out;
+  bool by_ids = false;
+  if (p.ids != nullptr) {
+    const int32_t c = load_uniform_i32(p.num_ids + j);
+    if (c > 0) {
+      by_ids = true;
+      n = (int)min((int64_t)min(c, W - 1), p.ids_stride);
+    }
+  }
+  if (lane == 0) {
+    oid[0] = key64_col(buf[0]);
+    olp[0] = value(key32_value((int32_t)(buf[0] >> 32)));
+    p.out_ranks[dst] = ties;
+  }
+  if (by_ids) {
+    const double rtc = 1.0 / (double)clamp_temp(T);
+    const int32_t *idr = p.ids + (int64_t)j * p.ids_stride;
+    for (int i = lane; i < n; i += kWave) {
+      const int32_t id = idr[i];
+      float v = -INFINITY;
+      if (id >= 0 && id < p.vocab) v = value(scale(p.logits[row * p.ld + id], rtc));
+      else atomicOr(p.err_flag, kErrIndex);
+      oid[1 + i] = id;
+      olp[1 + i] = v;
+    }
+  } else if (lane < n) {
+    oid[1 + lane] = key64_col(mine);
+    olp[1 + lane] = value(key32_value((int32_t)(mine >> 32)));
+  }
+  for (int c = 1 + n + lane; c < W; c += kWave) {
+    oid[c] = 0;
+    olp[c] = -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The merger's work for the kept row at position pos (row index `row`).
 // buf is the wave's LDS list area: the running top-K in [0, K), the keys
@@ -484,7 +557,9 @@ __device__ void merge_row_topk(const TopKParams &p, int64_t pos, int64_t row, in
   }
   flush();
 
-  if (lane < K) {
+  if (p.stash) {
+    write_stash_row(p, pos, row, buf, M, logS);
+  } else if (lane < K) {
     const int64_t key = buf[lane];
     const float s = key32_value((int32_t)(key >> 32));
     p.out_idx[row * K + lane] = key64_col(key);
@@ -492,10 +567,6 @@ __device__ void merge_row_topk(const TopKParams &p, int64_t pos, int64_t row, in
   }
   wave_lds_order();
   if (lane == 0) store_row_result(p.rowres, pos, __float_as_uint(M), 0u, p.epoch);
-}
-
-__device__ __forceinline__ int64_t load_uniform_i64(const int64_t *p) {
-  return *(const __attribute__((address_space(4))) int64_t *)p;
 }
 
 // ---------------------------------------------------------------------------
@@ -674,6 +745,68 @@ __global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kept-row list of the stash: each kept request j, in order, contributes
+// the rows src[j] * canvas_len + q for q < min(valid[j], canvas_len), with
+// kept_temp = temps[j], kept_dst = slots[j] * positions + q and kept_req = j;
+// kept[rows] = the count. A kept request whose rows fall outside the logits
+// or whose slot falls outside the stash is skipped and flags kErrIndex.
+// Also zeroes the row-claim counters. One workgroup; thread t handles a
+// contiguous range of requests.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kListThreads) void stash_rows_kernel(TopKParams p) {
+  __shared__ int64_t wave_tot[kListThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int64_t per = (p.m + kListThreads - 1) / kListThreads;
+  const int64_t j0 = min(p.m, (int64_t)tid * per), j1 = min(p.m, j0 + per);
+  // rows of request j; -1 for a kept request with an index out of range
+  auto rows_of = [&](int64_t j) -> int64_t {
+    if (!p.keep[j]) return 0;
+    const int64_t n = min((int64_t)max(p.valid[j], 0), p.canvas_len);
+    if (n == 0) return 0;
+    const int64_t src = p.src[j], slot = p.slots[j];
+    if (src < 0 || src * p.canvas_len + n > p.logits_rows || slot < 0 || slot >= p.stash_slots)
+      return -1;
+    return n;
+  };
+  int64_t cnt = 0;
+  for (int64_t j = j0; j < j1; ++j) {
+    const int64_t n = rows_of(j);
+    if (n > 0) cnt += n;
+    else if (n < 0) atomicOr(p.err_flag, kErrIndex);
+  }
+  // exclusive prefix over the workgroup
+  int64_t incl = cnt;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int64_t o = __shfl_up(incl, (unsigned)d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int64_t off = incl - cnt;
+  for (int w = 0; w < wave; ++w) off += wave_tot[w];
+  for (int64_t j = j0; j < j1; ++j) {
+    const int64_t n = rows_of(j);
+    if (n <= 0) continue;
+    const int64_t row0 = (int64_t)p.src[j] * p.canvas_len;
+    const int64_t dst0 = (int64_t)p.slots[j] * p.positions;
+    const float T = p.temps[j];
+    for (int64_t q = 0; q < n; ++q, ++off) {
+      p.kept[off] = row0 + q;
+      p.kept_temp[off] = T;
+      p.kept_dst[off] = dst0 + q;
+      p.kept_req[off] = (int32_t)j;
+    }
+  }
+  if (tid == kListThreads - 1) {
+    p.kept[p.rows] = off;
+    p.counters[0] = 0u;
+    p.counters[1] = 0u;
+  }
+}
+
 }  // namespace
 
 static const void *topk_kernel_ptr(bool vec) {
@@ -687,8 +820,11 @@ hipError_t topk_resident_blocks(bool vec, int *blocks_per_cu) {
 }
 
 hipError_t topk_launch(const TopKParams &p, int grid, hipStream_t stream) {
-  kept_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(
-      p.keep, p.temps, p.rows, p.canvas_len, p.kept, p.kept_temp, p.counters);
+  if (p.stash)
+    stash_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(p);
+  else
+    kept_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(
+        p.keep, p.temps, p.rows, p.canvas_len, p.kept, p.kept_temp, p.counters);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   TopKParams arg = p;

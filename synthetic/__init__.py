@@ -23,6 +23,11 @@ Workloads (rows x vocab, distribution, temperatures):
       over a random permutation), 8 slots at T = 0 and 24 at U(0, 1.5],
       bf16 probs, data seed 5.
 
+  S4  the stash over C4's logits: 16 requests (one per canvas of 256) with a
+      permuted src, slots spread over a stash of 24, C4's kept half, valid
+      200, 17 and 1 on three kept requests, two kept requests listing 5 and
+      20 token ids, K = 20, width 24.
+
 Every generator takes ``rows`` / ``vocab`` overrides so that the same recipe
 runs at sizes a CPU oracle finishes in seconds.
 """
@@ -291,6 +296,101 @@ def random_case(device="cpu", rows=8, vocab=100, canvas_len=3, seed=0, std=2.0,
     tc = torch.tensor(t_choices, dtype=torch.float32)
     temps = tc[torch.randint(0, len(tc), (slots,), generator=gc)]
     return Workload(f"random{seed}", x, temps.to(device), canvas_len, 777 + seed, probs_dtype)
+
+
+@dataclass
+class StashWorkload:
+    """Arguments of one converged-logprob stash call (outputs excluded)."""
+    name: str
+    logits: torch.Tensor      # [canvases * canvas_len, vocab] fp32
+    canvas_len: int
+    src: torch.Tensor         # int32 [m]
+    slots: torch.Tensor       # int32 [m], distinct
+    keep: torch.Tensor        # uint8 [m]
+    valid: torch.Tensor       # int32 [m]
+    temps: torch.Tensor       # fp32 [m]
+    K: int
+    num_ids: torch.Tensor     # int32 [m]
+    ids: torch.Tensor | None  # int32 [m, ids_stride]
+    n_slots: int
+    positions: int
+    width: int
+    logits_mode: bool = False
+
+    @property
+    def m(self) -> int:
+        return self.slots.numel()
+
+    @property
+    def vocab(self) -> int:
+        return self.logits.shape[1]
+
+
+def stash_case(device="cpu", m=6, canvas_len=4, vocab=1000, K=5, seed=0, std=2.0, ld=None,
+               with_ids=True, ties=False, width_pad=3, logits_mode=False,
+               t_choices=(0.0, 0.5, 1.0, 1.3)) -> StashWorkload:
+    """Small stash call: more canvases than requests, a permuted src, slots
+    spread over a larger stash, valid counts from -1 to past the canvas,
+    about two thirds of the requests kept, and (with_ids) some requests
+    listing token ids, one of them out of order and repeated."""
+    g = _gen(3000 + seed, device)
+    gc = _gen(4000 + seed, "cpu")
+    canvases = m + 2
+    ld = vocab if ld is None else ld
+    x = _alloc(canvases * canvas_len, vocab, ld, device)
+    _fill_normal(x, std, g)
+    if ties:
+        x.copy_(torch.round(x * 2.0) / 2.0)
+    src = torch.randperm(canvases, generator=gc)[:m].to(torch.int32)
+    n_slots = m + 3
+    slots = torch.randperm(n_slots, generator=gc)[:m].to(torch.int32)
+    keep = (torch.rand(m, generator=gc) < 0.67).to(torch.uint8)
+    keep[0] = 1
+    valid = torch.randint(-1, canvas_len + 2, (m,), generator=gc, dtype=torch.int32)
+    valid[0] = canvas_len
+    tc = torch.tensor(t_choices, dtype=torch.float32)
+    temps = tc[torch.randint(0, len(tc), (m,), generator=gc)]
+    width = K + 1 + width_pad
+    ids_stride = width + 2
+    num_ids = torch.zeros(m, dtype=torch.int32)
+    ids = None
+    if with_ids:
+        ids = torch.randint(0, vocab, (m, ids_stride), generator=gc, dtype=torch.int32)
+        ids[:, 1] = ids[:, 0]  # a repeated id
+        num_ids = torch.randint(0, ids_stride + 2, (m,), generator=gc, dtype=torch.int32)
+        num_ids[torch.arange(m) % 2 == 0] = 0  # half the requests take the top-K
+        ids = ids.to(device)
+    return StashWorkload(f"stash{seed}", x, canvas_len, src.to(device), slots.to(device),
+                         keep.to(device), valid.to(device), temps.to(device), K,
+                         num_ids.to(device), ids, n_slots, canvas_len, width, logits_mode)
+
+
+def stash_c4(device="cpu", K=20) -> StashWorkload:
+    """The stash over the C4 logits (4096 x 262144 as 16 canvases of 256):
+    16 requests with a permuted src, slots spread over a stash of 24, the
+    kept half (C4's kept slots), three kept requests with valid below 256,
+    and two kept requests listing 5 and 20 token ids; width K + 4."""
+    w = c4(device, K=K)
+    canvas_len = w.canvas_len
+    m = w.rows // canvas_len
+    gc = _gen(41, "cpu")
+    src = torch.randperm(m, generator=gc).to(torch.int32)
+    slots = torch.randperm(24, generator=gc)[:m].to(torch.int32)
+    keep = w.keep_mask.cpu()[src.long()]
+    temps = w.temps.cpu()[src.long()]
+    valid = torch.full((m,), canvas_len, dtype=torch.int32)
+    kept = torch.nonzero(keep).flatten().tolist()
+    for j, v in zip(kept[:3], (200, 17, 1)):
+        valid[j] = v
+    width = K + 4
+    ids_stride = 24
+    ids = torch.randint(0, w.vocab, (m, ids_stride), generator=gc, dtype=torch.int32)
+    num_ids = torch.zeros(m, dtype=torch.int32)
+    for j, n in zip(kept[-2:], (5, 20)):
+        num_ids[j] = n
+    return StashWorkload("S4", w.logits, canvas_len, src.to(device), slots.to(device),
+                         keep.to(device), valid.to(device), temps.to(device), K,
+                         num_ids.to(device), ids.to(device), 24, canvas_len, width)
 
 
 WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5}

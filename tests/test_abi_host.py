@@ -27,7 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["rowstats_run", "topk_logprobs", "rowstats_last_error",
+    assert declared_functions() == sorted(["rowstats_run", "topk_logprobs",
+                                           "stash_converged_logprobs", "rowstats_last_error",
                                            "rowstats_check_device", "rowstats_release"])
 
 
@@ -106,3 +107,46 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(2, 8)
     with pytest.raises(ValueError):
         rs.sample_row_stats(x, torch.ones(1), 2, 0)
+
+
+def stash(logits=FAKE, stride=8, lrows=8, vocab=8, canvas=2, m=3, src=FAKE, slots=FAKE,
+          keep=FAKE, valid=FAKE, temps=FAKE, K=2, nids=FAKE, ids=NULL, ids_stride=0,
+          n_slots=4, positions=2, width=3, out_ids=FAKE, out_lp=FAKE, out_rk=FAKE, mode=0):
+    return rs.lib().stash_converged_logprobs(
+        logits, stride, lrows, vocab, canvas, m, src, slots, keep, valid, temps, K, nids, ids,
+        ids_stride, n_slots, positions, width, out_ids, out_lp, out_rk, mode, NULL)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(m=-1), ERR_SHAPE),
+    (dict(lrows=0), ERR_SHAPE),
+    (dict(vocab=0), ERR_SHAPE),
+    (dict(stride=7), ERR_SHAPE),
+    (dict(canvas=0), ERR_SHAPE),
+    (dict(m=2**30, canvas=4, positions=4), ERR_SHAPE),
+    (dict(K=-1), ERR_K),
+    (dict(K=9), ERR_K),
+    (dict(K=65, vocab=100, stride=100, width=70), ERR_K),
+    (dict(width=2), ERR_SHAPE),        # num_topk + 1 <= width
+    (dict(n_slots=0), ERR_SHAPE),
+    (dict(positions=1), ERR_SHAPE),    # positions >= canvas_len
+    (dict(logits=NULL), ERR_NULL),
+    (dict(temps=NULL), ERR_NULL),
+    (dict(src=NULL), ERR_NULL),
+    (dict(slots=NULL), ERR_NULL),
+    (dict(keep=NULL), ERR_NULL),
+    (dict(valid=NULL), ERR_NULL),
+    (dict(out_ids=NULL), ERR_NULL),
+    (dict(out_lp=NULL), ERR_NULL),
+    (dict(out_rk=NULL), ERR_NULL),
+    (dict(ids=FAKE, nids=NULL, ids_stride=2), ERR_NULL),
+    (dict(ids=FAKE, ids_stride=0), ERR_SHAPE),
+])
+def test_stash_rejects(kwargs, code):
+    assert stash(**kwargs) == code
+    assert rs.last_error() != ""
+
+
+def test_stash_zero_requests_is_a_no_op():
+    assert stash(m=0, logits=NULL, src=NULL, slots=NULL, keep=NULL, valid=NULL, temps=NULL,
+                 out_ids=NULL, out_lp=NULL, out_rk=NULL) == OK

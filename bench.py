@@ -9,10 +9,11 @@ bf16 probs. Inputs are resident in HBM before the timed region.
 Prints one JSON line: the metric (algorithmic logits+probs GB/s), the
 roofline of the kernel (HBM, 8 TB/s), the oracle's CPU rate on a bounded
 sample of the same workload, and secondary measurements of the other
-workloads (C3 stats-only, C4 top-K, C5 large padded) under "others".
+workloads (C3 stats-only, C4 top-K, C5 large padded, S4 the converged-logprob
+stash over C4's logits) under "others".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others]
-       [--no-cpu] [--only C2|C3|C4|C5] [--calib-copy]
+       [--no-cpu] [--only C2|C3|C4|C5|S4] [--calib-copy]
 """
 from __future__ import annotations
 
@@ -43,6 +44,15 @@ def topk_algorithmic_bytes(kept_rows: int, vocab: int, K: int, slots: int = 0) -
     """Logits of kept rows read once + K (value, index) pairs per kept row +
     a temperature and a keep flag per slot."""
     return kept_rows * (4 * vocab + 12 * K) + 5 * slots
+
+
+def stash_algorithmic_bytes(kept_rows: int, vocab: int, width: int, m: int,
+                            id_reads: int) -> int:
+    """Logits of the kept requests' rows read once + one stash row (width
+    ids and values) and a rank per kept row + the per-request arguments
+    (src, slots, valid, num_ids, temps, keep) + 8 B per listed token id (the
+    id and the gathered logit)."""
+    return kept_rows * (4 * vocab + 8 * width + 4) + 21 * m + 8 * id_reads
 
 
 def source_hash() -> str:
@@ -168,6 +178,32 @@ def calib_copy(steps=5):
                       "launches": steps, "kernel": "torch.neg (elementwise)"}))
 
 
+def bench_stash(w, steps, warmup):
+    import torch
+    import row_softmax_statistics_amd as rs
+    dev = w.logits.device
+    out_ids = torch.empty(w.n_slots, w.positions, w.width, dtype=torch.int32, device=dev)
+    out_lp = torch.empty(w.n_slots, w.positions, w.width, dtype=torch.float32, device=dev)
+    out_rk = torch.empty(w.n_slots, w.positions, dtype=torch.int32, device=dev)
+
+    def step():
+        rs.stash_converged_logprobs(w.logits, w.canvas_len, w.src, w.slots, w.keep, w.valid,
+                                    w.temps, w.K, w.num_ids, w.ids, out_ids, out_lp, out_rk,
+                                    w.logits_mode)
+
+    ms, wall = time_launches(step, steps, warmup)
+    rs.check_device()
+    n = torch.clamp(w.valid.long(), 0, w.canvas_len) * (w.keep != 0).long()
+    kept = int(n.sum())
+    ids_stride = w.ids.shape[1] if w.ids is not None else 0
+    per_row_ids = torch.clamp(w.num_ids.long(), 0, min(w.width - 1, ids_stride)) \
+        if w.ids is not None else torch.zeros_like(n)
+    id_reads = int((per_row_ids * n).sum())
+    nbytes = stash_algorithmic_bytes(kept, w.vocab, w.width, w.m, id_reads)
+    return {"ms": ms, "wall_ms": wall, "bytes": nbytes, "gbs": nbytes / ms / 1e6,
+            "kept_rows_per_s": kept / ms * 1e3}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,7 +212,7 @@ def main():
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--only", choices=["C2", "C3", "C4", "C5"], default=None)
+    ap.add_argument("--only", choices=["C2", "C3", "C4", "C5", "S4"], default=None)
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -193,8 +229,9 @@ def main():
     dev = "cuda:0"
 
     if args.only:
-        w = syn.WORKLOADS[args.only](dev)
+        w = syn.stash_c4(dev) if args.only == "S4" else syn.WORKLOADS[args.only](dev)
         r = bench_topk(w, args.steps, args.warmup) if args.only == "C4" else \
+            bench_stash(w, args.steps, args.warmup) if args.only == "S4" else \
             bench_rowstats(w, args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **{k: round(v, 4) if isinstance(v, float) else v
                                                      for k, v in r.items()}}))
@@ -227,10 +264,12 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_others:
         others = {}
-        for name in ("C3", "C5", "C4"):
-            wo = syn.WORKLOADS[name](dev)
-            ro = bench_topk(wo, max(5, args.steps // 2), 2) if name == "C4" else \
-                bench_rowstats(wo, max(5, args.steps // 2), 2)
+        for name in ("C3", "C5", "C4", "S4"):
+            wo = syn.stash_c4(dev) if name == "S4" else syn.WORKLOADS[name](dev)
+            n_steps = max(5, args.steps // 2)
+            ro = bench_topk(wo, n_steps, 2) if name == "C4" else \
+                bench_stash(wo, n_steps, 2) if name == "S4" else \
+                bench_rowstats(wo, n_steps, 2)
             ro = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in ro.items()}
             ro["pct_hbm_peak"] = round(100 * ro["gbs"] / HBM_PEAK_GBS, 2)
             ro["traffic"] = recorded_traffic(name)

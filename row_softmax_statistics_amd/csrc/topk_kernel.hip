@@ -754,8 +754,11 @@ __global__ __launch_bounds__(kListThreads) void kept_rows_kernel(const uint8_t *
 // Also zeroes the row-claim counters. One workgroup; thread t handles a
 // contiguous range of requests.
 // ---------------------------------------------------------------------------
+constexpr int kStashLdsRequests = 4096;  // requests whose offsets fit in LDS
+
 __global__ __launch_bounds__(kListThreads) void stash_rows_kernel(TopKParams p) {
   __shared__ int64_t wave_tot[kListThreads / kWave];
+  __shared__ int64_t req_off[kStashLdsRequests + 1];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int64_t per = (p.m + kListThreads - 1) / kListThreads;
@@ -787,21 +790,40 @@ __global__ __launch_bounds__(kListThreads) void stash_rows_kernel(TopKParams p) 
   __syncthreads();
   int64_t off = incl - cnt;
   for (int w = 0; w < wave; ++w) off += wave_tot[w];
-  for (int64_t j = j0; j < j1; ++j) {
-    const int64_t n = rows_of(j);
-    if (n <= 0) continue;
-    const int64_t row0 = (int64_t)p.src[j] * p.canvas_len;
-    const int64_t dst0 = (int64_t)p.slots[j] * p.positions;
-    const float T = p.temps[j];
-    for (int64_t q = 0; q < n; ++q, ++off) {
-      p.kept[off] = row0 + q;
-      p.kept_temp[off] = T;
-      p.kept_dst[off] = dst0 + q;
-      p.kept_req[off] = (int32_t)j;
+  int64_t total = 0;
+  for (int w = 0; w < kListThreads / kWave; ++w) total += wave_tot[w];
+  auto put = [&](int64_t i, int64_t j, int64_t q) {
+    p.kept[i] = (int64_t)p.src[j] * p.canvas_len + q;
+    p.kept_temp[i] = p.temps[j];
+    p.kept_dst[i] = (int64_t)p.slots[j] * p.positions + q;
+    p.kept_req[i] = (int32_t)j;
+  };
+  if (p.m <= kStashLdsRequests) {
+    // every thread writes consecutive entries: the request of entry i is
+    // the last one whose first entry is at or below i
+    for (int64_t j = j0; j < j1; ++j) {
+      req_off[j] = off;
+      off += max(rows_of(j), (int64_t)0);
+    }
+    if (tid == 0) req_off[p.m] = total;
+    __syncthreads();
+    for (int64_t i = tid; i < total; i += kListThreads) {
+      int64_t lo = 0, hi = p.m;  // req_off[lo] <= i < req_off[hi]
+      while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (req_off[mid] <= i) lo = mid;
+        else hi = mid;
+      }
+      put(i, lo, i - req_off[lo]);
+    }
+  } else {
+    for (int64_t j = j0; j < j1; ++j) {
+      const int64_t n = rows_of(j);
+      for (int64_t q = 0; q < n; ++q, ++off) put(off, j, q);
     }
   }
   if (tid == kListThreads - 1) {
-    p.kept[p.rows] = off;
+    p.kept[p.rows] = total;
     p.counters[0] = 0u;
     p.counters[1] = 0u;
   }

@@ -207,11 +207,15 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, 
   // ---- mask the row end, scale s = fl32(x / Tc) ----
   const int32_t left = V - c0;
   if (left < kChunkCols) {
+    // columns left from this lane's first one; the lane number is taken
+    // afresh here, else the compiler keeps the 32 comparisons across the
+    // row loop as scalar register pairs (and spills them)
+    const int32_t lim = left - 4 * lane_here();
 #pragma unroll
     for (int j = 0; j < kQ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        set_comp(v[j], i, (4 * (j * kWave + lane) + i < left) ? comp(v[j], i) : -INFINITY);
+        set_comp(v[j], i, (4 * j * kWave + i < lim) ? comp(v[j], i) : -INFINITY);
   }
   float mt = -INFINITY;
   if (T == 1.0f) {  // x / 1 = x

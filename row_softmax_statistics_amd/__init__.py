@@ -201,6 +201,8 @@ def stash_converged_logprobs(logits: torch.Tensor, canvas_len: int, src: torch.T
         num_token_ids = _gpu_vec(num_token_ids, torch.int32, "num_token_ids", m)
         if token_ids.dtype != torch.int32 or not token_ids.is_cuda or token_ids.dim() != 2:
             raise ValueError("token_ids must be a 2-D int32 GPU tensor")
+        if token_ids.shape[0] < m or token_ids.shape[1] < 1:
+            raise ValueError("token_ids needs a row of at least one id per request")
         if token_ids.stride(1) != 1:
             token_ids = token_ids.contiguous()
         ids_stride = token_ids.stride(0) if token_ids.shape[0] > 1 else token_ids.shape[1]

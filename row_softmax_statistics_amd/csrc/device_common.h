@@ -308,7 +308,9 @@ __device__ __forceinline__ uint32_t pack_fp16x2(float a, float b) {
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  // every lane reads a valid lane for the patterns used here; with no
+  // "old" value the compiler can fold the move into the consuming operation
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
 constexpr int kDppQuadSwap1 = 0xB1, kDppQuadSwap2 = 0x4E, kDppHalfMirror = 0x141,
@@ -386,12 +388,22 @@ __device__ __forceinline__ T wave_allreduce(T v, Op op) {
 }
 
 struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct MaxI { __device__ int32_t operator()(int32_t a, int32_t b) const { return a > b ? a : b; } };
 struct MinI { __device__ int32_t operator()(int32_t a, int32_t b) const { return a < b ? a : b; } };
 struct SumF { __device__ float operator()(float a, float b) const { return a + b; } };
 struct SumD { __device__ double operator()(double a, double b) const { return a + b; } };
 struct SumI { __device__ int32_t operator()(int32_t a, int32_t b) const { return a + b; } };
 struct MaxD { __device__ double operator()(double a, double b) const { return fmax(a, b); } };
 struct MaxI64 { __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; } };
+
+// Largest of a non-NaN fp32 value over the wave (every lane gets it), taken
+// on the order-preserving integers of the bits: an fp32 max would first
+// quiet (canonicalise) every value a lane exchange brings in.
+__device__ __forceinline__ float wave_max_f32(float v) {
+  const int32_t b = __float_as_int(v);
+  const int32_t k = wave_allreduce(b ^ ((b >> 31) & 0x7FFFFFFF), MaxI());
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
+}
 
 // Workgroup-wide reductions through one LDS slot per wave.
 template <int NT, class T, class Op>

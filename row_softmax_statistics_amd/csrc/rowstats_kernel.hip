@@ -112,7 +112,7 @@ __device__ __forceinline__ Tuple combine(const Tuple &a, const Tuple &b) {
 // Merge of the summaries held by the 64 lanes; every lane gets the result.
 __device__ __forceinline__ Tuple wave_merge(const Tuple &t) {
   Tuple r;
-  r.m = wave_allreduce(t.m, MaxF());
+  r.m = wave_max_f32(t.m);
   double S = 0.0, W = 0.0;
   add_rescaled(t, r.m, S, W);
   r.S = wave_allreduce(S, SumD());
@@ -314,7 +314,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
       mt = fmaxf(mt, max4(v[j]));
     }
   }
-  const float mw = wave_allreduce(mt, MaxF());
+  const float mw = wave_max_f32(mt);
 
   // ---- lowest column of the wave attaining its max ----
   // kt: this lane's first element equal to its own maximum (the Gumbel
@@ -377,7 +377,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
         const uint4 w = philox4x32_10((uint32_t)(ct >> 2), 0u, r0, r1, k0, k1);
         zt = (mt - mw) + g32(pick(w, ct & 3)) - 0x1p-10f;
       }
-      zt = wave_allreduce(zt, MaxF());
+      zt = wave_max_f32(zt);
       a = fminf(a, __builtin_amdgcn_exp2f(-zt * kLog2e) * (1.0f + 0x1p-12f));
     }
     const float kc = a * kTestMargin;
@@ -435,7 +435,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
       }
     }
     // Only candidates within 2^-8 of the wave's best estimate can win.
-    const float zmax = wave_allreduce(za1, MaxF());
+    const float zmax = wave_max_f32(za1);
     const float zcut = zmax - 0x1p-8f;
     const uint64_t near = __ballot(za1 >= zcut);
     if (!exact && __popcll(near) == 1 && __ballot(za2 >= zcut) == 0) {

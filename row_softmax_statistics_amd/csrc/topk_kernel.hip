@@ -231,7 +231,7 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, 
       mt = fmaxf(mt, max4(v[j]));
     }
   }
-  const float mw = wave_allreduce(mt, MaxF());
+  const float mw = wave_max_f32(mt);
 
   // ---- S = sum exp(s - m) of the chunk (1 <= S <= 2048 unless empty) ----
   const float mu = (mw == -INFINITY) ? 0.0f : mw;
@@ -447,7 +447,7 @@ __device__ void merge_row_topk(const TopKParams &p, int64_t pos, int64_t row, in
     add_header(ready(h, o));
     umax = max(umax, words_ukey(ready(w0, o + 16u)));
   }
-  const float M = wave_allreduce(ml, MaxF());
+  const float M = wave_max_f32(ml);
   const double S = wave_allreduce(
       Sl > 0.0 ? Sl * (double)__builtin_amdgcn_exp2f((ml - M) * kLog2e) : 0.0, SumD());
   const double logS = log_d(S);  // log Z = M + logS

@@ -112,6 +112,19 @@ def test_stash_many_requests():
     check(w, "stash m=300")
 
 
+def test_stash_more_requests_than_lds_offsets():
+    # above 4096 requests the pre-pass lists rows thread by thread
+    w = syn.stash_case(DEV, m=5000, canvas_len=2, vocab=300, K=4, seed=72)
+    check(w, "stash m=5000")
+
+
+def test_stash_wider_positions():
+    # the stash holds more positions than a canvas: the extra ones stay untouched
+    w = syn.stash_case(DEV, m=5, canvas_len=3, vocab=900, K=2, seed=73)
+    w.positions = 7
+    check(w, "stash positions=7")
+
+
 def test_stash_bad_indices_are_skipped_and_flagged():
     w = syn.stash_case(DEV, m=5, canvas_len=4, vocab=700, K=3, seed=80, with_ids=True)
     w.keep.fill_(1)

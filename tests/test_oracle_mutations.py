@@ -65,3 +65,50 @@ def test_every_planted_mistake_is_caught():
         results = list(ex.map(lambda m: _run_mutant(*m, workdir), MUTANTS))
     survivors = [name for name, rc in results if rc == 0]
     assert not survivors, f"mutants not caught by the pins: {survivors}"
+
+
+# The numpy oracle of the stash, mutated the same way and run against its pins.
+STASH_SRC = os.path.join(ROOT, "oracle", "stash.py")
+STASH_MUTANTS = [
+    ("stash_ties_to_higher_id", "order = np.lexsort((np.arange(V), -s64))",
+     "order = np.lexsort((-np.arange(V), -s64))"),
+    ("stash_rank_strict", "rank = int(np.count_nonzero(s64 >= s64[top]))",
+     "rank = int(np.count_nonzero(s64 > s64[top]))"),
+    ("stash_valid_not_cut", "n = min(max(int(valid[j]), 0), canvas_len)", "n = max(int(valid[j]), 0)"),
+    ("stash_row_from_slot", "row = int(src[j]) * canvas_len + p", "row = int(slots[j]) * canvas_len + p"),
+    ("stash_pad_id_one", "out_ids = np.zeros(width, np.int32)", "out_ids = np.ones(width, np.int32)"),
+    ("stash_no_temperature", "s = (logits[row].astype(np.float32) / tc).astype(np.float32)",
+     "s = logits[row].astype(np.float32)"),
+    ("stash_logprob_drops_logS", "return np.float32((s64[c] - m) - logS)", "return np.float32(s64[c] - m)"),
+    ("stash_ids_not_cut_at_width", "cnt = min(int(num_token_ids[j]), width - 1, token_ids.shape[1])",
+     "cnt = min(int(num_token_ids[j]), token_ids.shape[1])"),
+    ("stash_zero_ids_means_ids", "if token_ids is not None and int(num_token_ids[j]) > 0:",
+     "if token_ids is not None and int(num_token_ids[j]) >= 0:"),
+    ("stash_keep_ignored", "        if not keep[j]:\n            continue", "        if False:\n            continue"),
+    ("stash_clamp_constant", "T_MIN = np.float32(1e-10)", "T_MIN = np.float32(1e-9)"),
+    ("stash_logits_mode_logprob", "        if logits_mode:\n            return np.float32(s[c])",
+     "        if logits_mode:\n            return np.float32((s64[c] - m) - logS)"),
+]
+
+
+def _run_stash_mutant(name, old, new, workdir):
+    src = open(STASH_SRC).read()
+    assert src.count(old) == 1, f"mutation {name} does not match exactly once"
+    path = os.path.join(workdir, f"{name}.py")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    env = dict(os.environ, ROWSTATS_STASH_ORACLE=path)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_stash.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode
+
+
+def test_stash_pins_reject_every_mutant():
+    with tempfile.TemporaryDirectory() as d:
+        # control: an unchanged copy loaded the same way passes the pins
+        assert _run_stash_mutant("control", "T_MIN = np.float32(1e-10)", "T_MIN = np.float32(1e-10)", d)[1] == 0
+        with ThreadPoolExecutor(max_workers=4) as ex:
+            results = list(ex.map(lambda m: _run_stash_mutant(*m, d), STASH_MUTANTS))
+    survivors = [name for name, rc in results if rc == 0]
+    assert not survivors, f"stash mutants not caught by any pin: {survivors}"

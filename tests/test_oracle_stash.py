@@ -9,13 +9,23 @@ padded with token 0 at -inf. The values are pinned to the separately
 pinned C oracle of the top-K entry point, to closed forms and to
 invariants of log-softmax.
 """
+import importlib.util
 import math
+import os
 
 import numpy as np
 import pytest
 
 import oracle
 from oracle import stash
+
+# ROWSTATS_STASH_ORACLE lets the mutation test load a deliberately broken
+# copy of the stash oracle and check that these pins reject it
+if os.environ.get("ROWSTATS_STASH_ORACLE"):
+    _spec = importlib.util.spec_from_file_location("stash_mutant",
+                                                   os.environ["ROWSTATS_STASH_ORACLE"])
+    stash = importlib.util.module_from_spec(_spec)
+    _spec.loader.exec_module(stash)
 
 pytestmark = pytest.mark.filterwarnings("ignore:divide by zero")
 

@@ -6,6 +6,8 @@
 // epoch.
 #pragma once
 
+#include <stddef.h>
+
 #include "device_common.h"
 #include "rowstats_internal.h"
 
@@ -138,6 +140,23 @@ __device__ __forceinline__ void lds_read_chunk(float4 (&v)[kQ], const float4 *bu
 #pragma unroll
   for (int j = 0; j < kQ; ++j) v[j] = make_float4(r[j][0], r[j][1], r[j][2], r[j][3]);
 }
+
+// A field of the kernel's argument block, loaded where it is used. Fields
+// that only a rare path needs (the merger's outputs) would otherwise be
+// loaded at the kernel start and held in scalar registers across the row
+// loop, pushing hot values out to vector-register lanes. The empty
+// statement keeps the offset opaque, so the load is not merged with the one
+// at the start. Only for kernels whose single argument is `Params`, which
+// then starts the block.
+template <class T>
+__device__ __forceinline__ T kernel_arg_at(uint32_t offset) {
+  __asm__ volatile("" : "+s"(offset));
+  const __attribute__((address_space(4))) char *base =
+      (const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr();
+  return *reinterpret_cast<const __attribute__((address_space(4))) T *>(base + offset);
+}
+#define LATE_ARG(Params, field) \
+  kernel_arg_at<decltype(Params::field)>((uint32_t)offsetof(Params, field))
 
 // cm = 2 cm + (a >= b): the compare writes VCC and the add takes it as the
 // carry in (the compiler would spend a select and a shift instead). A carry

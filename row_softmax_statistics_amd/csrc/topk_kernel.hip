@@ -37,7 +37,6 @@
 
 #include <float.h>
 #include <limits.h>
-#include <stddef.h>
 
 namespace rowstats {
 namespace {
@@ -315,21 +314,6 @@ __device__ __forceinline__ int32_t load_uniform_i32(const int32_t *p) {
   return *(const __attribute__((address_space(4))) int32_t *)p;
 }
 
-// A field of the kernel's argument block, loaded where it is used. Fields
-// that only the stash writer needs would otherwise be loaded at the kernel
-// start and held in scalar registers across the row loop, pushing hot
-// values out to vector-register lanes. The empty statement keeps the
-// offset opaque, so the load is not merged with the one at the start.
-// (TopKParams is the kernel's only argument, at the start of the block.)
-template <class T>
-__device__ __forceinline__ T late_arg(uint32_t offset) {
-  __asm__ volatile("" : "+s"(offset));
-  const __attribute__((address_space(4))) char *base =
-      (const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr();
-  return *reinterpret_cast<const __attribute__((address_space(4))) T *>(base + offset);
-}
-#define LATE_ARG(field) late_arg<decltype(TopKParams::field)>((uint32_t)offsetof(TopKParams, field))
-
 // Columns of the row whose scaled value reaches M (its maximum): one pass
 // over the row by the merger, for rows whose K largest keys all tie at M.
 __device__ __forceinline__ int count_at_max(const TopKParams &p, int64_t row, float T, float M) {
@@ -349,12 +333,12 @@ __device__ __forceinline__ void write_stash_row(const TopKParams &p, int64_t pos
   const int lane = lane_here();
   const int K = p.K;
   const float T = load_uniform(p.kept_temp + pos);
-  const int64_t dst = load_uniform_i64(LATE_ARG(kept_dst) + pos);
-  const int32_t j = load_uniform_i32(LATE_ARG(kept_req) + pos);
-  const int32_t W = LATE_ARG(width);
-  const bool logits_mode = LATE_ARG(logits_mode) != 0;
-  int32_t *oid = LATE_ARG(out_ids32) + dst * W;
-  float *olp = LATE_ARG(out_lp) + dst * W;
+  const int64_t dst = load_uniform_i64(LATE_ARG(TopKParams, kept_dst) + pos);
+  const int32_t j = load_uniform_i32(LATE_ARG(TopKParams, kept_req) + pos);
+  const int32_t W = LATE_ARG(TopKParams, width);
+  const bool logits_mode = LATE_ARG(TopKParams, logits_mode) != 0;
+  int32_t *oid = LATE_ARG(TopKParams, out_ids32) + dst * W;
+  float *olp = LATE_ARG(TopKParams, out_lp) + dst * W;
   auto value = [&](float s) -> float {
     return logits_mode ? s : (float)(((double)s - (double)M) - logS);
   };
@@ -362,12 +346,12 @@ __device__ __forceinline__ void write_stash_row(const TopKParams &p, int64_t pos
   const int64_t mine = lane < K ? buf[lane] : INT64_MIN;
   int ties = __popcll(__ballot(lane < K && (int32_t)(mine >> 32) == key32(M)));
   if (ties == K) ties = count_at_max(p, row, T, M);
-  int n = LATE_ARG(K_out);
+  int n = LATE_ARG(TopKParams, K_out);
   bool by_ids = false;
-  const int32_t *ids = LATE_ARG(ids);
-  const int64_t ids_stride = LATE_ARG(ids_stride);
+  const int32_t *ids = LATE_ARG(TopKParams, ids);
+  const int64_t ids_stride = LATE_ARG(TopKParams, ids_stride);
   if (ids != nullptr) {
-    const int32_t c = load_uniform_i32(LATE_ARG(num_ids) + j);
+    const int32_t c = load_uniform_i32(LATE_ARG(TopKParams, num_ids) + j);
     if (c > 0) {
       by_ids = true;
       n = (int)min((int64_t)min(c, W - 1), ids_stride);
@@ -376,7 +360,7 @@ __device__ __forceinline__ void write_stash_row(const TopKParams &p, int64_t pos
   if (lane == 0) {
     oid[0] = key64_col(buf[0]);
     olp[0] = value(key32_value((int32_t)(buf[0] >> 32)));
-    LATE_ARG(out_ranks)[dst] = ties;
+    LATE_ARG(TopKParams, out_ranks)[dst] = ties;
   }
   if (by_ids) {
     const double rtc = 1.0 / (double)clamp_temp(T);

@@ -344,6 +344,9 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     v[j] = e;
   }
 
+  // wave sums in fp32 (the summary carries them as fp32 words)
+  const float Sw = wave_allreduce(St, SumF());
+
   // ---- Gumbel-max over the wave's columns (T > 0) ----
   // The wave reports its best perturbed score z = s + g and that column. The
   // score is an fp32 estimate (within 2^-9 of exact) unless the wave had to
@@ -369,7 +372,6 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     // Flat waves let many columns pass the test; the expected number is
     // sum_c exp(s_c - zlb) = a sum e / 2^32. When it is large, raise zlb to
     // a lower bound of the best score among every lane's own maximum.
-    const float Sw = wave_allreduce(St, SumF());
     if (Sw * 0x1p-32f * a > 8.0f) {
       float zt = -INFINITY;  // relative to m
       if (mt != -INFINITY) {
@@ -473,8 +475,8 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   Tuple t;
   t.m = mw;
   t.am = amw;
-  t.S = wave_allreduce((double)St, SumD());
-  t.W = wave_allreduce((double)Wt, SumD());
+  t.S = (double)Sw;
+  t.W = (double)wave_allreduce(Wt, SumF());
   t.zb = zb;
   t.zc = zc;
   t.zx = zx;

@@ -241,7 +241,7 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) St += __builtin_amdgcn_exp2f((comp(v[j], i) - mu) * kLog2e);
   out.mw = mw;
-  out.S = (float)wave_allreduce((double)St, SumD());
+  out.S = wave_allreduce(St, SumF());  // the record header holds it as fp32
 
   // ---- threshold: the K-th largest lane maximum ----
   const uint32_t uk = wave_kth_largest<uint32_t>((uint32_t)key32(mt) ^ 0x80000000u, K);

@@ -366,19 +366,19 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     constexpr float kLn2 = 0.693147180559945309f;
     // fp32 Gumbel value -log(-log u) of a word, error below 2^-12
     auto g32 = [&](uint32_t w) { return -__builtin_amdgcn_logf(neg_log_u_f32(w)) * kLn2; };
+    // The word of each lane's own maximum (column ct); the lane holding the
+    // wave's argmax thereby has the argmax's word.
+    const int32_t ct = col_of(kt);
+    const uint32_t wt = pick(philox4x32_10((uint32_t)(ct >> 2), 0u, r0, r1, k0, k1), ct & 3);
     // a = exp(m - zlb) = -log u of the argmax's word, zlb = m + g_argmax
-    float a = neg_log_u_f32(
-        pick(philox4x32_10((uint32_t)(amw >> 2), 0u, r0, r1, k0, k1), amw & 3));
+    const int la = __builtin_ctzll(__ballot(mt == mw && ct == amw));
+    float a = neg_log_u_f32((uint32_t)__builtin_amdgcn_readlane((int)wt, la));
     // Flat waves let many columns pass the test; the expected number is
     // sum_c exp(s_c - zlb) = a sum e / 2^32. When it is large, raise zlb to
     // a lower bound of the best score among every lane's own maximum.
     if (Sw * 0x1p-32f * a > 8.0f) {
-      float zt = -INFINITY;  // relative to m
-      if (mt != -INFINITY) {
-        const int32_t ct = col_of(kt);
-        const uint4 w = philox4x32_10((uint32_t)(ct >> 2), 0u, r0, r1, k0, k1);
-        zt = (mt - mw) + g32(pick(w, ct & 3)) - 0x1p-10f;
-      }
+      // relative to m
+      float zt = (mt != -INFINITY) ? (mt - mw) + g32(wt) - 0x1p-10f : -INFINITY;
       zt = wave_max_f32(zt);
       a = fminf(a, __builtin_amdgcn_exp2f(-zt * kLog2e) * (1.0f + 0x1p-12f));
     }

@@ -20,20 +20,23 @@
 // call's epoch in its high half; stores and loads of these words are
 // device-scope coherent and 64-bit words are never torn, so a word that
 // shows the current epoch is final. One member per row (the merger,
-// rotating over the members) polls the row's summaries one chunk later,
-// merges them, writes the row's argmax, sample and entropy, and publishes
-// (m, 1 / S) of the row. Every member waits for that row result two chunks
-// later: with probs it then writes its chunk's probabilities from the exp
-// values it kept in registers, so the exchange overlaps two chunks of work.
-// The launch is cooperative (every wave resident), so each wait ends.
+// rotating over the members) polls the row's summaries one or two chunks
+// later (kMergeLag), merges them, writes the row's argmax, sample and
+// entropy, and publishes (m, 1 / S) of the row. Every member waits for that
+// row result two chunks after the merge (kLag): with probs it then writes
+// its chunk's probabilities from the exp values it kept in registers, so
+// the exchange overlaps chunks of work. The launch is cooperative (every
+// wave resident), so each wait ends.
 //
 // Gumbel sample (T > 0). The wave's argmax a gives a lower bound
 // zlb = s_a + g_a on its best perturbed score. A column can reach zlb only
 // if s >= zlb - 22.8739 (the largest Gumbel value a 32-bit word yields), so
 // quads below that skip the Philox draw; a drawn column can reach zlb only
 // if 1 - u <= exp(s - zlb), which follows from -log u >= 1 - u and reuses
-// the column's exp value. The few columns passing both are scored exactly
-// in fp64 and the best score wins (ties to the lower column).
+// the column's exp value (tested per quad first, then per column). The few
+// columns passing get an fp32 score estimate; those within 2^-8 of the best
+// are scored exactly in fp64, and the best score wins (ties to the lower
+// column).
 #include "chunk_common.h"
 #include "device_common.h"
 #include "device_math.h"

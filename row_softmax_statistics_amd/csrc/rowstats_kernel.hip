@@ -333,6 +333,10 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   // ---- exp values e = 2^32 exp(s - m) in place of s, and their sums ----
   // The 2^32 factor keeps every probability that survives rounding to
   // bf16/fp16 away from fp32 denormals; it cancels in every ratio.
+  // d = s - m is -inf for a -inf logit (and for a masked column, or when the
+  // difference overflows); then e = 0 and e d is NaN, which the wave sum of
+  // W shows. Such a wave recomputes W below with d clamped to -FLT_MAX (its
+  // terms are then 0), in the same order; every other wave skips the clamp.
   const float mu = (mw == -INFINITY) ? 0.0f : mw;
   float St = 0.0f, Wt = 0.0f;
 #pragma unroll
@@ -340,7 +344,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     float4 e;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float d = fmaxf(comp(v[j], i) - mu, -FLT_MAX);
+      const float d = comp(v[j], i) - mu;
       const float ei = __builtin_amdgcn_exp2f(fmaf(d, kLog2e, 32.0f));
       St += ei;
       Wt = fmaf(ei, d, Wt);
@@ -480,11 +484,34 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     }
   }
 
+  float Ww = wave_allreduce(Wt, SumF());
+  if (Ww != Ww) {
+    // Some e d was 0 times -inf: W again, with d clamped, from the logits
+    // (the LDS copy of the chunk, else memory; rare: -inf logits, the row
+    // end, values near the fp32 limit).
+    const int32_t left = V - c0 - 4 * lane_here();
+    Wt = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kQ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t k = 4 * j * kWave + i;  // column c0 + 4 lane + k
+        float x = -INFINITY;
+        if (k < left) {
+          if constexpr (LDSX) x = lds_read_f32(xbuf, 4 * lane_here() + k);
+          else x = p.logits[row * p.ld + c0 + 4 * lane_here() + k];
+        }
+        const float s = (T == 1.0f || x == -INFINITY) ? x : scale(x, rtc);
+        Wt = fmaf(comp(v[j], i), fmaxf(s - mu, -FLT_MAX), Wt);
+      }
+    Ww = wave_allreduce(Wt, SumF());
+  }
+
   Tuple t;
   t.m = mw;
   t.am = amw;
   t.S = (double)Sw;
-  t.W = (double)wave_allreduce(Wt, SumF());
+  t.W = (double)Ww;
   t.zb = zb;
   t.zc = zc;
   t.zx = zx;

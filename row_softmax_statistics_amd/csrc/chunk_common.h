@@ -44,6 +44,30 @@ __device__ __forceinline__ int lane_here() {
 // the counts above hold for the issue order written here.
 __device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
 
+// Exclusive prefix sum over the lanes of cnt (0 <= cnt < 128) and the wave
+// total, one bit of cnt at a time: a ballot of the bit and mbcnt (set bits
+// of lower lanes).
+__device__ __forceinline__ int wave_prefix(int cnt, int &total) {
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 7; ++b) {
+    const uint64_t m = __ballot((cnt >> b) & 1);
+    off += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))
+           << b;
+    tot += __popcll(m) << b;
+    if (__ballot(cnt >> (b + 1)) == 0) break;
+  }
+  total = tot;
+  return off;
+}
+
+// Keeps the compiler's LDS accesses in program order between lanes of a
+// wave (the hardware executes a wave's LDS operations in order).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");

@@ -278,11 +278,13 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
 // wave's summary (its best score exact when `exact` is set).
 // ---------------------------------------------------------------------------
 // With LDSX, xbuf is the wave's LDS copy of this chunk's raw logits (kept
-// until the chunk is reduced): candidates read their logits there.
+// until the chunk is reduced): candidates read their logits there. clist is
+// the wave's LDS list of kWave candidate columns.
 template <bool VEC, bool VKEYS, bool LDSX>
 __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t row, int32_t chunk,
                                               float4 (&v)[kQ], bool exact,
-                                              const PhiloxRoundKeys &rk, const float4 *xbuf) {
+                                              const PhiloxRoundKeys &rk, const float4 *xbuf,
+                                              int32_t *clist) {
   const int lane = lane_id();
   const int32_t V = p.vocab;
   const float T = load_uniform(p.temps + slot_of(p, row));
@@ -428,11 +430,8 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     // flight). Scoring from the exp values in registers avoids both but
     // costs more vector instructions, and measures slower.
     float za1 = -INFINITY, za2 = -INFINITY;
-    int32_t kbest = 0;
-    for (uint32_t c2 = cm; c2 != 0;) {
-      const int k = __builtin_clz(c2);
-      c2 &= ~(0x80000000u >> k);
-      const int32_t c = col_of(k);
+    int32_t cbest = INT_MAX;
+    auto score = [&](int32_t c) {
       if (c < V) {
         float x;
         if constexpr (LDSX) x = lds_read_f32(xbuf, c - c0);
@@ -442,10 +441,38 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
         if (z > za1) {
           za2 = za1;
           za1 = z;
-          kbest = k;
+          cbest = c;
         } else {
           za2 = fmaxf(za2, z);
         }
+      }
+    };
+    // The loop over a lane's candidates runs as often as the lane with the
+    // most of them needs. When some lane has two or more and the wave has at
+    // most 64, the candidates are first spread one per lane through LDS, so
+    // one scoring pass serves them all (each lane then holds at most one).
+    bool spread = false;
+    if (__ballot(__popc(cm) >= 2) != 0) {
+      int total;
+      int o = wave_prefix(__popc(cm), total);
+      if (total <= kWave) {
+        spread = true;
+        for (uint32_t c2 = cm; c2 != 0;) {
+          const int k = __builtin_clz(c2);
+          c2 &= ~(0x80000000u >> k);
+          clist[o++] = col_of(k);
+        }
+        wave_lds_order();
+        const int32_t c = lane < total ? clist[lane] : INT_MAX;
+        wave_lds_order();
+        score(c);
+      }
+    }
+    if (!spread) {
+      for (uint32_t c2 = cm; c2 != 0;) {
+        const int k = __builtin_clz(c2);
+        c2 &= ~(0x80000000u >> k);
+        score(col_of(k));
       }
     }
     // Only candidates within 2^-8 of the wave's best estimate can win.
@@ -453,15 +480,14 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
     const float zcut = zmax - 0x1p-8f;
     const uint64_t near = __ballot(za1 >= zcut);
     if (!exact && __popcll(near) == 1 && __ballot(za2 >= zcut) == 0) {
-      zc = __builtin_amdgcn_readlane(col_of(kbest), __builtin_ctzll(near));
+      zc = __builtin_amdgcn_readlane(cbest, __builtin_ctzll(near));
       zb = (double)mw + (double)zmax;
       zx = 0;
     } else {
       // exact fp64 scores of the candidates within the cut
       double bz = -INFINITY;
       int32_t bc = INT_MAX;
-      auto score_exact = [&](int k) {
-        const int32_t c = col_of(k);
+      auto score_exact = [&](int32_t c) {
         if (c < V) {
           const double z = exact_score(p, row, rtc, c);
           if (z > bz || (z == bz && c < bc)) {
@@ -470,12 +496,12 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
           }
         }
       };
-      if (za1 >= zcut) score_exact(kbest);
-      if (za2 >= zcut) {
-        for (uint32_t c2 = cm & ~(0x80000000u >> kbest); c2 != 0;) {
+      if (za1 >= zcut) score_exact(cbest);
+      if (za2 >= zcut) {  // (never after spreading: one candidate per lane)
+        for (uint32_t c2 = cm; c2 != 0;) {
           const int k = __builtin_clz(c2);
           c2 &= ~(0x80000000u >> k);
-          score_exact(k);
+          if (col_of(k) != cbest) score_exact(col_of(k));
         }
       }
       zb = wave_allreduce(bz, MaxD());
@@ -574,6 +600,8 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
   // other, so its candidates read their logits from LDS.
   constexpr int kBufs = (VEC && PROBS != 0) ? 2 : 1;
   __shared__ float4 stage[VEC ? kWaves * kChunkQuads * kBufs : 1];
+  // Gumbel candidates spread one per lane (kWave columns per wave)
+  __shared__ int32_t clists[kWaves * kWave];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int gw = (int)blockIdx.x * kWaves + wave;
   // the next call's row-claim counter starts at zero
@@ -649,7 +677,8 @@ __global__ __launch_bounds__(kThreads, PROBS ? 2 : 4) void rowstats_kernel(RowSt
       chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
     }
     const Tuple t = reduce_chunk<VEC, PROBS != 0, kBufs == 2>(p, row, chunk, cur, false, rk,
-                                                              (n & 1) ? buf1 : buf0);
+                                                              (n & 1) ? buf1 : buf0,
+                                                              clists + wave * kWave);
     // The empty statement consumes the loads issued before the copy on
     // every path, so the wait for them is placed here, exactly, and does not
     // wait for the copy.

@@ -96,24 +96,6 @@ __device__ __forceinline__ u32x4 poll_words(Rsrc r, uint32_t off, uint32_t epoch
 // ---------------------------------------------------------------------------
 // Wave-wide helpers.
 // ---------------------------------------------------------------------------
-// Exclusive prefix sum over the lanes of cnt (0 <= cnt < 128) and the wave
-// total, one bit of cnt at a time: a ballot of the bit and mbcnt (set bits
-// of lower lanes).
-__device__ __forceinline__ int wave_prefix(int cnt, int &total) {
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int b = 0; b < 7; ++b) {
-    const uint64_t m = __ballot((cnt >> b) & 1);
-    off += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))
-           << b;
-    tot += __popcll(m) << b;
-    if (__ballot(cnt >> (b + 1)) == 0) break;
-  }
-  total = tot;
-  return off;
-}
-
 // The k-th largest (1 <= k <= 64) over the lanes of u, in unsigned order.
 // Bits are fixed from the top: a bit is set when at least k lanes are at or
 // above the prefix with that bit set.
@@ -128,11 +110,6 @@ __device__ __forceinline__ U wave_kth_largest(U u, int k) {
   return res;
 }
 
-// Keeps the compiler's LDS accesses in program order between lanes of a
-// wave (the hardware executes a wave's LDS operations in order).
-__device__ __forceinline__ void wave_lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-}
 
 // Ranks of the keys of an LDS list of n <= 64 NX keys (distinct, except for
 // INT64_MIN): key[x] = list[lane + 64 x], rank[x] = the number of list keys

@@ -463,7 +463,10 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
           clist[o++] = col_of(k);
         }
         wave_lds_order();
-        const int32_t c = lane < total ? clist[lane] : INT_MAX;
+        // (the lane number taken afresh: an address kept from before the
+        // row loop would be spilled, and its reload waits for the copy)
+        const int l = lane_here();
+        const int32_t c = l < total ? clist[l] : INT_MAX;
         wave_lds_order();
         score(c);
       }

@@ -7,9 +7,11 @@
  * stream is DEVICE memory owned by the caller; the library keeps no pointer
  * after a call returns. Work is queued asynchronously on `stream` (a
  * hipStream_t passed as void*, NULL = the default stream): buffers must stay
- * alive until that stream has been synchronised. Calls that overlap in time
- * on one device share the library's scratch memory and must be serialised
- * by the caller (queue them on one stream).
+ * alive until that stream has been synchronised. rowstats_run,
+ * topk_logprobs and stash_converged_logprobs share a grow-only scratch
+ * buffer per device: a call queued on another stream than the previous one
+ * first waits, on the device, for that previous call (an event wait), so
+ * calls from several streams run one after another.
  *
  * All functions return ROWSTATS_OK (0) or a negative rowstats_status; they
  * never abort and never throw. Argument checks run before any HIP call, so

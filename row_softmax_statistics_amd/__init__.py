@@ -10,6 +10,7 @@ library is missing or fails to load, every call raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 
@@ -69,7 +70,20 @@ def lib() -> ctypes.CDLL:
             fn.restype = res
             fn.argtypes = args
         _lib = handle
+        atexit.register(_release_at_exit)
     return _lib
+
+
+def _release_at_exit():
+    """Frees the library's scratch before the interpreter (and the HIP
+    runtime under it) shuts down, once queued work has finished."""
+    if _lib is None or not torch.cuda.is_initialized():
+        return
+    try:
+        torch.cuda.synchronize()
+        _lib.rowstats_release()
+    except Exception:
+        pass
 
 
 def last_error() -> str:
@@ -99,25 +113,29 @@ def _check_logits(logits: torch.Tensor):
         raise ValueError("logits must have unit column stride")
 
 
-def sample_row_stats(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int, seed: int,
-                     probs_dtype: torch.dtype | None = None, *, out=None):
-    """Argmax, Gumbel-max sample, entropy and (optionally) softmax per row.
+def _check_out(t: torch.Tensor, name: str, shape, dtype, device):
+    if (not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != device
+            or tuple(t.shape) != tuple(shape) or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}")
 
-    Row ``i`` of ``logits`` ([rows, vocab] fp32, unit column stride, any row
-    stride) uses temperature ``temps[i // canvas_len]``; a temperature <= 0 is
-    greedy. Returns ``(argmax int64, sample int64, entropy fp32,
-    probs [rows, vocab] in probs_dtype or None)``. ``out`` may pass
-    preallocated ``(argmax, sample, entropy, probs)`` tensors.
-    """
+
+def _check_temps(temps: torch.Tensor, rows: int, canvas_len: int, device):
+    if temps.dtype != torch.float32 or temps.device != device or not temps.is_contiguous():
+        raise ValueError("temps must be a contiguous float32 tensor on the logits' device")
+    if canvas_len < 1:
+        raise ValueError("canvas_len must be >= 1")
+    if rows > 0 and temps.numel() < (rows + canvas_len - 1) // canvas_len:
+        raise ValueError("temps needs ceil(rows / canvas_len) entries")
+
+
+def _rowstats_call(entry: str, logits, temps, canvas_len, seed, probs_dtype, out):
     _check_logits(logits)
     if probs_dtype not in PROBS_CODES:
         raise ValueError("probs_dtype must be None, torch.bfloat16 or torch.float16")
-    if temps.dtype != torch.float32 or not temps.is_cuda or not temps.is_contiguous():
-        raise ValueError("temps must be a contiguous float32 GPU tensor")
     rows, vocab = logits.shape
-    if rows > 0 and temps.numel() < (rows + canvas_len - 1) // max(canvas_len, 1):
-        raise ValueError("temps needs ceil(rows / canvas_len) entries")
     dev = logits.device
+    _check_temps(temps, rows, canvas_len, dev)
     if out is None:
         argmax = torch.empty(rows, dtype=torch.int64, device=dev)
         sample = torch.empty(rows, dtype=torch.int64, device=dev)
@@ -126,36 +144,60 @@ def sample_row_stats(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int,
                  if probs_dtype is not None else None)
     else:
         argmax, sample, entropy, probs = out
-    rc = lib().rowstats_run(
+        _check_out(argmax, "argmax", (rows,), torch.int64, dev)
+        _check_out(sample, "sample", (rows,), torch.int64, dev)
+        _check_out(entropy, "entropy", (rows,), torch.float32, dev)
+        if probs_dtype is not None:
+            _check_out(probs, "probs", (rows, vocab), probs_dtype, dev)
+        elif probs is not None:
+            raise ValueError("probs must be None when probs_dtype is None")
+    rc = getattr(lib(), entry)(
         _ptr(logits), logits.stride(0) if rows > 1 else vocab, rows, vocab, _ptr(temps),
         canvas_len, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), PROBS_CODES[probs_dtype],
         _ptr(argmax), _ptr(sample), _ptr(entropy), _ptr(probs), _stream_ptr(dev))
-    _check(rc, "rowstats_run")
+    _check(rc, entry)
     return argmax, sample, entropy, probs
+
+
+def sample_row_stats(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int, seed: int,
+                     probs_dtype: torch.dtype | None = None, *, out=None):
+    """Per row of temperature-scaled logits: the argmax, one Gumbel-max draw,
+    the softmax entropy and, if ``probs_dtype`` is given, the softmax.
+
+    Row ``i`` of ``logits`` ([rows, vocab] fp32, unit column stride, any row
+    stride) uses temperature ``temps[i // canvas_len]``; a temperature <= 0 is
+    greedy. Returns ``(argmax int64, sample int64, entropy fp32,
+    probs [rows, vocab] in probs_dtype or None)``. ``out`` may pass
+    preallocated ``(argmax, sample, entropy, probs)`` tensors.
+    """
+    return _rowstats_call("rowstats_run", logits, temps, canvas_len, seed, probs_dtype, out)
 
 
 def topk_logprobs(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int,
                   keep_mask: torch.Tensor, K: int, out_vals: torch.Tensor | None = None,
                   out_idx: torch.Tensor | None = None):
-    """Top-K logprobs (descending, ties to the lower column) of kept slots' rows.
+    """For the rows of kept slots: the K largest scaled logits as logprobs, in
+    descending order with equal values ordered by column.
 
     Rows of slots with ``keep_mask[slot] == 0`` are not written. Returns
     ``(out_vals fp32 [rows, K], out_idx int64 [rows, K])``.
     """
     _check_logits(logits)
-    if temps.dtype != torch.float32 or not temps.is_cuda or not temps.is_contiguous():
-        raise ValueError("temps must be a contiguous float32 GPU tensor")
-    if keep_mask.dtype not in (torch.uint8, torch.bool) or not keep_mask.is_cuda:
-        raise ValueError("keep_mask must be a uint8/bool GPU tensor")
-    keep_mask = keep_mask.contiguous()
     rows, vocab = logits.shape
     dev = logits.device
+    _check_temps(temps, rows, canvas_len, dev)
+    slots = (rows + canvas_len - 1) // canvas_len
+    if (keep_mask.dtype not in (torch.uint8, torch.bool) or keep_mask.device != dev
+            or keep_mask.dim() != 1 or keep_mask.numel() < slots):
+        raise ValueError("keep_mask must be a 1-D uint8/bool tensor of ceil(rows / canvas_len) "
+                         "entries on the logits' device")
+    keep_mask = keep_mask.contiguous()
     if out_vals is None:
         out_vals = torch.empty(rows, K, dtype=torch.float32, device=dev)
     if out_idx is None:
         out_idx = torch.empty(rows, K, dtype=torch.int64, device=dev)
-    if not (out_vals.is_contiguous() and out_idx.is_contiguous()):
-        raise ValueError("outputs must be contiguous")
+    _check_out(out_vals, "out_vals", (rows, K), torch.float32, dev)
+    _check_out(out_idx, "out_idx", (rows, K), torch.int64, dev)
     rc = lib().topk_logprobs(
         _ptr(logits), logits.stride(0) if rows > 1 else vocab, rows, vocab, _ptr(temps),
         canvas_len, _ptr(keep_mask), int(K), _ptr(out_vals), _ptr(out_idx), _stream_ptr(dev))
@@ -176,13 +218,14 @@ def stash_converged_logprobs(logits: torch.Tensor, canvas_len: int, src: torch.T
                              token_ids: torch.Tensor | None, out_ids: torch.Tensor,
                              out_logprobs: torch.Tensor, out_ranks: torch.Tensor,
                              logits_mode: bool) -> None:
-    """Write the stash rows of the kept requests (arguments as on the page).
+    """Fills the stash rows of the kept requests (argument order of the
+    page's launcher).
 
-    Request ``j`` owns logits rows ``src[j] * canvas_len + p`` for
-    ``p < valid[j]``, divided by ``temps[j]``; where ``keep[j]`` they go to
-    ``out_*[slots[j], p]``: the argmax, then the request's token ids if it
-    has any (``num_token_ids[j] > 0``), else the ``num_topk`` largest, padded
-    with token 0 at -inf. ``src``, ``slots``, ``valid``, ``num_token_ids``,
+    The rows of request ``j`` are ``src[j] * canvas_len + p`` for positions
+    ``p < valid[j]``, scaled by ``1 / temps[j]``. For a kept request (``keep[j]``)
+    position ``p`` fills ``out_*[slots[j], p]`` with the argmax first, then
+    either the request's own token ids (when ``num_token_ids[j] > 0``) or its
+    ``num_topk`` largest columns, and token 0 at -inf in the remaining cells. ``src``, ``slots``, ``valid``, ``num_token_ids``,
     ``token_ids``, ``out_ids`` and ``out_ranks`` are int32; ``out_ids`` and
     ``out_logprobs`` are ``[slots, positions, width]``, ``out_ranks``
     ``[slots, positions]``, all contiguous.

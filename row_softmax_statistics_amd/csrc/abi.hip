@@ -16,6 +16,10 @@ using namespace rowstats;
 
 namespace {
 
+// Error words of the scratch: {report bits, epoch of the last call whose
+// wait gave up}. Host code reaches them through hipGetSymbolAddress.
+static __device__ __align__(16) uint32_t err_words[2];
+
 thread_local std::string g_last_error;
 
 int fail(int code, const char *fmt, ...) {
@@ -33,7 +37,7 @@ int fail_hip(hipError_t e, const char *what) {
 }
 
 constexpr int kMaxDevices = 64;
-// Start of the scratch buffer, for both entry points: the two row-claim
+// Start of each scratch area, for both entry points: the two row-claim
 // counters (at the same place for every call, since each call zeroes the
 // counter of the next one); the groups' row rings follow.
 constexpr size_t kScratchHead = 256;
@@ -41,20 +45,29 @@ constexpr size_t kScratchHead = 256;
 // the top-K key stores 0x7FFFFFFF - column: keep them all below 2^31.
 constexpr int64_t kMaxVocab = 0x7FFFFFFFLL - 65536;
 
-// Scratch of one device, grow-only, shared by both entry points: the
-// waves' tagged summaries (row-statistics tuples or top-K records), row
-// results and, for top-K, the kept-row list. Zeroed when allocated, after
-// which tagged words are only ever told apart by the call epoch in their
-// high half (epoch 0 never occurs; every call takes the next epoch).
+// A scratch area: the waves' tagged summaries (row-statistics tuples or
+// top-K records), row results and, for top-K, the kept-row list. Zero when
+// it comes into use, after which tagged words are only ever told apart by
+// the call epoch in their high half (epoch 0 never occurs; every call takes
+// the next epoch, committed once its launch is queued).
+struct Area {
+  void *base = nullptr;
+  size_t bytes = 0;
+  uint32_t epoch = 0;        // epoch of the last queued call
+  uint32_t *err = nullptr;   // its error words (device)
+};
+
 struct DeviceState {
   bool ready = false;
   int cus = 0;
   int resident[2][3] = {};  // row-stats blocks per CU by [vector path][probs dtype]
   int topk_resident[2] = {};
-  void *row_scratch = nullptr;
-  size_t row_scratch_bytes = 0;
-  uint32_t epoch = 0;       // epoch of the last call
-  uint32_t *err_flag = nullptr;
+  Area grow;                // grow-only, shared by rowstats_run, topk_logprobs and the stash
+  // The stream of the last call on the grow-only scratch; a call on another
+  // stream first waits (on the device) for the work queued there so far.
+  hipStream_t last_stream = nullptr;
+  bool has_last = false;
+  hipEvent_t order_event = nullptr;
 };
 
 std::mutex g_mu;
@@ -66,6 +79,8 @@ __global__ void fill_zero_u32(uint32_t *p, size_t n) {
     p[i] = 0u;
 }
 
+// Zeroes n words with a fill kernel (no memset node, so it also records
+// correctly into a captured graph).
 hipError_t zero_async(uint32_t *p, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   size_t blocks = (n + 255) / 256;
@@ -74,6 +89,9 @@ hipError_t zero_async(uint32_t *p, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Per-device set-up, once per device with it current: occupancy of every
+// kernel variant and the device address of the error words. Allocates
+// nothing.
 int device_state(DeviceState **out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -93,44 +111,71 @@ int device_state(DeviceState **out) {
       e = topk_resident_blocks(vec != 0, &d.topk_resident[vec]);
       if (e != hipSuccess) return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     }
-    e = hipMalloc(&d.err_flag, sizeof(uint32_t));
-    if (e != hipSuccess) return fail_hip(e, "hipMalloc(error flag)");
-    e = hipMemset(d.err_flag, 0, sizeof(uint32_t));
-    if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
+    void *err = nullptr;
+    e = hipGetSymbolAddress(&err, HIP_SYMBOL(err_words));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(error words)");
+    d.grow.err = static_cast<uint32_t *>(err);
     d.ready = true;
   }
   *out = &d;
   return ROWSTATS_OK;
 }
 
-int ensure_row_scratch(DeviceState &d, size_t bytes, hipStream_t s) {
-  if (bytes <= d.row_scratch_bytes) return ROWSTATS_OK;
+int ensure_grow_scratch(DeviceState &d, size_t bytes, hipStream_t s) {
+  Area &a = d.grow;
+  if (bytes <= a.bytes) return ROWSTATS_OK;
   hipError_t e;
-  if (d.row_scratch) {
-    e = hipFree(d.row_scratch);
+  if (a.base) {
+    e = hipFree(a.base);  // waits for the work that may still use it
     if (e != hipSuccess) return fail_hip(e, "hipFree(row scratch)");
-    d.row_scratch = nullptr;
-    d.row_scratch_bytes = 0;
+    a.base = nullptr;
+    a.bytes = 0;
   }
   size_t cap = bytes + bytes / 4;
   cap = (cap + 255) & ~(size_t)255;
-  e = hipMalloc(&d.row_scratch, cap);
+  e = hipMalloc(&a.base, cap);
   if (e != hipSuccess) return fail_hip(e, "hipMalloc(row scratch)");
-  d.row_scratch_bytes = cap;
-  e = zero_async(reinterpret_cast<uint32_t *>(d.row_scratch), cap / 4, s);
+  a.bytes = cap;
+  e = zero_async(reinterpret_cast<uint32_t *>(a.base), cap / 4, s);
   if (e != hipSuccess) return fail_hip(e, "zeroing row scratch");
   return ROWSTATS_OK;
 }
 
-// The epoch of a new call (clearing the scratch when the counter wraps).
-int next_epoch(DeviceState &d, hipStream_t s, uint32_t *epoch) {
-  if (++d.epoch == 0) {
-    // the epoch wrapped: clear every tag it could still match
-    hipError_t e = zero_async(reinterpret_cast<uint32_t *>(d.row_scratch), d.row_scratch_bytes / 4, s);
-    if (e != hipSuccess) return fail_hip(e, "zeroing scratch");
-    d.epoch = 1;
+// The epoch of a new call on area a. When the counter wraps, the area and
+// its failed-epoch word are cleared first, since old tags could match again.
+int next_epoch(Area &a, hipStream_t s, uint32_t *epoch) {
+  uint32_t e = a.epoch + 1;
+  if (e == 0) {
+    hipError_t h = zero_async(reinterpret_cast<uint32_t *>(a.base), a.bytes / 4, s);
+    if (h == hipSuccess) h = zero_async(a.err + 1, 1, s);
+    if (h != hipSuccess) return fail_hip(h, "zeroing scratch");
+    e = 1;
   }
-  *epoch = d.epoch;
+  *epoch = e;
+  return ROWSTATS_OK;
+}
+
+// Orders a call on the grow-only scratch after the last call queued on
+// another stream (they share the scratch and its row-claim counters): the
+// event recorded after every launch on the grow-only scratch.
+int order_after_last(DeviceState &d, hipStream_t s) {
+  if (d.has_last && d.last_stream != s) {
+    hipError_t e = hipStreamWaitEvent(s, d.order_event, 0);
+    if (e != hipSuccess) return fail_hip(e, "waiting for the previous call's stream");
+  }
+  return ROWSTATS_OK;
+}
+
+int note_stream(DeviceState &d, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (!d.order_event) e = hipEventCreateWithFlags(&d.order_event, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(d.order_event, s);
+  if (e != hipSuccess) {
+    d.has_last = false;
+    return fail_hip(e, "recording the call's completion event");
+  }
+  d.last_stream = s;
+  d.has_last = true;
   return ROWSTATS_OK;
 }
 
@@ -178,11 +223,13 @@ int plan_and_launch_topk(DeviceState &d, TopKParams &p, hipStream_t s) {
   const size_t kept_bytes = align16(((size_t)rows + 1) * sizeof(int64_t));
   const size_t dst_bytes = p.stash ? (size_t)rows * sizeof(int64_t) : 0;
   const size_t req_bytes = p.stash ? align16((size_t)rows * sizeof(int32_t)) : 0;
-  int rc = ensure_row_scratch(d, head_bytes + record_bytes + rowres_bytes + temp_bytes +
-                                     kept_bytes + dst_bytes + req_bytes, s);
+  int rc = order_after_last(d, s);
   if (rc) return rc;
-  if ((rc = next_epoch(d, s, &p.epoch))) return rc;
-  char *base = reinterpret_cast<char *>(d.row_scratch);
+  rc = ensure_grow_scratch(d, head_bytes + record_bytes + rowres_bytes + temp_bytes +
+                                  kept_bytes + dst_bytes + req_bytes, s);
+  if (rc) return rc;
+  if ((rc = next_epoch(d.grow, s, &p.epoch))) return rc;
+  char *base = reinterpret_cast<char *>(d.grow.base);
   p.counters = reinterpret_cast<uint32_t *>(base);
   p.rings = reinterpret_cast<uint64_t *>(base + kScratchHead);
   base += head_bytes;
@@ -197,39 +244,22 @@ int plan_and_launch_topk(DeviceState &d, TopKParams &p, hipStream_t s) {
   p.kept_dst = p.stash ? reinterpret_cast<int64_t *>(base) : nullptr;
   base += dst_bytes;
   p.kept_req = p.stash ? reinterpret_cast<int32_t *>(base) : nullptr;
-  p.err_flag = d.err_flag;
+  p.err_flag = d.grow.err;
   hipError_t e = topk_launch(p, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "top-K kernel launch");
-  return ROWSTATS_OK;
+  d.grow.epoch = p.epoch;
+  return note_stream(d, s);
 }
 
-}  // namespace
-
-extern "C" {
-
-const char *rowstats_last_error(void) { return g_last_error.c_str(); }
-
-int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
-                 const float *temps, int64_t canvas_len, uint64_t seed, int probs_dtype,
-                 int64_t *argmax, int64_t *sample, float *entropy, void *probs, void *stream) {
-  g_last_error.clear();
-  if (probs_dtype < ROWSTATS_PROBS_NONE || probs_dtype > ROWSTATS_PROBS_FP16)
-    return fail(ROWSTATS_ERR_DTYPE, "probs_dtype must be 0 (none), 1 (bf16) or 2 (fp16), got %d",
-                probs_dtype);
-  if (rows < 0) return fail(ROWSTATS_ERR_SHAPE, "rows must be >= 0, got %lld", (long long)rows);
-  if (rows == 0) return ROWSTATS_OK;
-  int rc = check_common(logits, row_stride, rows, vocab, temps, canvas_len);
-  if (rc) return rc;
-  if (!argmax || !sample || !entropy) return fail(ROWSTATS_ERR_NULL, "an output pointer is NULL");
-  if (probs_dtype != ROWSTATS_PROBS_NONE && !probs)
-    return fail(ROWSTATS_ERR_NULL, "probs is NULL but probs_dtype asks for probabilities");
-
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceState *d = nullptr;
-  if ((rc = device_state(&d))) return rc;
-
-  RowStatsParams p = {};
+// Checks and launch plan of a row-statistics call: fills p except the
+// scratch pointers and the epoch, and returns the grid and the scratch
+// bytes the call needs.
+int plan_rowstats(const DeviceState &d, const float *logits, int64_t row_stride, int64_t rows,
+                  int64_t vocab, const float *temps, int64_t canvas_len, uint64_t seed,
+                  int probs_dtype, int64_t *argmax, int64_t *sample, float *entropy, void *probs,
+                  RowStatsParams &p, int64_t *grid, size_t *need, size_t *head_bytes,
+                  size_t *tuple_bytes) {
+  p = RowStatsParams{};
   p.logits = logits;
   p.ld = row_stride;
   p.rows = rows;
@@ -250,7 +280,7 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
   // of a row's group keep their chunks in registers until the row is
   // merged, so a group must fit.
   constexpr int kWavesPerBlock = kRowThreads / 64;
-  const int64_t waves = (int64_t)d->resident[p.vec_ok][probs_dtype] * d->cus * kWavesPerBlock;
+  const int64_t waves = (int64_t)d.resident[p.vec_ok][probs_dtype] * d.cus * kWavesPerBlock;
   if (waves < 1) return fail(ROWSTATS_ERR_HIP, "row-stats kernel cannot be resident");
   if (p.C > waves)
     return fail(ROWSTATS_ERR_COOP,
@@ -259,22 +289,73 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
   int64_t groups = waves / p.C;
   if (groups > rows) groups = rows;
   p.n_groups = (int32_t)groups;
-  const int64_t grid = (groups * p.C + kWavesPerBlock - 1) / kWavesPerBlock;
+  *grid = (groups * p.C + kWavesPerBlock - 1) / kWavesPerBlock;
+  *head_bytes = kScratchHead + (size_t)groups * kRingBytes;
+  *tuple_bytes = (size_t)rows * p.C * kTupleBytes;
+  *need = *head_bytes + *tuple_bytes + (size_t)rows * kRowResultBytes;
+  return ROWSTATS_OK;
+}
 
-  const size_t head_bytes = kScratchHead + (size_t)groups * kRingBytes;
-  const size_t tuple_bytes = (size_t)rows * p.C * kTupleBytes;
-  const size_t rowres_bytes = (size_t)rows * kRowResultBytes;
-  if ((rc = ensure_row_scratch(*d, head_bytes + tuple_bytes + rowres_bytes, s))) return rc;
-  if ((rc = next_epoch(*d, s, &p.epoch))) return rc;
-  char *base = reinterpret_cast<char *>(d->row_scratch);
+// Argument checks of rowstats_run that need no device.
+int check_rowstats_args(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
+                        const float *temps, int64_t canvas_len, int probs_dtype,
+                        const int64_t *argmax, const int64_t *sample, const float *entropy,
+                        const void *probs) {
+  if (probs_dtype < ROWSTATS_PROBS_NONE || probs_dtype > ROWSTATS_PROBS_FP16)
+    return fail(ROWSTATS_ERR_DTYPE, "probs_dtype must be 0 (none), 1 (bf16) or 2 (fp16), got %d",
+                probs_dtype);
+  if (rows < 0) return fail(ROWSTATS_ERR_SHAPE, "rows must be >= 0, got %lld", (long long)rows);
+  if (rows == 0) return ROWSTATS_OK;
+  int rc = check_common(logits, row_stride, rows, vocab, temps, canvas_len);
+  if (rc) return rc;
+  if (!argmax || !sample || !entropy) return fail(ROWSTATS_ERR_NULL, "an output pointer is NULL");
+  if (probs_dtype != ROWSTATS_PROBS_NONE && !probs)
+    return fail(ROWSTATS_ERR_NULL, "probs is NULL but probs_dtype asks for probabilities");
+  return ROWSTATS_OK;
+}
+
+void set_scratch(RowStatsParams &p, const Area &a, size_t head_bytes, size_t tuple_bytes) {
+  char *base = reinterpret_cast<char *>(a.base);
   p.counters = reinterpret_cast<uint32_t *>(base);
   p.rings = reinterpret_cast<uint64_t *>(base + kScratchHead);
   p.tuples = reinterpret_cast<uint64_t *>(base + head_bytes);
   p.rowres = reinterpret_cast<uint64_t *>(base + head_bytes + tuple_bytes);
-  p.err_flag = d->err_flag;
+  p.err_flag = a.err;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rowstats_last_error(void) { return g_last_error.c_str(); }
+
+int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
+                 const float *temps, int64_t canvas_len, uint64_t seed, int probs_dtype,
+                 int64_t *argmax, int64_t *sample, float *entropy, void *probs, void *stream) {
+  g_last_error.clear();
+  int rc = check_rowstats_args(logits, row_stride, rows, vocab, temps, canvas_len, probs_dtype,
+                               argmax, sample, entropy, probs);
+  if (rc || rows == 0) return rc;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState *d = nullptr;
+  if ((rc = device_state(&d))) return rc;
+  RowStatsParams p;
+  int64_t grid = 0;
+  size_t need = 0, head_bytes = 0, tuple_bytes = 0;
+  if ((rc = plan_rowstats(*d, logits, row_stride, rows, vocab, temps, canvas_len, seed, probs_dtype,
+                          argmax, sample, entropy, probs, p, &grid, &need, &head_bytes,
+                          &tuple_bytes)))
+    return rc;
+  if ((rc = order_after_last(*d, s))) return rc;
+  if ((rc = ensure_grow_scratch(*d, need, s))) return rc;
+  if ((rc = next_epoch(d->grow, s, &p.epoch))) return rc;
+  set_scratch(p, d->grow, head_bytes, tuple_bytes);
   hipError_t e = rowstats_launch(p, probs_dtype, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
-  return ROWSTATS_OK;
+  d->grow.epoch = p.epoch;
+  return note_stream(*d, s);
 }
 
 int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
@@ -403,11 +484,17 @@ int rowstats_check_device(void *stream) {
   int rc = device_state(&d);
   if (rc) return rc;
   uint32_t flag = 0;
-  e = hipMemcpy(&flag, d->err_flag, sizeof flag, hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return fail_hip(e, "hipMemcpy(error flag)");
+  for (Area *a : {&d->grow}) {
+    uint32_t f = 0;
+    e = hipMemcpy(&f, a->err, sizeof f, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpy(error flag)");
+    if (f != 0) {
+      e = hipMemset(a->err, 0, sizeof(uint32_t));
+      if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
+    }
+    flag |= f;
+  }
   if (flag == 0) return ROWSTATS_OK;
-  e = hipMemset(d->err_flag, 0, sizeof(uint32_t));
-  if (e != hipSuccess) return fail_hip(e, "hipMemset(error flag)");
   return fail(ROWSTATS_ERR_DEVICE, "a kernel flagged %s (flag %u)",
               (flag & kErrWait) ? "an inter-workgroup wait that ran out"
                                 : "a stash index out of range (request or token id skipped)",
@@ -422,11 +509,17 @@ int rowstats_release(void) {
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
   for (int dev = 0; dev < kMaxDevices; ++dev) {
     DeviceState &d = g_dev[dev];
-    if (!d.ready) continue;
+    if (!d.ready || (!d.grow.base && !d.order_event)) continue;
     if ((e = hipSetDevice(dev)) != hipSuccess) return fail_hip(e, "hipSetDevice");
-    if (d.row_scratch) (void)hipFree(d.row_scratch);
-    if (d.err_flag) (void)hipFree(d.err_flag);
-    d = DeviceState();
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+    if (d.grow.base) (void)hipFree(d.grow.base);
+    if (d.order_event) (void)hipEventDestroy(d.order_event);
+    // the next call on the grow-only scratch allocates it afresh (zeroed);
+    // the epoch keeps counting
+    d.grow.base = nullptr;
+    d.grow.bytes = 0;
+    d.order_event = nullptr;
+    d.has_last = false;
   }
   if ((e = hipSetDevice(cur)) != hipSuccess) return fail_hip(e, "hipSetDevice");
   return ROWSTATS_OK;

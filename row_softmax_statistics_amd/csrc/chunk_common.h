@@ -18,7 +18,7 @@ constexpr int kQ = kWaveQuads;
 // is bypassed and the access is coherent across XCDs).
 constexpr int kDevScope = 16;
 // Polls of one wait before it gives up and flags the call (about a second);
-// once any wait has given up, every later wait of the call gives up at once.
+// once any wait of a call has given up, its later waits give up at once.
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 typedef __attribute__((address_space(3))) void *LdsPtr;
@@ -121,11 +121,6 @@ __device__ __forceinline__ void chunk_copy_bytes(float4 *buf, const float *src, 
 #undef ROWSTATS_DMA
 }
 
-__device__ __forceinline__ void chunk_copy_async(float4 *buf, const float *xrow, int32_t c0,
-                                                 int32_t V) {
-  chunk_copy_bytes(buf, xrow + c0, chunk_bytes(c0, V));
-}
-
 // Scalar path (unaligned rows or vocab % 4 != 0): four 4-byte loads a quad.
 __device__ __forceinline__ void chunk_load(float4 (&v)[kQ], const float *xrow, int32_t c0,
                                            int32_t V) {
@@ -196,22 +191,13 @@ __device__ __forceinline__ T kernel_arg_at(uint32_t offset) {
 #define LATE_ARG(Params, field) \
   kernel_arg_at<decltype(Params::field)>((uint32_t)offsetof(Params, field))
 
-// cm = 2 cm + (a >= b): the compare writes VCC and the add takes it as the
-// carry in (the compiler would spend a select and a shift instead). A carry
-// or mask read of a compare's result needs two wait states after the
-// compare on gfx950; the compiler adds them to its own code but not inside
-// inline assembly, hence the s_nop.
-__device__ __forceinline__ uint32_t push_bit_ge(uint32_t cm, float a, float b) {
-  __asm__("v_cmp_ge_f32 vcc, %1, %2\n\ts_nop 1\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
-          : "+v"(cm)
-          : "v"(a), "v"(b)
-          : "vcc");
-  return cm;
-}
-
-// Four such pushes (a0 first). The compares write VCC and two scalar
-// register pairs in turn, so that every add reads a result written at least
-// two instructions before it: no wait states are needed.
+// cm = 2 cm + (a >= b), four times (a0 first): each compare writes VCC or a
+// scalar register pair and an add takes it as the carry in (the compiler
+// would spend a select and a shift instead). A carry or mask read of a
+// compare's result needs two wait states after the compare on gfx950; the
+// compiler adds them to its own code but not inside inline assembly, so the
+// compares write VCC and two scalar register pairs in turn and every add
+// reads a result written at least two instructions before it.
 __device__ __forceinline__ uint32_t push4_bits_ge(uint32_t cm, float a0, float a1, float a2,
                                                   float a3, float b0, float b1, float b2,
                                                   float b3) {
@@ -272,10 +258,17 @@ __device__ __forceinline__ bool row_result_ready(const u32x4 &v, uint32_t epoch)
   return ((v[1] == epoch) & (v[3] == epoch)) != 0;
 }
 
-// Whether some wait of this call has already given up (bit 0 of the error
-// flag; other bits report bad arguments and do not stop the waits).
-__device__ __forceinline__ bool call_failed(const uint32_t *err_flag) {
-  return (__hip_atomic_load(err_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u) != 0u;
+// Error words of a scratch area: err[0] collects report bits over calls
+// (cleared by rowstats_check_device), err[1] holds the epoch of the last
+// call whose bounded wait gave up. Once one wait of a call has given up,
+// the call's other waits give up at once; the next call (a new epoch) waits
+// normally again.
+__device__ __forceinline__ bool call_failed(const uint32_t *err, uint32_t epoch) {
+  return __hip_atomic_load(err + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+}
+__device__ __forceinline__ void give_up(uint32_t *err, uint32_t epoch) {
+  atomicOr(err, kErrWait);
+  __hip_atomic_store(err + 1, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Waits until the row result of `row` (pre-loaded in v) shows `epoch`;
@@ -289,8 +282,8 @@ __device__ __forceinline__ u32x4 wait_row_result(uint64_t *rowres, int64_t row, 
     do {
       __builtin_amdgcn_s_sleep(1);
       v = load_row_result(rowres, row);
-    } while (!row_result_ready(v, epoch) && ++spins <= kSpinLimit && !call_failed(err_flag));
-    if (!row_result_ready(v, epoch) && lane_id() == 0) atomicOr(err_flag, 1u);
+    } while (!row_result_ready(v, epoch) && ++spins <= kSpinLimit && !call_failed(err_flag, epoch));
+    if (!row_result_ready(v, epoch) && lane_id() == 0) give_up(err_flag, epoch);
   }
   return v;
 }
@@ -335,9 +328,9 @@ struct RowDealer {
       do {
         __builtin_amdgcn_s_sleep(1);
         w = load_slot(n);
-      } while (!slot_ready(w, n) && ++spins <= kSpinLimit && !call_failed(err_flag));
+      } while (!slot_ready(w, n) && ++spins <= kSpinLimit && !call_failed(err_flag, epoch));
       if (!slot_ready(w, n)) {
-        if (lane_id() == 0) atomicOr(err_flag, 1u);
+        if (lane_id() == 0) give_up(err_flag, epoch);
         return -1;
       }
     }

@@ -90,17 +90,48 @@ __device__ __forceinline__ uint32_t pick(const uint4 &w, int i) {
 }
 
 // ---------------------------------------------------------------------------
-// Temperature: T <= 0 (and NaN-free T below 1e-10) clamps to 1e-10f.
-// s = fl32(x / Tc) is computed as fl32((double)x * fl64(1 / Tc)): the double
-// product is within 2^-52 (relative) of x / Tc, while x / Tc is never within
-// 2^-49 of a midpoint between two fp32 values unless it equals one, and it
-// can equal one only if x / Tc needs 25 significant bits, which two 24-bit
-// operands cannot produce. So the final rounding is the IEEE quotient.
+// Temperature: T <= 0 (and NaN-free T below 1e-10) clamps to 1e-10f, and
+// s = fl32(x / Tc), the IEEE fp32 quotient.
+//
+// Fast form: s = fl32(P), P = fl64(x * fl64(1 / Tc)) = q (1 + d) with
+// q = x / Tc and |d| < 2^-51.99. Write Tc = t 2^(f-23), t < 2^24 an integer.
+//  * Normal results, q in [2^e, 2^(e+1)), e >= -126: a midpoint between two
+//    fp32 values there is mid = (2M + 1) 2^(e-24) with 2M + 1 >= 2^24 + 1, so
+//    mid Tc has more than 24 significant bits and is not x. x - mid Tc is then
+//    a nonzero multiple of 2^(e+f-47), so |q - mid| > 2^(e-48) > |P - q|:
+//    fl32(P) is the IEEE quotient, for every Tc.
+//  * Subnormal results (|q| < 2^-126; midpoints n 2^-150, n odd) that are not
+//    midpoints: x - mid Tc is a nonzero multiple of 2^min(-149, f-173), so
+//    |q - mid| > 2^min(-150-f, -174) > 2^-177.99 > |P - q| when Tc < 2.
+//  * A subnormal quotient equal to a midpoint n 2^-150 needs x = n 2^-150 Tc
+//    to be a multiple of 2^-149, i.e. Tc = (odd) 2^k with k >= 1: Tc >= 2. It
+//    happens there: x = 147 2^-149 and T = 98 give the midpoint 3 2^-150,
+//    which rounds to the even 2^-148, while fl32(P) gives 2^-149.
+// So scale() is exact for every x when Tc < 2; rows with Tc >= 2 take
+// scale_checked.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float clamp_temp(float t) { return t > 1e-10f ? t : 1e-10f; }
 
 __device__ __forceinline__ float scale(float x, double rtc) {
   return (float)((double)x * rtc);
+}
+
+// Rows with Tc >= 2: a result at or below 2^-126 in magnitude (the true
+// quotient is then subnormal, or 2^-126 itself) is recomputed with an fp64
+// division. Its rounding is exact there: a midpoint n 2^-150 is an fp64
+// value, so fl64(q) = q and the fp32 conversion breaks the tie to even; any
+// other q lies more than min(2^-174, 2^-25 q) from every midpoint, while
+// |fl64(q) - q| <= 2^-53 q. Normal results keep the fast form (exact by the
+// first case above, for any Tc).
+__device__ __forceinline__ float scale_checked(float x, double rtc, float tc) {
+  const float s = (float)((double)x * rtc);
+  return fabsf(s) <= 0x1p-126f ? (float)((double)x / (double)tc) : s;
+}
+
+// Scale for a row whose clamped temperature is tc (any tc): the fast form
+// below 2, the checked one from 2 on.
+__device__ __forceinline__ float scale_any(float x, double rtc, float tc) {
+  return tc < 2.0f ? scale(x, rtc) : scale_checked(x, rtc, tc);
 }
 
 // Order-preserving int32 of the fp32 bits (after +0.0f so that -0 == +0).
@@ -160,134 +191,14 @@ __device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
                                            kRsrcWord3);
 }
 
-// Column of element (j, i) of thread t in a slice starting at quad q0:
-// 4 * (q0 + j * NT + t) + i. Element k = 4 j + i is a compile-time index.
-template <int NT>
-__device__ __forceinline__ int32_t slice_col(int32_t q0, int k) {
-  return 4 * (q0 + (k >> 2) * NT + (int32_t)threadIdx.x) + (k & 3);
-}
-
-// ---------------------------------------------------------------------------
-// Slice loads. Thread t of an NT-thread workgroup holds quads q0 + j NT + t
-// (j < QPT): each load instruction of a wave covers 1 KiB of contiguous
-// logits. VEC (row base 16-byte aligned, vocab % 4 == 0) moves 16 bytes per
-// quad, otherwise four 4-byte loads. Columns past the row end read as 0 and
-// are set to -inf by scale_slice.
-// ---------------------------------------------------------------------------
-template <int QPT, int NT>
-__device__ __forceinline__ Rsrc slice_rsrc(const float *xrow, int32_t q0, int32_t V) {
-  const int32_t left = V - 4 * q0;  // valid columns from the slice start (> 0)
-  return make_rsrc(xrow + 4 * q0, 4u * (uint32_t)min(left, 4 * NT * QPT));
-}
-
-template <int QPT, int NT, bool VEC>
-__device__ __forceinline__ void load_slice(const float *xrow, int32_t q0, int32_t V,
-                                           float4 (&v)[QPT]) {
-  const Rsrc r = slice_rsrc<QPT, NT>(xrow, q0, V);
-  const uint32_t voff = 16u * threadIdx.x;
-  if constexpr (VEC) {
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 16 * j * NT, 0);
-      v[j] = make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]),
-                         __uint_as_float(t[3]));
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < QPT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        set_comp(v[j], i,
-                 __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 16 * j * NT + 4 * i, 0)));
-  }
-}
-
-// Asynchronous copy of a slice (VEC layout) into an LDS stage of NT * QPT
-// quads laid out like the registers: quad j of thread t at stage[j NT + t].
-// Waves 1..NW-1 issue all the copies (wave 0 keeps its memory queue free for
-// latency-critical work: waits on it would otherwise also wait for the
-// in-order copies). Before reading, every copying wave waits for its copies
-// (stage_wait) and the workgroup synchronises.
-template <int QPT, int NT>
-__device__ __forceinline__ void stage_slice_async(float4 *stage, const float *xrow, int32_t q0,
-                                                  int32_t V) {
-  constexpr int NW = NT / 64;
-  const int wave = threadIdx.x / 64;
-  if (wave == 0) return;
-  const Rsrc r = slice_rsrc<QPT, NT>(xrow, q0, V);
-  const uint32_t voff = 16u * (threadIdx.x & 63);
-  for (int n = wave - 1; n < QPT * NW; n += NW - 1) {
-    const int off = (n / NW) * NT + (n % NW) * 64;  // quad offset of 64 lanes
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)(stage + off), 16, voff, 16 * off, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void stage_wait() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-}
-
-template <int QPT, int NT>
-__device__ __forceinline__ void read_stage(const float4 *stage, float4 (&v)[QPT]) {
-#pragma unroll
-  for (int j = 0; j < QPT; ++j) v[j] = stage[j * NT + threadIdx.x];
-}
-
 // Scalar (uniform-address) load through the constant address space.
 __device__ __forceinline__ float load_uniform(const float *p) {
   return *(const __attribute__((address_space(4))) float *)p;
 }
 
-// Masks columns past the row end to -inf and scales s = fl32(x / Tc).
-// Returns the thread's maximum of s.
-template <int QPT, int NT>
-__device__ __forceinline__ float scale_slice(float4 (&v)[QPT], int32_t q0, int32_t V,
-                                             double rtc) {
-  const int32_t left = V - 4 * q0;
-  if (left < 4 * NT * QPT) {  // the slice runs past the row end
-    const int32_t tcol = 4 * (int32_t)threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < QPT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        set_comp(v[j], i, (tcol + 4 * j * NT + i < left) ? comp(v[j], i) : -INFINITY);
-  }
-  float mt = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    v[j].x = scale(v[j].x, rtc);
-    v[j].y = scale(v[j].y, rtc);
-    v[j].z = scale(v[j].z, rtc);
-    v[j].w = scale(v[j].w, rtc);
-    mt = fmaxf(mt, max4(v[j]));
-  }
-  return mt;
-}
-
-template <int QPT, int NT, bool VEC>
-__device__ __forceinline__ float load_scaled_slice(const float *xrow, int32_t q0, int32_t V,
-                                                   double rtc, float4 (&v)[QPT]) {
-  load_slice<QPT, NT, VEC>(xrow, q0, V, v);
-  return scale_slice<QPT, NT>(v, q0, V, rtc);
-}
-
-// One logit of the slice (for rare re-reads), column c = 4 * q0 + cl.
-__device__ __forceinline__ float load_one(const float *xrow, int32_t q0, int32_t cl) {
-  return xrow[4 * (int64_t)q0 + cl];
-}
-
 // ---------------------------------------------------------------------------
 // Rounding to the probs dtypes. p is finite and >= 0.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t bf16_rne_bits(float p) {
-  const uint32_t b = __float_as_uint(p);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ uint32_t fp16_rne_bits(float p) {
-  // fp32 -> fp16 conversion rounds to nearest-even; fp16 denormals are kept
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p);
-}
-
 // Two values rounded to nearest-even and packed (a in the low half), with
 // one gfx950 conversion instruction (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32;
 // round-to-nearest-even is the default rounding mode, denormals are kept).
@@ -387,7 +298,6 @@ __device__ __forceinline__ T wave_allreduce(T v, Op op) {
   return group_allreduce<64>(v, op);
 }
 
-struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
 struct MaxI { __device__ int32_t operator()(int32_t a, int32_t b) const { return a > b ? a : b; } };
 struct MinI { __device__ int32_t operator()(int32_t a, int32_t b) const { return a < b ? a : b; } };
 struct SumF { __device__ float operator()(float a, float b) const { return a + b; } };
@@ -403,20 +313,6 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   const int32_t b = __float_as_int(v);
   const int32_t k = wave_allreduce(b ^ ((b >> 31) & 0x7FFFFFFF), MaxI());
   return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
-}
-
-// Workgroup-wide reductions through one LDS slot per wave.
-template <int NT, class T, class Op>
-__device__ __forceinline__ T block_allreduce(T v, Op op, T *lds) {
-  v = wave_allreduce(v, op);
-  const int wave = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) lds[wave] = v;
-  __syncthreads();
-  T r = lds[0];
-#pragma unroll
-  for (int w = 1; w < (NT / kWave); ++w) r = op(r, lds[w]);
-  __syncthreads();
-  return r;
 }
 
 }  // namespace rowstats

@@ -1,10 +1,8 @@
-// Inline fp64 log and exp for the few exact scores a slice needs (Gumbel
-// values of candidate columns, merges of partial sums), written from their
-// series definitions:
+// Inline fp64 log for the few exact scores a chunk needs (Gumbel values of
+// candidate columns) and the row entropies, written from its series:
 //   log x = k ln2 + 2 atanh(s),  x = m 2^k, m in [sqrt(1/2), sqrt(2)),
 //           s = (m - 1) / (m + 1), atanh s = s + s^3/3 + s^5/5 + ...
-//   exp x = 2^k exp(r),          k = rint(x / ln2), r = x - k ln2, |r| <= ln2/2
-// Both are accurate to a few fp64 ulps, far below what any comparison here
+// It is accurate to a few fp64 ulps, far below what any comparison here
 // needs. The coefficients are read through a pointer the compiler cannot see
 // through, so they are loaded at the point of use (scalar loads) instead of
 // being kept in registers across the kernels' loops.
@@ -17,21 +15,15 @@ namespace rowstats {
 
 struct MathTable {
   double inv_odd[12];   // 1 / (2 i + 3), i = 0..11
-  double inv_fact[15];  // 1 / n!, n = 0..14
   double ln2_hi;        // ln 2 to 32 significant bits: k * ln2_hi is exact
   double ln2_lo;        // ln 2 - ln2_hi
-  double inv_ln2;
 };
 
 __constant__ const MathTable kMath = {
     {1.0 / 3, 1.0 / 5, 1.0 / 7, 1.0 / 9, 1.0 / 11, 1.0 / 13, 1.0 / 15, 1.0 / 17, 1.0 / 19,
      1.0 / 21, 1.0 / 23, 1.0 / 25},
-    {1.0, 1.0, 1.0 / 2, 1.0 / 6, 1.0 / 24, 1.0 / 120, 1.0 / 720, 1.0 / 5040, 1.0 / 40320,
-     1.0 / 362880, 1.0 / 3628800, 1.0 / 39916800, 1.0 / 479001600, 1.0 / 6227020800.0,
-     1.0 / 87178291200.0},
     0x1.62e42fee00000p-1,
     0x1.a39ef35793c76p-33,
-    0x1.71547652b82fep+0,
 };
 
 typedef const __attribute__((address_space(4))) MathTable *MathTablePtr;
@@ -67,19 +59,6 @@ __device__ __forceinline__ double log_d(double x) {
   const double lm = fma(ts * s2, p, ts);
   const double kd = (double)k;
   return fma(kd, T->ln2_hi, fma(kd, T->ln2_lo, lm));
-}
-
-// exp of x; underflows to 0 below about -745.
-__device__ __forceinline__ double exp_d(double x) {
-  MathTablePtr T = math_table();
-  if (x < -745.2) return 0.0;
-  const double k = rint(x * T->inv_ln2);
-  double r = fma(-k, T->ln2_hi, x);
-  r = fma(-k, T->ln2_lo, r);
-  double e = T->inv_fact[14];
-#pragma unroll
-  for (int n = 13; n >= 0; --n) e = fma(e, r, T->inv_fact[n]);
-  return ldexp(e, (int)k);
 }
 
 // Standard Gumbel variate of a 32-bit word: u = (w + 0.5) 2^-32 lies in

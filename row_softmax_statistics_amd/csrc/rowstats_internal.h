@@ -26,6 +26,12 @@ constexpr int kDealAhead = 8;
 constexpr int kRingSlots = 16;
 constexpr int kRingBytes = 16 * kRingSlots;
 
+// Report bits of a scratch area's first error word: a bounded wait ran out
+// (the call's other waits then give up too), and an index argument of the
+// stash was out of range (that request or token id is skipped).
+constexpr uint32_t kErrWait = 1u;
+constexpr uint32_t kErrIndex = 2u;
+
 struct RowStatsParams {
   const float *logits;
   int64_t ld;
@@ -49,7 +55,7 @@ struct RowStatsParams {
   uint64_t *rings;    // [n_groups] rings of rows (RowDealer)
   uint32_t *counters; // two row-claim counters: a call uses counters[epoch & 1]
                       // and zeroes counters[(epoch + 1) & 1] for the next call
-  uint32_t *err_flag;
+  uint32_t *err_flag;  // the scratch's error words: {report bits, failed epoch}
 };
 
 // Multiplier and shift with floor(n / d) = (n * mul) >> shift for every

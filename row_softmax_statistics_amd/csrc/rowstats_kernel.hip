@@ -190,8 +190,8 @@ __device__ __forceinline__ void write_row_outputs(const RowStatsParams &p, int64
 // Exact perturbed score of column c of `row`: s from the raw logit (re-read
 // from HBM), g in fp64.
 __device__ __forceinline__ double exact_score(const RowStatsParams &p, int64_t row, double rtc,
-                                              int32_t c) {
-  const float s = scale(p.logits[row * p.ld + c], rtc);
+                                              float tc, int32_t c) {
+  const float s = scale_any(p.logits[row * p.ld + c], rtc, tc);
   const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, (uint32_t)(uint64_t)row,
                                 (uint32_t)((uint64_t)row >> 32), (uint32_t)p.seed,
                                 (uint32_t)(p.seed >> 32));
@@ -216,8 +216,8 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
     uint32_t spins = 0;
     while (!read_tuple(r, i, p.epoch, t)) {
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit || call_failed(p.err_flag)) {
-        atomicOr(p.err_flag, 1u);
+      if (++spins > kSpinLimit || call_failed(p.err_flag, p.epoch)) {
+        give_up(p.err_flag, p.epoch);
         break;
       }
     }
@@ -241,11 +241,12 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
     if (__popcll(near) == 1 && __ballot(b2 >= zcut) == 0) {
       m.zc = __builtin_amdgcn_readlane(c1, __builtin_ctzll(near));
     } else {
-      const double rtc = 1.0 / (double)clamp_temp(T);
+      const float tc = clamp_temp(T);
+      const double rtc = 1.0 / (double)tc;
       double bz = -INFINITY;
       int32_t bc = INT_MAX;
       auto consider = [&](double zrep, int32_t c, int32_t zx) {
-        const double z = zx ? zrep : exact_score(p, row, rtc, c);
+        const double z = zx ? zrep : exact_score(p, row, rtc, tc, c);
         if (z > bz || (z == bz && c < bc)) {
           bz = z;
           bc = c;
@@ -289,7 +290,8 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   const int32_t V = p.vocab;
   const float T = load_uniform(p.temps + slot_of(p, row));
   const bool greedy = !(T > 0.0f);
-  const double rtc = 1.0 / (double)clamp_temp(T);
+  const float tc = clamp_temp(T);
+  const double rtc = 1.0 / (double)tc;
   const int32_t c0 = chunk * kChunkCols;
   // column of element k = 4 j + i of this lane
   auto col_of = [&](int k) -> int32_t { return c0 + 4 * ((k >> 2) * kWave + lane) + (k & 3); };
@@ -311,13 +313,22 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   if (T == 1.0f) {  // x / 1 = x
 #pragma unroll
     for (int j = 0; j < kQ; ++j) mt = fmaxf(mt, max4(v[j]));
-  } else {
+  } else if (tc < 2.0f) {
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
       v[j].x = scale(v[j].x, rtc);
       v[j].y = scale(v[j].y, rtc);
       v[j].z = scale(v[j].z, rtc);
       v[j].w = scale(v[j].w, rtc);
+      mt = fmaxf(mt, max4(v[j]));
+    }
+  } else {  // subnormal quotients may be midpoints (device_common.h)
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      v[j].x = scale_checked(v[j].x, rtc, tc);
+      v[j].y = scale_checked(v[j].y, rtc, tc);
+      v[j].z = scale_checked(v[j].z, rtc, tc);
+      v[j].w = scale_checked(v[j].w, rtc, tc);
       mt = fmaxf(mt, max4(v[j]));
     }
   }
@@ -492,7 +503,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
       int32_t bc = INT_MAX;
       auto score_exact = [&](int32_t c) {
         if (c < V) {
-          const double z = exact_score(p, row, rtc, c);
+          const double z = exact_score(p, row, rtc, tc, c);
           if (z > bz || (z == bz && c < bc)) {
             bz = z;
             bc = c;
@@ -530,7 +541,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
           if constexpr (LDSX) x = lds_read_f32(xbuf, 4 * lane_here() + k);
           else x = p.logits[row * p.ld + c0 + 4 * lane_here() + k];
         }
-        const float s = (T == 1.0f || x == -INFINITY) ? x : scale(x, rtc);
+        const float s = (T == 1.0f || x == -INFINITY) ? x : scale_any(x, rtc, tc);
         Wt = fmaf(comp(v[j], i), fmaxf(s - mu, -FLT_MAX), Wt);
       }
     Ww = wave_allreduce(Wt, SumF());

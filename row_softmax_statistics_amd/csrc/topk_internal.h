@@ -38,7 +38,7 @@ struct TopKParams {
   uint64_t *rings;    // [n_groups] rings of kept positions (RowDealer)
   uint32_t *counters; // two row-claim counters: a call uses counters[epoch & 1]
                       // (the pre-pass zeroes both)
-  uint32_t *err_flag;
+  uint32_t *err_flag;  // the scratch's error words: {report bits, failed epoch}
 
   // Stash mode (stash != 0): rows come from requests instead of slots and
   // each kept row is written as one stash row.
@@ -62,12 +62,6 @@ struct TopKParams {
   int64_t *kept_dst;     // [rows]: stash row slots[j] * positions + p of kept row i
   int32_t *kept_req;     // [rows]: request j of kept row i
 };
-
-// Bits of the error flag: a bounded wait ran out (the call's waits then give
-// up), and an index argument of the stash was out of range (that request or
-// token id is skipped).
-constexpr uint32_t kErrWait = 1u;
-constexpr uint32_t kErrIndex = 2u;
 
 hipError_t topk_resident_blocks(bool vec, int *blocks_per_cu);
 // Queues the kept-row pre-pass and the top-K kernel (cooperative) on `stream`.

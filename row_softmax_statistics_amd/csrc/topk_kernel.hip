@@ -88,8 +88,8 @@ __device__ __forceinline__ u32x4 poll_words(Rsrc r, uint32_t off, uint32_t epoch
   do {
     __builtin_amdgcn_s_sleep(1);
     w = load_words(r, off);
-  } while (!words_ready(w, epoch) && ++spins <= kSpinLimit && !call_failed(err_flag));
-  if (!words_ready(w, epoch)) atomicOr(err_flag, 1u);
+  } while (!words_ready(w, epoch) && ++spins <= kSpinLimit && !call_failed(err_flag, epoch));
+  if (!words_ready(w, epoch)) give_up(err_flag, epoch);
   return w;
 }
 
@@ -170,7 +170,8 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, 
   const int lane = lane_id();
   const int32_t V = p.vocab;
   const int K = p.K;
-  const double rtc = 1.0 / (double)clamp_temp(T);
+  const float tc = clamp_temp(T);
+  const double rtc = 1.0 / (double)tc;
   const int32_t c0 = chunk * kChunkCols;
   // column of element 0 of this lane. The columns are the same for every
   // row of this wave: without this the compiler computes the fallback's
@@ -198,13 +199,22 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, 
   if (T == 1.0f) {  // x / 1 = x
 #pragma unroll
     for (int j = 0; j < kQ; ++j) mt = fmaxf(mt, max4(v[j]));
-  } else {
+  } else if (tc < 2.0f) {
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
       v[j].x = scale(v[j].x, rtc);
       v[j].y = scale(v[j].y, rtc);
       v[j].z = scale(v[j].z, rtc);
       v[j].w = scale(v[j].w, rtc);
+      mt = fmaxf(mt, max4(v[j]));
+    }
+  } else {  // subnormal quotients may be midpoints (device_common.h)
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      v[j].x = scale_checked(v[j].x, rtc, tc);
+      v[j].y = scale_checked(v[j].y, rtc, tc);
+      v[j].z = scale_checked(v[j].z, rtc, tc);
+      v[j].w = scale_checked(v[j].w, rtc, tc);
       mt = fmaxf(mt, max4(v[j]));
     }
   }
@@ -294,10 +304,11 @@ __device__ __forceinline__ int32_t load_uniform_i32(const int32_t *p) {
 // Columns of the row whose scaled value reaches M (its maximum): one pass
 // over the row by the merger, for rows whose K largest keys all tie at M.
 __device__ __forceinline__ int count_at_max(const TopKParams &p, int64_t row, float T, float M) {
-  const double rtc = 1.0 / (double)clamp_temp(T);
+  const float tc = clamp_temp(T);
+  const double rtc = 1.0 / (double)tc;
   const float *x = p.logits + row * p.ld;
   int cnt = 0;
-  for (int32_t c = lane_here(); c < p.vocab; c += kWave) cnt += scale(x[c], rtc) >= M ? 1 : 0;
+  for (int32_t c = lane_here(); c < p.vocab; c += kWave) cnt += scale_any(x[c], rtc, tc) >= M ? 1 : 0;
   return wave_allreduce(cnt, SumI());
 }
 
@@ -340,12 +351,13 @@ __device__ __forceinline__ void write_stash_row(const TopKParams &p, int64_t pos
     LATE_ARG(TopKParams, out_ranks)[dst] = ties;
   }
   if (by_ids) {
-    const double rtc = 1.0 / (double)clamp_temp(T);
+    const float tc = clamp_temp(T);
+    const double rtc = 1.0 / (double)tc;
     const int32_t *idr = ids + (int64_t)j * ids_stride;
     for (int i = lane; i < n; i += kWave) {
       const int32_t id = idr[i];
       float v = -INFINITY;
-      if (id >= 0 && id < p.vocab) v = value(scale(p.logits[row * p.ld + id], rtc));
+      if (id >= 0 && id < p.vocab) v = value(scale_any(p.logits[row * p.ld + id], rtc, tc));
       else atomicOr(p.err_flag, kErrIndex);
       oid[1 + i] = id;
       olp[1 + i] = v;

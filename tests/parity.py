@@ -4,12 +4,22 @@ the same rows and compare them to the bar each output has.
 Tolerances (derived in the design notes from the arithmetic of both sides):
   argmax, top-K indices        bit-exact
   sample                       exact, except rows whose oracle top-two
-                               perturbed scores are within 1e-6 (counted)
+                               perturbed scores are within 1e-6; there the
+                               GPU's column must itself score within 1e-6 of
+                               the best (its exact score is recomputed from
+                               the oracle's scale, noise word and Gumbel map),
+                               and such rows are counted and recorded
   entropy                      |gpu - oracle| <= 1e-4
   probs (bf16 / fp16)          at most 1 unit in the last place
   top-K logprobs               |gpu - oracle| <= 1e-5 * max(1, |oracle|)
+
+Near-tie counts go to stdout and, when ROWSTATS_PARITY_LOG names a file, to
+that file as one JSON line per compared case.
 """
 from __future__ import annotations
+
+import json
+import os
 
 import numpy as np
 import torch
@@ -37,14 +47,30 @@ def probs_bits(p: torch.Tensor) -> np.ndarray:
     return p.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def record(case: str, **fields):
+    """Prints a parity record and appends it to $ROWSTATS_PARITY_LOG."""
+    line = {"case": case, **fields}
+    print("parity:", json.dumps(line), flush=True)
+    path = os.environ.get("ROWSTATS_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(line) + "\n")
+
+
+def exact_score(x_row: np.ndarray, row: int, col: int, temp: float, seed: int) -> float:
+    """The oracle's perturbed score z = s + g of one column, from its parts."""
+    s = float(oracle.scale_row(x_row[col:col + 1], temp)[0])
+    return s + oracle.uniform_gumbel(oracle.noise_word(seed, row, col))[1]
+
+
 def compare_rowstats(w, out, rows, label=""):
-    """Compares the GPU outputs `out` on `rows` with the oracle; returns the
-    number of near-tie sample rows that were excused."""
+    """Compares the GPU outputs `out` on `rows` with the oracle; returns
+    (near-tie rows, near-tie rows whose sample differs from the oracle's)."""
     argmax, sample, entropy, probs = out
     rows = np.asarray(rows, dtype=np.int64)
     x = host_rows(w.logits, rows)
-    ref = oracle.rowstats(x, rows, w.temps.cpu().numpy(), w.canvas_len, w.seed,
-                          PROBS_CODE[w.probs_dtype])
+    temps = w.temps.cpu().numpy()
+    ref = oracle.rowstats(x, rows, temps, w.canvas_len, w.seed, PROBS_CODE[w.probs_dtype])
     ridx = torch.as_tensor(rows, device=argmax.device)
     g_arg = argmax[ridx].cpu().numpy()
     g_smp = sample[ridx].cpu().numpy()
@@ -54,17 +80,43 @@ def compare_rowstats(w, out, rows, label=""):
     near = ref["gap"] < GAP_BAND
     smp_bad = np.nonzero((g_smp != ref["sample"]) & ~near)[0]
     assert smp_bad.size == 0, f"{label} sample differs on rows {rows[smp_bad][:10]}: gpu {g_smp[smp_bad][:10]} oracle {ref['sample'][smp_bad][:10]} gap {ref['gap'][smp_bad][:10]}"
+    excused = np.nonzero((g_smp != ref["sample"]) & near)[0]
+    for i in excused:
+        # several columns are within the band of the best: the GPU's must be one
+        r = int(rows[i])
+        t = float(temps[r // w.canvas_len])
+        z_best = exact_score(x[i], r, int(ref["sample"][i]), t, w.seed)
+        z_gpu = exact_score(x[i], r, int(g_smp[i]), t, w.seed)
+        assert 0.0 <= z_best - z_gpu <= GAP_BAND, (
+            f"{label} row {r}: the GPU's sample {g_smp[i]} scores {z_gpu!r}, "
+            f"more than {GAP_BAND} below the best {z_best!r} (column {ref['sample'][i]})")
     err = np.abs(g_ent - ref["entropy"])
     assert np.all(err <= ENTROPY_TOL), f"{label} entropy off by {err.max():.3g} on row {rows[np.argmax(err)]}"
     if w.probs_dtype is not None:
         gp = probs_bits(probs.index_select(0, ridx))
-        d = np.abs(gp.astype(np.int64) - ref["probs"].astype(np.int64))
-        worst = int(d.max()) if d.size else 0
-        if worst > 1:
-            r, c = np.unravel_index(np.argmax(d), d.shape)
-            raise AssertionError(f"{label} probs differ by {worst} ulp at row {rows[r]} col {c}: "
-                                 f"gpu {gp[r, c]:#06x} oracle {ref['probs'][r, c]:#06x}")
-    return int(near.sum())
+        ne = np.nonzero(gp != ref["probs"])
+        if ne[0].size:
+            d = np.abs(gp[ne].astype(np.int32) - ref["probs"][ne].astype(np.int32))
+            worst = int(d.max())
+            if worst > 1:
+                k = int(np.argmax(d))
+                r, c = ne[0][k], ne[1][k]
+                raise AssertionError(f"{label} probs differ by {worst} ulp at row {rows[r]} col {c}: "
+                                     f"gpu {gp[r, c]:#06x} oracle {ref['probs'][r, c]:#06x}")
+    return int(near.sum()), int(excused.size)
+
+
+def compare_all_rows(w, out, label, block=256):
+    """compare_rowstats over every row of the workload, `block` rows at a
+    time (host memory stays bounded); records the near-tie counts."""
+    near = excused = 0
+    for r0 in range(0, w.rows, block):
+        n, e = compare_rowstats(w, out, range(r0, min(w.rows, r0 + block)), f"{label} rows {r0}+")
+        near += n
+        excused += e
+    record(label, rows=w.rows, compared="all", near_tie_rows=near,
+           near_tie_sample_differs=excused)
+    return near
 
 
 def compare_topk(w, vals, idx, rows, label=""):
@@ -76,13 +128,13 @@ def compare_topk(w, vals, idx, rows, label=""):
     ridx = torch.as_tensor(rows, device=vals.device)
     gv = vals[ridx].cpu().numpy()
     gi = idx[ridx].cpu().numpy()
-    for n, r in enumerate(rows):
-        if not keep[n]:
-            continue
-        assert np.array_equal(gi[n], ref_i[n]), f"{label} top-K indices differ on row {r}: gpu {gi[n]} oracle {ref_i[n]}"
-        tol = LOGPROB_TOL * np.maximum(1.0, np.abs(ref_v[n].astype(np.float64)))
-        err = np.abs(gv[n].astype(np.float64) - ref_v[n].astype(np.float64))
-        assert np.all(err <= tol), f"{label} logprobs off by {err.max():.3g} on row {r}"
+    bad = np.nonzero(np.any(gi != ref_i, axis=1) & keep)[0]
+    assert bad.size == 0, f"{label} top-K indices differ on row {rows[bad[0]]}: gpu {gi[bad[0]]} oracle {ref_i[bad[0]]}"
+    kv = gv[keep].astype(np.float64)
+    rv = ref_v[keep].astype(np.float64)
+    err = np.abs(kv - rv)
+    tol = LOGPROB_TOL * np.maximum(1.0, np.abs(rv))
+    assert np.all(err <= tol), f"{label} logprobs off by {err.max():.3g}"
 
 
 def check_properties(w, out):

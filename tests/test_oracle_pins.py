@@ -292,12 +292,19 @@ def test_sample_frequencies_follow_softmax(t):
 
 
 def test_sample_depends_on_seed_and_row_only():
-    x = (RNG.standard_normal((4, 257))).astype(np.float32)
-    a = oracle.rowstats(x, [0, 1, 2, 3], [1.0], 4, seed=77)
-    b = oracle.rowstats(x[[2, 0]].copy(), [2, 0], [1.0], 4, seed=77)
+    x = (RNG.standard_normal((64, 257))).astype(np.float32)
+    rows = np.arange(64)
+    a = oracle.rowstats(x, rows, [1.0], 64, seed=77)
+    b = oracle.rowstats(x[[2, 0]].copy(), [2, 0], [1.0], 64, seed=77)
     assert a["sample"][2] == b["sample"][0] and a["sample"][0] == b["sample"][1]
-    c = oracle.rowstats(x, [0, 1, 2, 3], [1.0], 4, seed=78)
-    assert not np.array_equal(a["sample"], c["sample"]) or True  # different stream
+    # another seed is another noise stream: the words differ and, over 64 rows
+    # of 257 near-uniform columns, so do some samples
+    c = oracle.rowstats(x, rows, [1.0], 64, seed=78)
+    assert oracle.noise_word(77, 5, 9) != oracle.noise_word(78, 5, 9)
+    assert np.count_nonzero(a["sample"] != c["sample"]) >= 32
+    # and another row of the same values draws other noise
+    d = oracle.rowstats(np.repeat(x[:1], 64, axis=0), rows, [1.0], 64, seed=77)
+    assert len(set(d["sample"].tolist())) >= 16
     assert np.all(a["gap"] >= 0)
 
 

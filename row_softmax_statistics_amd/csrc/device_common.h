@@ -107,8 +107,15 @@ __device__ __forceinline__ uint32_t pick(const uint4 &w, int i) {
 //    to be a multiple of 2^-149, i.e. Tc = (odd) 2^k with k >= 1: Tc >= 2. It
 //    happens there: x = 147 2^-149 and T = 98 give the midpoint 3 2^-150,
 //    which rounds to the even 2^-148, while fl32(P) gives 2^-149.
-// So scale() is exact for every x when Tc < 2; rows with Tc >= 2 take
-// scale_checked.
+// So scale() is exact for every x when Tc < 2.
+//
+// Double-double form, exact for every Tc: r_hi = fl64(1 / Tc),
+// r_lo = fl64((1 - r_hi Tc) r_hi) (the residual 1 - r_hi Tc is exact in an
+// fma), and P = fl64(x r_hi + fl64(x r_lo)) = q (1 + e), |e| < 2^-103.9.
+// A midpoint q = n 2^-150 (or any value of at most 25 significant bits) is an
+// fp64 number more than 2^-54 q from its fp64 neighbours, so P = q and the
+// fp32 conversion breaks the tie to even; every other case keeps the
+// distances above with a far smaller |P - q|. Rows with Tc >= 2 use it.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float clamp_temp(float t) { return t > 1e-10f ? t : 1e-10f; }
 
@@ -116,22 +123,33 @@ __device__ __forceinline__ float scale(float x, double rtc) {
   return (float)((double)x * rtc);
 }
 
-// Rows with Tc >= 2: a result at or below 2^-126 in magnitude (the true
-// quotient is then subnormal, or 2^-126 itself) is recomputed with an fp64
-// division. Its rounding is exact there: a midpoint n 2^-150 is an fp64
-// value, so fl64(q) = q and the fp32 conversion breaks the tie to even; any
-// other q lies more than min(2^-174, 2^-25 q) from every midpoint, while
-// |fl64(q) - q| <= 2^-53 q. Normal results keep the fast form (exact by the
-// first case above, for any Tc).
-__device__ __forceinline__ float scale_checked(float x, double rtc, float tc) {
-  const float s = (float)((double)x * rtc);
-  return fabsf(s) <= 0x1p-126f ? (float)((double)x / (double)tc) : s;
+// The reciprocal of a row's clamped temperature as r_hi + r_lo.
+struct Recip {
+  double hi, lo;
+};
+__device__ __forceinline__ double uniform_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
-
-// Scale for a row whose clamped temperature is tc (any tc): the fast form
-// below 2, the checked one from 2 on.
-__device__ __forceinline__ float scale_any(float x, double rtc, float tc) {
-  return tc < 2.0f ? scale(x, rtc) : scale_checked(x, rtc, tc);
+// For a wave-uniform tc the pair is moved to scalar registers, where the
+// scaling loops read it without holding vector registers.
+__device__ __forceinline__ Recip recip_of(float tc) {
+  const double hi = 1.0 / (double)tc;
+  return {hi, fma(-hi, (double)tc, 1.0) * hi};
+}
+__device__ __forceinline__ Recip recip_of_uniform(float tc) {
+  const Recip r = recip_of(tc);
+  return {uniform_f64(r.hi), uniform_f64(r.lo)};
+}
+__device__ __forceinline__ float scale_dd(float x, const Recip &r) {
+  return (float)fma((double)x, r.hi, (double)x * r.lo);
+}
+// The exact quotient for any tc: the one-product form below 2, the
+// double-double form from 2 on.
+__device__ __forceinline__ float scale_any(float x, const Recip &r, float tc) {
+  return tc < 2.0f ? scale(x, r.hi) : scale_dd(x, r);
 }
 
 // Order-preserving int32 of the fp32 bits (after +0.0f so that -0 == +0).

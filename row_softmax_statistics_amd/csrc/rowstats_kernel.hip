@@ -189,9 +189,9 @@ __device__ __forceinline__ void write_row_outputs(const RowStatsParams &p, int64
 
 // Exact perturbed score of column c of `row`: s from the raw logit (re-read
 // from HBM), g in fp64.
-__device__ __forceinline__ double exact_score(const RowStatsParams &p, int64_t row, double rtc,
-                                              float tc, int32_t c) {
-  const float s = scale_any(p.logits[row * p.ld + c], rtc, tc);
+__device__ __forceinline__ double exact_score(const RowStatsParams &p, int64_t row,
+                                              const Recip &rc, float tc, int32_t c) {
+  const float s = scale_any(p.logits[row * p.ld + c], rc, tc);
   const uint4 w = philox4x32_10((uint32_t)(c >> 2), 0u, (uint32_t)(uint64_t)row,
                                 (uint32_t)((uint64_t)row >> 32), (uint32_t)p.seed,
                                 (uint32_t)(p.seed >> 32));
@@ -242,11 +242,11 @@ __device__ __forceinline__ void merge_row(const RowStatsParams &p, int64_t row) 
       m.zc = __builtin_amdgcn_readlane(c1, __builtin_ctzll(near));
     } else {
       const float tc = clamp_temp(T);
-      const double rtc = 1.0 / (double)tc;
+      const Recip rc = recip_of(tc);
       double bz = -INFINITY;
       int32_t bc = INT_MAX;
       auto consider = [&](double zrep, int32_t c, int32_t zx) {
-        const double z = zx ? zrep : exact_score(p, row, rtc, tc, c);
+        const double z = zx ? zrep : exact_score(p, row, rc, tc, c);
         if (z > bz || (z == bz && c < bc)) {
           bz = z;
           bc = c;
@@ -291,7 +291,8 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   const float T = load_uniform(p.temps + slot_of(p, row));
   const bool greedy = !(T > 0.0f);
   const float tc = clamp_temp(T);
-  const double rtc = 1.0 / (double)tc;
+  const Recip rc = recip_of_uniform(tc);
+  const double rtc = rc.hi;
   const int32_t c0 = chunk * kChunkCols;
   // column of element k = 4 j + i of this lane
   auto col_of = [&](int k) -> int32_t { return c0 + 4 * ((k >> 2) * kWave + lane) + (k & 3); };
@@ -313,7 +314,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   if (T == 1.0f) {  // x / 1 = x
 #pragma unroll
     for (int j = 0; j < kQ; ++j) mt = fmaxf(mt, max4(v[j]));
-  } else if (tc < 2.0f) {
+  } else {
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
       v[j].x = scale(v[j].x, rtc);
@@ -322,14 +323,28 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
       v[j].w = scale(v[j].w, rtc);
       mt = fmaxf(mt, max4(v[j]));
     }
-  } else {  // subnormal quotients may be midpoints (device_common.h)
+    // From Tc = 2 on, a quotient below 2^-126 can be a midpoint of the
+    // subnormal grid that the product form rounds the wrong way by one unit
+    // (device_common.h): such results are recomputed exactly from their raw
+    // logits. Rare (values within 2^-126 T of zero).
+    if (tc >= 2.0f) {
+      bool any = false;
 #pragma unroll
-    for (int j = 0; j < kQ; ++j) {
-      v[j].x = scale_checked(v[j].x, rtc, tc);
-      v[j].y = scale_checked(v[j].y, rtc, tc);
-      v[j].z = scale_checked(v[j].z, rtc, tc);
-      v[j].w = scale_checked(v[j].w, rtc, tc);
-      mt = fmaxf(mt, max4(v[j]));
+      for (int k = 0; k < 4 * kQ; ++k) any |= fabsf(comp(v[k >> 2], k & 3)) <= 0x1p-126f;
+      if (__ballot(any) != 0) {
+#pragma unroll
+        for (int k = 0; k < 4 * kQ; ++k) {
+          if (fabsf(comp(v[k >> 2], k & 3)) <= 0x1p-126f) {
+            float x;
+            if constexpr (LDSX) x = lds_read_f32(xbuf, 4 * ((k >> 2) * kWave + lane_here()) + (k & 3));
+            else x = p.logits[row * p.ld + c0 + 4 * ((k >> 2) * kWave + lane_here()) + (k & 3)];
+            set_comp(v[k >> 2], k & 3, scale_dd(x, rc));
+          }
+        }
+        mt = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kQ; ++j) mt = fmaxf(mt, max4(v[j]));
+      }
     }
   }
   const float mw = wave_max_f32(mt);
@@ -503,7 +518,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
       int32_t bc = INT_MAX;
       auto score_exact = [&](int32_t c) {
         if (c < V) {
-          const double z = exact_score(p, row, rtc, tc, c);
+          const double z = exact_score(p, row, rc, tc, c);
           if (z > bz || (z == bz && c < bc)) {
             bz = z;
             bc = c;
@@ -541,7 +556,7 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
           if constexpr (LDSX) x = lds_read_f32(xbuf, 4 * lane_here() + k);
           else x = p.logits[row * p.ld + c0 + 4 * lane_here() + k];
         }
-        const float s = (T == 1.0f || x == -INFINITY) ? x : scale_any(x, rtc, tc);
+        const float s = (T == 1.0f || x == -INFINITY) ? x : scale_any(x, rc, tc);
         Wt = fmaf(comp(v[j], i), fmaxf(s - mu, -FLT_MAX), Wt);
       }
     Ww = wave_allreduce(Wt, SumF());
@@ -558,16 +573,32 @@ __device__ __forceinline__ Tuple reduce_chunk(const RowStatsParams &p, int64_t r
   return t;
 }
 
-// exp value of a chunk whose wave maximum is mw -> probability:
-// p = e exp(mw - m) / S
-__device__ __forceinline__ float prob_scale(float mw, float m, float inv_s) {
-  if (mw == -INFINITY) return 0.0f;
-  return __builtin_amdgcn_exp2f(fmaxf(mw - m, -FLT_MAX) * kLog2e) * inv_s;
+// From a chunk's exp values e = 2^32 exp(s - mw) to probabilities
+// p = e exp(mw - m) / S, S carrying the same 2^32 factor: p = e f with
+// f = exp(mw - m) / S. For a chunk far below the row maximum f leaves the
+// fp32 normal range (below 2^-126 once mw - m is under about -65 + log S)
+// while its probabilities can still be nonzero bf16 / fp16 values (down to
+// 2^-133, s - m near -92), so there the factor is lifted by 2^96 and the
+// product brought back with an exact power-of-two multiply:
+// p = (e f') 2^-96, f' = 2^96 f, rounded once into the subnormal range.
+struct ProbScale {
+  float f;
+  bool lifted;
+};
+
+__device__ __forceinline__ ProbScale prob_scale(float mw, float m, float inv_s) {
+  if (mw == -INFINITY) return {0.0f, false};
+  const float d = fmaxf(mw - m, -FLT_MAX) * kLog2e;  // <= 0
+  const float f = __builtin_amdgcn_exp2f(d) * inv_s;
+  if (f >= 0x1p-126f) return {f, false};
+  // 2^64 exp(mw - m) stays normal down to mw - m = -131, past which every
+  // probability of the chunk is below 2^-189; inv_s 2^32 = 2^32 / S <= 1
+  return {__builtin_amdgcn_exp2f(d + 64.0f) * (inv_s * 0x1p32f), true};
 }
 
 template <int PROBS, bool VEC>
 __device__ __forceinline__ void write_probs(const RowStatsParams &p, int64_t row, int32_t chunk,
-                                            const float4 (&e)[kQ], float sc) {
+                                            const float4 (&e)[kQ], ProbScale ps) {
   const int lane = lane_id();
   const int32_t c0 = chunk * kChunkCols;
   const Rsrc w = make_rsrc(reinterpret_cast<uint16_t *>(p.probs) + row * (int64_t)p.vocab + c0,
@@ -575,9 +606,7 @@ __device__ __forceinline__ void write_probs(const RowStatsParams &p, int64_t row
   auto pack = [](float a, float b) {
     return (PROBS == 1) ? pack_bf16x2(a, b) : pack_fp16x2(a, b);
   };
-#pragma unroll
-  for (int j = 0; j < kQ; ++j) {
-    const u32x2 pk = {pack(e[j].x * sc, e[j].y * sc), pack(e[j].z * sc, e[j].w * sc)};
+  auto store = [&](int j, const u32x2 &pk) {
     if constexpr (VEC) {
       __builtin_amdgcn_raw_buffer_store_b64(pk, w, 8u * lane, 8 * kWave * j, kNonTemporal);
     } else {
@@ -586,6 +615,18 @@ __device__ __forceinline__ void write_probs(const RowStatsParams &p, int64_t row
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk[i >> 1] >> (16 * (i & 1))), w, 8u * lane,
                                               8 * kWave * j + 2 * i, kNonTemporal);
     }
+  };
+  const float sc = ps.f;
+  if (!ps.lifted) {
+#pragma unroll
+    for (int j = 0; j < kQ; ++j)
+      store(j, u32x2{pack(e[j].x * sc, e[j].y * sc), pack(e[j].z * sc, e[j].w * sc)});
+  } else {
+    constexpr float kDown = 0x1p-96f;
+#pragma unroll
+    for (int j = 0; j < kQ; ++j)
+      store(j, u32x2{pack((e[j].x * sc) * kDown, (e[j].y * sc) * kDown),
+                     pack((e[j].z * sc) * kDown, (e[j].w * sc) * kDown)});
   }
 }
 

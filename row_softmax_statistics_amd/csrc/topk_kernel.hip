@@ -165,13 +165,15 @@ struct ChunkTop {
 };
 
 template <bool VEC>
-__device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, int32_t chunk,
-                                                  float4 (&v)[kQ], int64_t *cand, ChunkTop &out) {
+__device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, int64_t row, float T,
+                                                  int32_t chunk, float4 (&v)[kQ], int64_t *cand,
+                                                  ChunkTop &out) {
   const int lane = lane_id();
   const int32_t V = p.vocab;
   const int K = p.K;
   const float tc = clamp_temp(T);
-  const double rtc = 1.0 / (double)tc;
+  const Recip rc = recip_of_uniform(tc);
+  const double rtc = rc.hi;
   const int32_t c0 = chunk * kChunkCols;
   // column of element 0 of this lane. The columns are the same for every
   // row of this wave: without this the compiler computes the fallback's
@@ -199,22 +201,13 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, 
   if (T == 1.0f) {  // x / 1 = x
 #pragma unroll
     for (int j = 0; j < kQ; ++j) mt = fmaxf(mt, max4(v[j]));
-  } else if (tc < 2.0f) {
+  } else {
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
       v[j].x = scale(v[j].x, rtc);
       v[j].y = scale(v[j].y, rtc);
       v[j].z = scale(v[j].z, rtc);
       v[j].w = scale(v[j].w, rtc);
-      mt = fmaxf(mt, max4(v[j]));
-    }
-  } else {  // subnormal quotients may be midpoints (device_common.h)
-#pragma unroll
-    for (int j = 0; j < kQ; ++j) {
-      v[j].x = scale_checked(v[j].x, rtc, tc);
-      v[j].y = scale_checked(v[j].y, rtc, tc);
-      v[j].z = scale_checked(v[j].z, rtc, tc);
-      v[j].w = scale_checked(v[j].w, rtc, tc);
       mt = fmaxf(mt, max4(v[j]));
     }
   }
@@ -229,6 +222,31 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, float T, 
     for (int i = 0; i < 4; ++i) St += __builtin_amdgcn_exp2f((comp(v[j], i) - mu) * kLog2e);
   out.mw = mw;
   out.S = wave_allreduce(St, SumF());  // the record header holds it as fp32
+  // (after the sum, which a change of one subnormal unit in s cannot alter;
+  // the order of the values below, the keys, needs them exact)
+  // From Tc = 2 on, a quotient below 2^-126 can be a midpoint of the
+  // subnormal grid that the product form rounds the wrong way by one unit
+  // (device_common.h): such results are recomputed exactly from their raw
+  // logits. Rare (values within 2^-126 T of zero).
+  if (tc >= 2.0f) {
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < 4 * kQ; ++k) any |= fabsf(comp(v[k >> 2], k & 3)) <= 0x1p-126f;
+    if (__ballot(any) != 0) {
+#pragma unroll
+      for (int k = 0; k < 4 * kQ; ++k) {
+        if (fabsf(comp(v[k >> 2], k & 3)) <= 0x1p-126f) {
+          const float x = p.logits[row * p.ld + col_of((uint32_t)k)];
+          set_comp(v[k >> 2], k & 3, scale_dd(x, rc));
+        }
+      }
+      mt = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) mt = fmaxf(mt, max4(v[j]));
+      // the header's maximum must equal the largest key's value
+      out.mw = wave_max_f32(mt);
+    }
+  }
 
   // ---- threshold: the K-th largest lane maximum ----
   const uint32_t uk = wave_kth_largest<uint32_t>((uint32_t)key32(mt) ^ 0x80000000u, K);
@@ -305,10 +323,10 @@ __device__ __forceinline__ int32_t load_uniform_i32(const int32_t *p) {
 // over the row by the merger, for rows whose K largest keys all tie at M.
 __device__ __forceinline__ int count_at_max(const TopKParams &p, int64_t row, float T, float M) {
   const float tc = clamp_temp(T);
-  const double rtc = 1.0 / (double)tc;
+  const Recip rc = recip_of(tc);
   const float *x = p.logits + row * p.ld;
   int cnt = 0;
-  for (int32_t c = lane_here(); c < p.vocab; c += kWave) cnt += scale_any(x[c], rtc, tc) >= M ? 1 : 0;
+  for (int32_t c = lane_here(); c < p.vocab; c += kWave) cnt += scale_any(x[c], rc, tc) >= M ? 1 : 0;
   return wave_allreduce(cnt, SumI());
 }
 
@@ -352,12 +370,12 @@ __device__ __forceinline__ void write_stash_row(const TopKParams &p, int64_t pos
   }
   if (by_ids) {
     const float tc = clamp_temp(T);
-    const double rtc = 1.0 / (double)tc;
+    const Recip rc = recip_of(tc);
     const int32_t *idr = ids + (int64_t)j * ids_stride;
     for (int i = lane; i < n; i += kWave) {
       const int32_t id = idr[i];
       float v = -INFINITY;
-      if (id >= 0 && id < p.vocab) v = value(scale_any(p.logits[row * p.ld + id], rtc, tc));
+      if (id >= 0 && id < p.vocab) v = value(scale_any(p.logits[row * p.ld + id], rc, tc));
       else atomicOr(p.err_flag, kErrIndex);
       oid[1 + i] = id;
       olp[1 + i] = v;
@@ -643,7 +661,7 @@ __global__ __launch_bounds__(kThreads, 4) void topk_kernel(TopKParams p) {
       chunk_load(cur, p.logits + row * p.ld, chunk * kChunkCols, p.vocab);
     }
     ChunkTop t;
-    reduce_chunk_topk<VEC>(p, load_uniform(p.kept_temp + pos), chunk, cur, list, t);
+    reduce_chunk_topk<VEC>(p, row, load_uniform(p.kept_temp + pos), chunk, cur, list, t);
     // consume the loads issued before the copy here, before the record
     // stores, so that their wait does not wait for the copy above
     __asm__ volatile("" ::"v"(rr), "v"(slot), "v"(claim));

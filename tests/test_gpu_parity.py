@@ -210,6 +210,32 @@ def test_c5_full_size_padded_stride():
     done()
 
 
+@pytest.mark.parametrize("temp", [1.0, 0.5, 0.07])
+def test_probs_of_chunks_far_below_the_row_max(temp):
+    # each 2048-column chunk sits d below the row maximum; a chunk 65 to 92
+    # below still holds nonzero bf16 probabilities (normal down to e^-87.3,
+    # subnormal to e^-92), which must survive the scaling from the chunk's
+    # own maximum to the row's
+    drops = [20, 40, 60, 66, 72, 78, 81, 84, 86, 87.5, 89, 90.5, 92, 95, 100, 130]
+    rows, vocab = 6, 2048 * len(drops)
+    g = torch.Generator().manual_seed(int(temp * 100))
+    x = torch.randn(rows, vocab, generator=g) * (0.4 * temp)
+    for c, d in enumerate(drops):
+        x[:, 2048 * c:2048 * (c + 1)] -= d * temp
+    x[:, 5] = 0.0                                   # the row maximum: S is about 1
+    x[1] = x[1].roll(4096, dims=0)
+    x[2, ::3] = float("-inf")
+    w = syn.Workload(f"far chunks T={temp}", x.to(DEV), torch.full((rows,), temp, device=DEV), 1,
+                     99, torch.bfloat16)
+    out = gpu_rowstats(w)
+    compare_rowstats(w, out, range(rows), f"far chunks T={temp}")
+    p = out[3].float()
+    assert float(p[0, 2048 * 9:2048 * 10].max()) >= 2.0 ** -126     # 87.5 below: normal
+    sub = float(p[0, 2048 * 11:2048 * 12].max())                   # 90.5 below: subnormal
+    assert 0.0 < sub < 2.0 ** -126
+    done()
+
+
 def _coop_case(vocab, probs_dtype):
     x = torch.zeros(1, vocab, device=DEV)
     return x, torch.ones(1, device=DEV)
@@ -229,9 +255,11 @@ def test_vocab_beyond_co_residency_is_rejected(probs_dtype, vocab):
         rs.sample_row_stats(x, t, 1, 0, probs_dtype, out=out)
     assert e.value.code == -6
     assert int(out[0][0]) == -5 and int(out[1][0]) == -5
-    with pytest.raises(rs.RowStatsError) as e:
-        rs.topk_logprobs(x, t, 1, torch.ones(1, dtype=torch.uint8, device=DEV), 3)
-    assert e.value.code == -6
+    if probs_dtype is None:
+        # top-K keeps 4096 chunks resident as well (4 waves per SIMD)
+        with pytest.raises(rs.RowStatsError) as e:
+            rs.topk_logprobs(x, t, 1, torch.ones(1, dtype=torch.uint8, device=DEV), 3)
+        assert e.value.code == -6
     # the largest vocab that fits still runs
     ok = 2048 * (2048 if probs_dtype else 4096)
     w = syn.random_case(DEV, rows=2, vocab=ok, canvas_len=1, seed=8, t_choices=(0.0, 1.0),
@@ -267,16 +295,29 @@ def test_subnormal_midpoint_quotients(temp):
     for r in range(rows):
         x[r, 2 * (r % 8)] = xs[r]
         x[r, 2 * (r % 8) + 1] = partner[r]
-        x[r, 40 + r % 7] = xs[(r + 5) % rows]
+        if r >= 12:   # another midpoint value elsewhere, larger or smaller
+            x[r, 40 + r % 7] = xs[(r + 5) % rows]
     w = syn.Workload(f"midpoints T={temp}", torch.from_numpy(x).to(DEV),
                      torch.full((rows,), temp, device=DEV), 1, 77, torch.bfloat16)
     out = gpu_rowstats(w)
     compare_rowstats(w, out, range(rows), f"midpoints T={temp}")
-    assert out[0].cpu().tolist() == [2 * (r % 8) for r in range(rows)]
+    # in the rows holding only the pair, the two tie at the maximum
+    assert out[0].cpu().tolist()[:12] == [2 * (r % 8) for r in range(12)]
     w.keep_mask = torch.ones(rows, dtype=torch.uint8, device=DEV)
     w.K = 3
     vals, idx = _run_topk(w)
     compare_topk(w, vals, idx, range(rows), f"topk midpoints T={temp}")
+    # the stash: one request per row; logits mode writes the scaled values
+    # themselves, and the rank counts the ties at the maximum
+    import test_gpu_stash as ts
+    ar = torch.arange(rows, dtype=torch.int32)
+    for mode in (False, True):
+        sw = syn.StashWorkload(f"midpoint stash T={temp}", w.logits, 1, ar.to(DEV), ar.to(DEV),
+                               torch.ones(rows, dtype=torch.uint8, device=DEV),
+                               torch.ones(rows, dtype=torch.int32, device=DEV), w.temps, 3,
+                               torch.zeros(rows, dtype=torch.int32, device=DEV), None, rows, 1, 4,
+                               mode)
+        ts.compare(ts.run_gpu(sw), ts.run_oracle(sw), mode, f"stash midpoints T={temp} {mode}")
     done()
 
 

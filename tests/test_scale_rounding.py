@@ -2,15 +2,34 @@
 
 The kernels compute s = x / Tc (Tc = max(T, 1e-10f), one IEEE fp32 division
 by the page's reading) as fl32(fl64(x) * fl64(1 / Tc)) and, on rows with
-Tc >= 2, recompute results at or below 2^-126 in magnitude as
-fl32(fl64(x) / fl64(Tc)) (the proof is written beside the device code).
-These tests evaluate the same two formulas in numpy's IEEE fp64/fp32
-arithmetic and compare them with numpy's fp32 division over every input
-whose quotient can be subnormal, for temperatures on both sides of 2, and
-over random inputs of every magnitude.
+Tc >= 2, recompute results at or below 2^-126 in magnitude with the
+double-double form fl32(fma(x, r_hi, fl64(x r_lo))) (the proof is written
+beside the device code). These tests evaluate the same formulas in IEEE
+fp64/fp32 arithmetic on the host (numpy, and tests/scale_check.c where a
+fused multiply-add is needed) and compare them with fp32 division over every
+input whose quotient can be subnormal, for temperatures on both sides of 2,
+and over random inputs of every magnitude.
 """
+import ctypes
+import os
+import subprocess
+import tempfile
+
 import numpy as np
 import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def checker():
+    out = os.path.join(tempfile.mkdtemp(prefix="scale_check"), "libscale_check.so")
+    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                    "-shared", "-o", out, os.path.join(HERE, "scale_check.c"), "-lm"], check=True)
+    lib = ctypes.CDLL(out)
+    lib.scale_mismatches.argtypes = [ctypes.c_float, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int]
+    lib.scale_mismatches.restype = ctypes.c_long
+    return lib
 
 TINY = np.float32(2.0 ** -126)
 
@@ -19,16 +38,7 @@ def fast(x, t):
     return (x.astype(np.float64) * (1.0 / np.float64(t))).astype(np.float32)
 
 
-def checked(x, t):
-    s = fast(x, t)
-    low = np.abs(s) <= TINY
-    s[low] = (x[low].astype(np.float64) / np.float64(t)).astype(np.float32)
-    return s
-
-
-def kernel_scale(x, t):
-    t = np.float32(max(np.float32(t), np.float32(1e-10)))
-    return fast(x, t) if t < 2 else checked(x, t)
+FAST, DOUBLE_DOUBLE, KERNEL = 0, 1, 2
 
 
 # Both formulas and the division are odd functions of x (rounding to nearest
@@ -56,34 +66,40 @@ def test_fast_form_is_ieee_below_two(t):
 
 
 @pytest.mark.parametrize("t", [2.0, 6.0, 98.0, 150.0, 364.0])
-def test_checked_form_is_ieee_from_two(t):
-    t32 = np.float32(t)
+def test_kernel_form_is_ieee_from_two(checker, t):
     # every x whose quotient can be subnormal (x < 2^-126 t), and a margin
     hi = bits_of(2.0 ** -126 * t * 2)
-    for xs in positive_floats(1, hi):
-        assert np.array_equal(kernel_scale(xs, t32), xs / t32), t
+    assert checker.scale_mismatches(t, 1, hi, KERNEL) == 0
+    assert checker.scale_mismatches(t, 1, hi, DOUBLE_DOUBLE) == 0
 
 
-def test_fast_form_misses_a_midpoint_at_98():
+@pytest.mark.parametrize("t", [1e-10, 0.37, 1.5, 936.0, 3.3e4, 1.7e9])
+def test_double_double_form_is_ieee(checker, t):
+    # the double-double form alone is exact too, at any temperature
+    # (subnormal and first-binade inputs)
+    assert checker.scale_mismatches(t, *SMALL_BITS, DOUBLE_DOUBLE) == 0
+
+
+def test_fast_form_misses_midpoints_at_98(checker):
     # 147 2^-149 / 98 = 3 2^-150: ties to the even 2^-148, but fl64(1 / 98)
     # is below 1/98, so the product falls just under the midpoint
     x = np.array([147 * 2.0 ** -149], np.float32)
     t = np.float32(98.0)
     assert (x / t)[0] == np.float32(2.0 ** -148)
     assert fast(x, t)[0] == np.float32(2.0 ** -149)
-    assert checked(x, t)[0] == np.float32(2.0 ** -148)
     # and it is not a rare case at this temperature
-    assert sum(np.count_nonzero(fast(xs, t) != xs / t) for xs in positive_floats(*SMALL_BITS)) > 10000
+    assert checker.scale_mismatches(98.0, 1, 1 << 23, FAST) == 19950
 
 
 def test_every_magnitude_random():
+    # normal results: the fast form is exact at any temperature
     rng = np.random.default_rng(5)
     bits = rng.integers(1, 0x7F7FFFFF, size=4_000_000, dtype=np.uint32)
     x = bits.view(np.float32) * np.where(rng.random(bits.size) < 0.5, -1, 1).astype(np.float32)
     for t in [1e-10, 0.013, 0.5, 0.7, 1.0, 1.5, 2.5, 98.0, 3.3e4, 1.7e9]:
         t32 = np.float32(t)
-        with np.errstate(over="ignore"):
+        with np.errstate(over="ignore", under="ignore"):
             ref = x / t32
-            got = kernel_scale(x, t32)
-        ok = np.isfinite(ref)   # x / T overflowing fp32 is outside the contract
+            got = fast(x, t32)
+        ok = np.isfinite(ref) & (np.abs(ref) > TINY)   # overflow is outside the contract
         assert np.array_equal(got[ok], ref[ok]), t

@@ -12,8 +12,13 @@ sample of the same workload, and secondary measurements of the other
 workloads (C3 stats-only, C4 top-K, C5 large padded, S4 the converged-logprob
 stash over C4's logits) under "others".
 
+--ceiling times streaming kernels with the row-statistics memory structure
+and no arithmetic (row_softmax_statistics_amd/csrc/ceiling): the fraction of
+the 8 TB/s peak that a read of the C2 logits, and a read plus a bf16 write of
+half the bytes, reach with each structure.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others]
-       [--no-cpu] [--only C2|C3|C4|C5|S4] [--calib-copy]
+       [--no-cpu] [--only C2|C3|C4|C5|S4] [--calib-copy] [--ceiling]
 """
 from __future__ import annotations
 
@@ -30,6 +35,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+SELFCOND_D = 2560
 METRIC = "row-stats logits GB/s and % of HBM peak at V=262144 (rows/s alongside)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -58,6 +65,8 @@ def stash_algorithmic_bytes(kept_rows: int, vocab: int, width: int, m: int,
 def source_hash() -> str:
     h = hashlib.sha1()
     for f in sorted(glob.glob(os.path.join(ROOT, "row_softmax_statistics_amd", "csrc", "*"))):
+        if not os.path.isfile(f):
+            continue
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
@@ -121,6 +130,35 @@ def bench_rowstats(w, steps, warmup, keep_out=False):
     if keep_out:
         r["out"] = out
     return r
+
+
+def bench_selfcond(w, d, steps, warmup):
+    """rowstats_selfcond over the workload's logits with a seeded bf16
+    [vocab, d] embedding table: the statistics plus the bf16 softmax times the
+    table. Work per call: 2 rows vocab d flops on the matrix cores; bytes:
+    logits read twice (statistics, then the product's A operand), the table
+    read once, 20 B of statistics and 4 d B of product per row."""
+    import torch
+    import row_softmax_statistics_amd as rs
+    import synthetic as syn
+    dev = w.logits.device
+    embed = syn.embedding(w.vocab, d, seed=21, device=dev)
+    out = (torch.empty(w.rows, dtype=torch.int64, device=dev),
+           torch.empty(w.rows, dtype=torch.int64, device=dev),
+           torch.empty(w.rows, dtype=torch.float32, device=dev),
+           torch.empty(w.rows, d, dtype=torch.float32, device=dev))
+
+    def step():
+        rs.selfcond_embed(w.logits, w.temps, w.canvas_len, w.seed, embed, out=out)
+
+    ms, wall = time_launches(step, steps, warmup)
+    rs.check_device()
+    flops = 2.0 * w.rows * w.vocab * d
+    nbytes = 8 * w.rows * w.vocab + 2 * w.vocab * d + (20 + 4 * d) * w.rows
+    del embed, out
+    return {"ms": ms, "wall_ms": wall, "d": d, "tflops": flops / ms / 1e9,
+            "mfma_frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, "bytes": nbytes,
+            "gbs": nbytes / ms / 1e6}
 
 
 def bench_topk(w, steps, warmup):
@@ -195,6 +233,49 @@ def calib_copy(steps=5):
                       "launches": steps, "kernel": "torch.neg (elementwise)"}))
 
 
+CEILING_MODES = {0: ("lds_dma_read", 0), 1: ("lds_dma_read_write8", 2),
+                 2: ("lds_dma_read_write16", 2), 3: ("vgpr_read", 0), 4: ("vgpr_read_write16", 2)}
+
+
+def ceiling(steps=20, warmup=3, rows=4096, vocab=262144):
+    """Streaming ceilings over C2-sized data: each structure of
+    csrc/ceiling/stream_ceiling.hip at 2 and 4 waves per SIMD, and torch's
+    own read (sum) and read + half-size write (fp32 -> bf16) for reference.
+    Bytes counted: rows x vocab x 4 read, plus x 2 written for the write
+    modes."""
+    import ctypes
+    import torch
+    from row_softmax_statistics_amd import build as hb
+    lib = ctypes.CDLL(hb.CEILING_LIB)
+    fn = lib.stream_ceiling
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    n = rows * vocab
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    n_chunks = n // 2048
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for mode, (name, wb) in CEILING_MODES.items():
+        for occ in (2, 4):
+            def step():
+                rc = fn(mode, occ, src.data_ptr(), dst.data_ptr(), n_chunks, sink.data_ptr(), stream)
+                assert rc == 0, rc
+            ms, _ = time_launches(step, steps, warmup)
+            nbytes = n * (4 + wb)
+            res[f"{name}_occ{occ}"] = {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+                                       "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    ms, _ = time_launches(lambda: src.sum(), steps, warmup)
+    res["torch_sum_read"] = {"ms": round(ms, 4), "gbs": round(4 * n / ms / 1e6, 1),
+                             "frac": round(4 * n / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    ms, _ = time_launches(lambda: dst.copy_(src), steps, warmup)
+    res["torch_fp32_to_bf16_copy"] = {"ms": round(ms, 4), "gbs": round(6 * n / ms / 1e6, 1),
+                                      "frac": round(6 * n / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    print(json.dumps({"ceiling": res, "rows": rows, "vocab": vocab, "steps": steps}), flush=True)
+
+
 def bench_stash(w, steps, warmup):
     import torch
     import row_softmax_statistics_amd as rs
@@ -229,8 +310,9 @@ def main():
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--only", choices=["C2", "C3", "C4", "C5", "S4"], default=None)
+    ap.add_argument("--only", choices=["C2", "C3", "C4", "C5", "S4", "SC"], default=None)
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--ceiling", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the method's "
@@ -243,12 +325,17 @@ def main():
     if args.calib_copy:
         calib_copy()
         return
+    if args.ceiling:
+        ceiling(args.steps, args.warmup)
+        return
     dev = "cuda:0"
 
     if args.only:
-        w = syn.stash_c4(dev) if args.only == "S4" else syn.WORKLOADS[args.only](dev)
+        w = syn.stash_c4(dev) if args.only == "S4" else \
+            syn.c2(dev) if args.only == "SC" else syn.WORKLOADS[args.only](dev)
         r = bench_topk(w, args.steps, args.warmup) if args.only == "C4" else \
             bench_stash(w, args.steps, args.warmup) if args.only == "S4" else \
+            bench_selfcond(w, SELFCOND_D, args.steps, args.warmup) if args.only == "SC" else \
             bench_rowstats(w, args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **{k: round(v, 4) if isinstance(v, float) else v
                                                      for k, v in r.items()}}), flush=True)
@@ -281,7 +368,15 @@ def main():
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, gpu_out)
-    del w, gpu_out
+    del gpu_out
+    torch.cuda.empty_cache()
+    if not args.no_others:
+        # the self-conditioning product over the same logits (matrix cores)
+        sc = bench_selfcond(w, SELFCOND_D, max(5, args.steps // 4), 2)
+        sc = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in sc.items()}
+        line["selfcond"] = {"workload": f"C2 logits x bf16 embedding [262144, {SELFCOND_D}]",
+                            "bound": "mfma", "peak_tflops": MFMA_BF16_PEAK_TFLOPS, **sc}
+    del w
     torch.cuda.empty_cache()
     # the three V = 262144 row-statistics workloads the 75 % target covers,
     # side by side, each against the HBM roofline

@@ -8,7 +8,7 @@
  * after a call returns. Work is queued asynchronously on `stream` (a
  * hipStream_t passed as void*, NULL = the default stream): buffers must stay
  * alive until that stream has been synchronised. rowstats_run,
- * topk_logprobs and stash_converged_logprobs share a grow-only scratch
+ * rowstats_selfcond, topk_logprobs and stash_converged_logprobs share a grow-only scratch
  * buffer per device: a call queued on another stream than the previous one
  * first waits, on the device, for that previous call (an event wait), so
  * calls from several streams run one after another.
@@ -88,6 +88,35 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows,
                  int64_t vocab, const float *temps, int64_t canvas_len,
                  uint64_t seed, int probs_dtype, int64_t *argmax,
                  int64_t *sample, float *entropy, void *probs, void *stream);
+
+/*
+ * The row statistics of rowstats_run (without probs) and the
+ * self-conditioning input of the denoise step: the softmax of each row in
+ * bf16 (the model dtype) times the token embedding table, computed on the
+ * matrix cores without writing the probabilities,
+ *   out[r, j] = sum_c bf16(softmax(s_r))[c] * E[c, j],
+ * bf16(p) being the probabilities rowstats_run writes with
+ * ROWSTATS_PROBS_BF16 (each within one bf16 unit of the exact rounding).
+ * Defined by: diffusion_gemma_sampler page, module docstring (the softmax is
+ * produced in the model dtype for the self-conditioning matmul); the
+ * statistics as for rowstats_run.
+ *
+ *   logits ... seed, argmax, sample, entropy   as for rowstats_run.
+ *   embed       bf16 [vocab, d] row-major (row c is token c's embedding),
+ *               16-byte aligned.
+ *   d           embedding width: a multiple of 256, 256 <= d <= 2^20.
+ *   out         fp32 [rows, d] row-major, 16-byte aligned: fp32 sums of the
+ *               bf16 products, added in a fixed order (repeat calls give
+ *               the same bits).
+ *   Scratch: the grow-only buffer also holds 8 partial [rows, d] fp32
+ *   products. Errors as for rowstats_run; ROWSTATS_ERR_SHAPE also for a bad
+ *   d or alignment.
+ */
+int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows,
+                      int64_t vocab, const float *temps, int64_t canvas_len,
+                      uint64_t seed, const void *embed, int64_t d,
+                      int64_t *argmax, int64_t *sample, float *entropy,
+                      float *out, void *stream);
 
 /*
  * Top-K logprobs of the rows of kept slots.

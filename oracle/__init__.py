@@ -8,7 +8,9 @@ Semantics follow the vLLM API page "diffusion_gemma_sampler" (module
 docstring; ``sample_row_stats`` and ``sample_row_stats_reference``;
 ``stash_converged_logprobs`` and the ``_lp_topk_kernel`` docstring). The
 arithmetic lives in ``rowstats_oracle.c`` (plain C, fp32 divide then double
-reductions); this module only marshals numpy arrays through ctypes.
+reductions); this module marshals numpy arrays through ctypes, and
+``selfcond`` multiplies the oracle's bf16 probabilities by an embedding table
+with a float64 matrix product.
 """
 from __future__ import annotations
 
@@ -192,3 +194,30 @@ def topk_logprobs(logits: np.ndarray, row_ids, temps, canvas_len: int,
     if rc != 0:
         raise RuntimeError(f"oracle_topk_logprobs failed with code {rc}")
     return out_vals, out_idx
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64 values (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(
+        np.float64)
+
+
+def selfcond(logits: np.ndarray, row_ids, temps, canvas_len: int, embed_bits: np.ndarray,
+             block: int = 16384) -> np.ndarray:
+    """Self-conditioning input of the given rows (diffusion_gemma_sampler page,
+    module docstring: the softmax in the model dtype feeds the self-conditioning
+    matmul): out[i, :] = sum_c bf16(p_i)[c] * E[c, :], where bf16(p_i) are this
+    oracle's probabilities of row ``row_ids[i]`` rounded once to bf16
+    (``rowstats`` with PROBS_BF16) and ``embed_bits`` is E as bf16 bit patterns
+    [vocab, d]. Products and sums in float64, the vocab taken ``block``
+    columns at a time (a float64 matrix product per block).
+    """
+    ref = rowstats(logits, row_ids, temps, canvas_len, 0, PROBS_BF16)
+    p = bf16_to_f64(ref["probs"])
+    vocab, d = embed_bits.shape
+    if vocab != p.shape[1]:
+        raise ValueError("embed must have one row per logits column")
+    out = np.zeros((p.shape[0], d), np.float64)
+    for c0 in range(0, vocab, block):
+        out += p[:, c0:c0 + block] @ bf16_to_f64(embed_bits[c0:c0 + block])
+    return out

@@ -33,6 +33,10 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "rowstats_selfcond": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "topk_logprobs": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -171,6 +175,42 @@ def sample_row_stats(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int,
     preallocated ``(argmax, sample, entropy, probs)`` tensors.
     """
     return _rowstats_call("rowstats_run", logits, temps, canvas_len, seed, probs_dtype, out)
+
+
+def selfcond_embed(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int, seed: int,
+                   embed: torch.Tensor, *, out=None):
+    """The row statistics (as ``sample_row_stats`` without probs) and the
+    self-conditioning input: each row's softmax in bf16 times ``embed``
+    (bf16 [vocab, d], d a multiple of 256), accumulated in fp32, computed
+    without writing the probabilities.
+
+    Returns ``(argmax int64, sample int64, entropy fp32, out fp32 [rows, d])``.
+    ``out`` may pass preallocated ``(argmax, sample, entropy, out)``.
+    """
+    _check_logits(logits)
+    rows, vocab = logits.shape
+    dev = logits.device
+    _check_temps(temps, rows, canvas_len, dev)
+    if (embed.dtype != torch.bfloat16 or embed.device != dev or embed.dim() != 2
+            or embed.shape[0] != vocab or not embed.is_contiguous()):
+        raise ValueError("embed must be a contiguous bfloat16 [vocab, d] tensor on the logits' device")
+    d = embed.shape[1]
+    if out is None:
+        out = (torch.empty(rows, dtype=torch.int64, device=dev),
+               torch.empty(rows, dtype=torch.int64, device=dev),
+               torch.empty(rows, dtype=torch.float32, device=dev),
+               torch.empty(rows, d, dtype=torch.float32, device=dev))
+    argmax, sample, entropy, res = out
+    _check_out(argmax, "argmax", (rows,), torch.int64, dev)
+    _check_out(sample, "sample", (rows,), torch.int64, dev)
+    _check_out(entropy, "entropy", (rows,), torch.float32, dev)
+    _check_out(res, "out", (rows, d), torch.float32, dev)
+    rc = lib().rowstats_selfcond(
+        _ptr(logits), logits.stride(0) if rows > 1 else vocab, rows, vocab, _ptr(temps),
+        canvas_len, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(embed), d, _ptr(argmax),
+        _ptr(sample), _ptr(entropy), _ptr(res), _stream_ptr(dev))
+    _check(rc, "rowstats_selfcond")
+    return argmax, sample, entropy, res
 
 
 def topk_logprobs(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int,

@@ -10,6 +10,7 @@
 
 #include "../../include/rowstats.h"
 #include "rowstats_internal.h"
+#include "selfcond_internal.h"
 #include "topk_internal.h"
 
 using namespace rowstats;
@@ -251,9 +252,9 @@ int plan_and_launch_topk(DeviceState &d, TopKParams &p, hipStream_t s) {
   return note_stream(d, s);
 }
 
-// Checks and launch plan of a row-statistics call: fills p except the
-// scratch pointers and the epoch, and returns the grid and the scratch
-// bytes the call needs.
+// Checks and launch plan of a row-statistics call, shared by rowstats_run
+// and rowstats_selfcond: fills p except the scratch pointers and the epoch,
+// and returns the grid and the scratch bytes the call needs.
 int plan_rowstats(const DeviceState &d, const float *logits, int64_t row_stride, int64_t rows,
                   int64_t vocab, const float *temps, int64_t canvas_len, uint64_t seed,
                   int probs_dtype, int64_t *argmax, int64_t *sample, float *entropy, void *probs,
@@ -356,6 +357,71 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
   if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
   d->grow.epoch = p.epoch;
   return note_stream(*d, s);
+}
+
+int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
+                      const float *temps, int64_t canvas_len, uint64_t seed, const void *embed,
+                      int64_t d, int64_t *argmax, int64_t *sample, float *entropy, float *out,
+                      void *stream) {
+  g_last_error.clear();
+  int rc = check_rowstats_args(logits, row_stride, rows, vocab, temps, canvas_len,
+                               ROWSTATS_PROBS_NONE, argmax, sample, entropy, nullptr);
+  if (rc || rows == 0) return rc;
+  if (!embed || !out) return fail(ROWSTATS_ERR_NULL, "embed or out is NULL");
+  if (d < kSelfCondTileN || d % kSelfCondTileN != 0 || d > (1 << 20))
+    return fail(ROWSTATS_ERR_SHAPE, "d must be a multiple of %d in [%d, 2^20], got %lld",
+                kSelfCondTileN, kSelfCondTileN, (long long)d);
+  if ((reinterpret_cast<uintptr_t>(embed) & 15) || (reinterpret_cast<uintptr_t>(out) & 15))
+    return fail(ROWSTATS_ERR_SHAPE, "embed and out must be 16-byte aligned");
+  const int64_t m_tiles = (rows + kSelfCondTileM - 1) / kSelfCondTileM;
+  const int64_t n_tiles = d / kSelfCondTileN;
+  if ((int64_t)kSelfCondSplits * m_tiles * n_tiles > 0x7FFFFFFFLL)
+    return fail(ROWSTATS_ERR_SHAPE, "rows %lld x d %lld is too large", (long long)rows,
+                (long long)d);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState *dev = nullptr;
+  if ((rc = device_state(&dev))) return rc;
+  RowStatsParams p;
+  int64_t grid = 0;
+  size_t need = 0, head_bytes = 0, tuple_bytes = 0;
+  if ((rc = plan_rowstats(*dev, logits, row_stride, rows, vocab, temps, canvas_len, seed,
+                          ROWSTATS_PROBS_NONE, argmax, sample, entropy, nullptr, p, &grid, &need,
+                          &head_bytes, &tuple_bytes)))
+    return rc;
+  // the partial products follow the row-statistics scratch
+  const size_t partial_at = (need + 255) & ~(size_t)255;
+  const size_t partial_bytes = (size_t)kSelfCondSplits * rows * d * sizeof(float);
+  if ((rc = order_after_last(*dev, s))) return rc;
+  if ((rc = ensure_grow_scratch(*dev, partial_at + partial_bytes, s))) return rc;
+  if ((rc = next_epoch(dev->grow, s, &p.epoch))) return rc;
+  set_scratch(p, dev->grow, head_bytes, tuple_bytes);
+  hipError_t e = rowstats_launch(p, ROWSTATS_PROBS_NONE, (int)grid, s);
+  if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
+
+  SelfCondParams q = {};
+  q.logits = logits;
+  q.ld = row_stride;
+  q.rows = rows;
+  q.vocab = (int32_t)vocab;
+  q.d = (int32_t)d;
+  q.temps = temps;
+  q.slot_mul = p.slot_mul;
+  q.slot_shift = p.slot_shift;
+  q.rowres = p.rowres;
+  q.E = static_cast<const uint16_t *>(embed);
+  q.partial = reinterpret_cast<float *>(reinterpret_cast<char *>(dev->grow.base) + partial_at);
+  q.out = out;
+  const int64_t per = (vocab + kSelfCondSplits - 1) / kSelfCondSplits;
+  q.k_per_split = (int32_t)((per + kSelfCondStepK - 1) / kSelfCondStepK * kSelfCondStepK);
+  q.m_tiles = (int32_t)m_tiles;
+  q.n_tiles = (int32_t)n_tiles;
+  q.vec_ok = ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) && (row_stride % 4 == 0);
+  e = selfcond_launch(q, s);
+  if (e != hipSuccess) return fail_hip(e, "self-conditioning kernel launch");
+  dev->grow.epoch = p.epoch;
+  return note_stream(*dev, s);
 }
 
 int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,

@@ -1,0 +1,254 @@
+// Streaming ceilings of the row-statistics memory pattern on gfx950: how
+// fast a persistent grid of waves can read fp32 chunks of 2048 columns
+// (8 KiB) and, optionally, write a bf16 value per column (half the bytes),
+// with no arithmetic beyond consuming the data. Measurement code for the
+// benchmark's --ceiling mode, not part of the row-statistics library.
+//
+// Wave gw of W takes chunks gw, gw + W, ... . Modes:
+//   kDmaRead     the row-statistics kernels' structure: each chunk copied
+//                HBM -> the wave's LDS buffer by eight 1 KiB buffer_load ... lds
+//                (streaming bit set) while the previous one is reduced; two
+//                buffers per wave at 2 waves per SIMD (the copy of the next
+//                chunk goes to the other one), one at 4 (the copy is issued
+//                once the chunk is in registers)
+//   kDmaWrite8   kDmaRead + the probs store pattern of the kernels: lane l
+//                holds quads j 64 + l and stores 8 bytes per quad
+//   kDmaWrite16  kDmaRead + lane l holding two adjacent quads of each 128 and
+//                storing 16 bytes per pair (1 KiB per store instruction)
+//   kVgprRead    buffer_load_dwordx4 straight into registers (eight per lane
+//                per chunk, 1 KiB each), the next chunk's loads issued before
+//                the current chunk is consumed
+//   kVgprWrite16 kVgprRead with lane l loading quads 2 l, 2 l + 1 of each 128
+//                and storing 16 bytes per pair
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kChunkBytes = 8192;
+constexpr int kStream = 2;  // cache policy: streaming (nt)
+
+enum Mode { kDmaRead = 0, kDmaWrite8 = 1, kDmaWrite16 = 2, kVgprRead = 3, kVgprWrite16 = 4 };
+
+using Rsrc = __amdgpu_buffer_rsrc_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void *LdsPtr;
+
+__device__ __forceinline__ Rsrc rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ int lane() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ void fence() { __asm__ volatile("" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  fence();
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  fence();
+}
+
+// Copy of one chunk into an LDS buffer of 512 quads (eight 1 KiB pieces).
+__device__ __forceinline__ void dma_chunk(float4 *buf, const float *src, uint32_t bytes) {
+  const Rsrc r = rsrc(src, bytes);
+  const uint32_t voff = 16u * lane();
+#define CEIL_DMA(J)                                                                          \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(buf + ((J) >> 2) * 4 * kWave), 16, voff, \
+                                           4096 * ((J) >> 2), 1024 * ((J)&3), kStream)
+  CEIL_DMA(0);
+  CEIL_DMA(1);
+  CEIL_DMA(2);
+  CEIL_DMA(3);
+  CEIL_DMA(4);
+  CEIL_DMA(5);
+  CEIL_DMA(6);
+  CEIL_DMA(7);
+#undef CEIL_DMA
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const float4 *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float4 *)p;
+}
+
+// Eight quads of the buffer into registers: quads j 64 + l (PAIRS = false) or
+// quads j 128 + 2 l, + 1 (PAIRS = true, j < 4), with the read's own wait.
+template <bool PAIRS>
+__device__ __forceinline__ void lds_read(f32x4 (&v)[8], const float4 *buf) {
+  const uint32_t a = lds_addr(buf) + (PAIRS ? 32u : 16u) * (uint32_t)lane();
+  if constexpr (!PAIRS) {
+    __asm__ volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:1024\n"
+        "ds_read_b128 %2, %8 offset:2048\n"
+        "ds_read_b128 %3, %8 offset:3072\n"
+        "ds_read_b128 %4, %8 offset:4096\n"
+        "ds_read_b128 %5, %8 offset:5120\n"
+        "ds_read_b128 %6, %8 offset:6144\n"
+        "ds_read_b128 %7, %8 offset:7168\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a)
+        : "memory");
+  } else {
+    __asm__ volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:16\n"
+        "ds_read_b128 %2, %8 offset:2048\n"
+        "ds_read_b128 %3, %8 offset:2064\n"
+        "ds_read_b128 %4, %8 offset:4096\n"
+        "ds_read_b128 %5, %8 offset:4112\n"
+        "ds_read_b128 %6, %8 offset:6144\n"
+        "ds_read_b128 %7, %8 offset:6160\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a)
+        : "memory");
+  }
+}
+
+__device__ __forceinline__ uint32_t fold(const f32x4 (&v)[8]) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    x ^= __float_as_uint(v[j][0]) ^ __float_as_uint(v[j][1]) ^ __float_as_uint(v[j][2]) ^
+         __float_as_uint(v[j][3]);
+  return x;
+}
+
+// Half-size stores of a chunk's values (bf16 of each column).
+template <bool PAIRS>
+__device__ __forceinline__ void store_half(uint16_t *dst, const f32x4 (&v)[8]) {
+  const Rsrc w = rsrc(dst, kChunkBytes / 2);
+  if constexpr (!PAIRS) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{bf16x2(v[j][0], v[j][1]), bf16x2(v[j][2], v[j][3])},
+                                            w, 8u * lane(), 512 * j, kStream);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{bf16x2(v[2 * j][0], v[2 * j][1]), bf16x2(v[2 * j][2], v[2 * j][3]),
+                bf16x2(v[2 * j + 1][0], v[2 * j + 1][1]), bf16x2(v[2 * j + 1][2], v[2 * j + 1][3])},
+          w, 16u * lane(), 1024 * j, kStream);
+  }
+}
+
+template <int MODE, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void stream_kernel(const float *src, uint16_t *dst,
+                                                              int64_t n_chunks, uint32_t *sink) {
+  constexpr int kBufs = OCC == 2 ? 2 : 1;
+  __shared__ float4 stage[kWaves * kBufs * 512];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t W = (int64_t)gridDim.x * kWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
+  uint32_t acc = 0;
+  auto chunk_src = [&](int64_t c) { return src + c * (kChunkBytes / 4); };
+  if constexpr (MODE <= kDmaWrite16) {
+    float4 *const b0 = stage + wave * kBufs * 512;
+    float4 *const b1 = b0 + (kBufs - 1) * 512;
+    // stores of the previous chunk issued after its copy: the wait for the
+    // copy leaves them in flight
+    constexpr int kStores = MODE == kDmaWrite8 ? 8 : MODE == kDmaWrite16 ? 4 : 0;
+    int64_t c = gw;
+    if (c < n_chunks) dma_chunk(b0, chunk_src(c), kChunkBytes);
+    for (int n = 0; c < n_chunks; ++n, c += W) {
+      const int64_t next = c + W;
+      if (n == 0) wait_vm<0>();
+      else wait_vm<kStores>();
+      f32x4 v[8];
+      lds_read<MODE == kDmaWrite16>(v, (n & 1) ? b1 : b0);
+      fence();
+      // the copy past the last chunk goes through a zero-size descriptor
+      dma_chunk((n & 1) ? b0 : b1, next < n_chunks ? chunk_src(next) : src,
+                next < n_chunks ? kChunkBytes : 0u);
+      fence();
+      if constexpr (MODE == kDmaRead) acc ^= fold(v);
+      else store_half<MODE == kDmaWrite16>(dst + c * (kChunkBytes / 4), v);
+    }
+  } else {
+    constexpr bool kPairs = MODE == kVgprWrite16;
+    const uint32_t voff = (kPairs ? 32u : 16u) * (uint32_t)lane();
+    auto load = [&](f32x4 (&v)[8], int64_t c) {
+      const Rsrc r = rsrc(chunk_src(c < n_chunks ? c : 0), c < n_chunks ? kChunkBytes : 0u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int off = kPairs ? 2048 * (j >> 1) + 16 * (j & 1) : 1024 * j;
+        v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, off, kStream));
+      }
+    };
+    int64_t c = gw;
+    f32x4 a[8], b[8];
+    load(a, c);
+    for (; c < n_chunks; c += 2 * W) {
+      load(b, c + W);
+      if constexpr (MODE == kVgprRead) acc ^= fold(a);
+      else store_half<true>(dst + c * (kChunkBytes / 4), a);
+      if (c + W >= n_chunks) break;
+      load(a, c + 2 * W);
+      if constexpr (MODE == kVgprRead) acc ^= fold(b);
+      else store_half<true>(dst + (c + W) * (kChunkBytes / 4), b);
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the reads alive; never true for the inputs used
+}
+
+template <int MODE, int OCC>
+const void *kernel_of() {
+  return reinterpret_cast<const void *>(&stream_kernel<MODE, OCC>);
+}
+
+const void *select(int mode, int occ) {
+  const bool two = occ == 2;
+  switch (mode) {
+    case kDmaRead: return two ? kernel_of<kDmaRead, 2>() : kernel_of<kDmaRead, 4>();
+    case kDmaWrite8: return two ? kernel_of<kDmaWrite8, 2>() : kernel_of<kDmaWrite8, 4>();
+    case kDmaWrite16: return two ? kernel_of<kDmaWrite16, 2>() : kernel_of<kDmaWrite16, 4>();
+    case kVgprRead: return two ? kernel_of<kVgprRead, 2>() : kernel_of<kVgprRead, 4>();
+    case kVgprWrite16: return two ? kernel_of<kVgprWrite16, 2>() : kernel_of<kVgprWrite16, 4>();
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// One launch of mode `mode` (0..4, see above) at `occ` (2 or 4) waves per
+// SIMD over n_chunks chunks of 8 KiB at src (device, 16-byte aligned),
+// writing 4 KiB per chunk at dst for the write modes. The grid is every
+// workgroup the device holds at that occupancy. Returns 0, or -1 for a bad
+// argument, or the HIP error code.
+int stream_ceiling(int mode, int occ, const float *src, uint16_t *dst, int64_t n_chunks,
+                   uint32_t *sink, void *stream) {
+  const void *k = select(mode, occ);
+  if (!k || !src || !sink || n_chunks < 1 || (mode != kDmaRead && mode != kVgprRead && !dst))
+    return -1;
+  int dev = 0, per_cu = 0;
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0);
+  if (e != hipSuccess) return (int)e;
+  if (per_cu < 1) return -1;
+  void *args[] = {&src, &dst, &n_chunks, &sink};
+  e = hipLaunchKernel(k, dim3(per_cu * prop.multiProcessorCount), dim3(kThreads), args, 0,
+                      reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : (int)e;
+}
+
+}  // extern "C"

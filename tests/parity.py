@@ -161,3 +161,68 @@ def check_properties(w, out):
         if probs is not None and probs.dtype == torch.bfloat16:
             tot = probs[r0:r1].double().sum(dim=1)
             assert float((tot - 1.0).abs().max()) < 2.0 ** -7, f"probs do not sum to 1 in rows {r0}..{r1}"
+
+
+# Self-conditioning product (rowstats_selfcond). The kernel forms each
+# probability in fp32 from s - m, a fused multiply-add, exp2 and 1 / S; its
+# relative error stays below about 2^-15.8 (s - m down to -92, where bf16
+# ends), so its bf16 value can differ from the oracle's only where the exact
+# probability lies within SELFCOND_EPS of a rounding boundary, and then by one
+# unit. The fp32 sums of each of the 8 vocab ranges, then of the ranges, add
+# at most (K_range + 9) 2^-24 sum |p E| (every product exact in fp32).
+SELFCOND_EPS = 2.0 ** -14
+SELFCOND_SPLITS = 8
+
+
+def selfcond_k_range(vocab: int) -> int:
+    per = -(-vocab // SELFCOND_SPLITS)
+    return -(-per // 32) * 32
+
+
+def bf16_ulp(q: np.ndarray) -> np.ndarray:
+    """Unit in the last place of bf16 values q >= 0 (2^-133 below 2^-126)."""
+    e = np.floor(np.log2(np.maximum(q, 2.0 ** -126)))
+    return np.where(q >= 2.0 ** -126, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+def selfcond_bound(x: np.ndarray, rows, temps, canvas_len: int, embed_bits: np.ndarray):
+    """Per-element bound of |gpu - oracle| for the rows' products (see above)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    ref = oracle.rowstats(x, rows, temps, canvas_len, 0, oracle.PROBS_BF16)
+    q = oracle.bf16_to_f64(ref["probs"])
+    ulp = bf16_ulp(q)
+    w = np.empty_like(q)
+    for i, r in enumerate(rows):
+        s = oracle.scale_row(x[i], float(np.asarray(temps)[r // canvas_len])).astype(np.float64)
+        e = np.exp(s - s.max())
+        p = e / e.sum()
+        near = np.minimum(np.abs(p - (q[i] + ulp[i] / 2)),
+                          np.minimum(np.abs(p - (q[i] - ulp[i] / 2)), np.abs(p - (q[i] - ulp[i] / 4))))
+        amb = near <= SELFCOND_EPS * p + 2.0 ** -149
+        w[i] = amb * ulp[i] + (selfcond_k_range(x.shape[1]) + 9) * 2.0 ** -24 * (q[i] + ulp[i])
+    bound = np.zeros((len(rows), embed_bits.shape[1]))
+    for c0 in range(0, embed_bits.shape[0], 16384):
+        bound += w[:, c0:c0 + 16384] @ np.abs(oracle.bf16_to_f64(embed_bits[c0:c0 + 16384]))
+    return bound + 2.0 ** -140
+
+
+def compare_selfcond(w, embed: torch.Tensor, out, rows, label=""):
+    """Statistics as compare_rowstats (no probs) and the product within
+    selfcond_bound of the oracle's; returns the worst error / bound."""
+    import dataclasses
+    argmax, sample, entropy, res = out
+    compare_rowstats(dataclasses.replace(w, probs_dtype=None), (argmax, sample, entropy, None),
+                     rows, label)
+    rows = np.asarray(rows, dtype=np.int64)
+    x = host_rows(w.logits, rows)
+    eb = embed.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    temps = w.temps.cpu().numpy()
+    ref = oracle.selfcond(x, rows, temps, w.canvas_len, eb)
+    got = res[torch.as_tensor(rows, device=res.device)].double().cpu().numpy()
+    bound = selfcond_bound(x, rows, temps, w.canvas_len, eb)
+    err = np.abs(got - ref)
+    ratio = err / bound
+    k = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert np.all(err <= bound), (f"{label} product off by {err[k]:.3g} (bound {bound[k]:.3g}) "
+                                  f"at row {rows[k[0]]} column {k[1]}: gpu {got[k]!r} oracle {ref[k]!r}")
+    return float(ratio.max())

@@ -42,6 +42,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["rowstats_run",
+                                           "rowstats_selfcond",
                                            "topk_logprobs", "stash_converged_logprobs",
                                            "rowstats_last_error", "rowstats_check_device",
                                            "rowstats_release"])
@@ -114,6 +115,39 @@ def test_rowstats_run_zero_rows_is_a_no_op(entry):
 def test_topk_rejects(kwargs, code):
     assert topk(**kwargs) == code
     assert rs.last_error() != ""
+
+
+def selfcond(logits=FAKE, stride=8, rows=4, vocab=8, temps=FAKE, canvas=2, seed=1,
+             embed=FAKE, d=256, argmax=FAKE, sample=FAKE, entropy=FAKE, out=FAKE):
+    return rs.lib().rowstats_selfcond(logits, stride, rows, vocab, temps, canvas, seed, embed, d,
+                                      argmax, sample, entropy, out, NULL)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(rows=-1), ERR_SHAPE),
+    (dict(vocab=0), ERR_SHAPE),
+    (dict(stride=7), ERR_SHAPE),
+    (dict(canvas=0), ERR_SHAPE),
+    (dict(d=0), ERR_SHAPE),
+    (dict(d=128), ERR_SHAPE),
+    (dict(d=300), ERR_SHAPE),
+    (dict(d=2 ** 21), ERR_SHAPE),
+    (dict(embed=ctypes.c_void_p(0x1008)), ERR_SHAPE),   # not 16-byte aligned
+    (dict(out=ctypes.c_void_p(0x1004)), ERR_SHAPE),
+    (dict(logits=NULL), ERR_NULL),
+    (dict(temps=NULL), ERR_NULL),
+    (dict(embed=NULL), ERR_NULL),
+    (dict(out=NULL), ERR_NULL),
+    (dict(argmax=NULL), ERR_NULL),
+])
+def test_selfcond_rejects(kwargs, code):
+    assert selfcond(**kwargs) == code
+    assert rs.last_error() != ""
+
+
+def test_selfcond_zero_rows_is_a_no_op():
+    assert selfcond(rows=0, logits=NULL, temps=NULL, embed=NULL, out=NULL, argmax=NULL,
+                    sample=NULL, entropy=NULL) == OK
 
 
 def test_topk_zero_rows_is_a_no_op():

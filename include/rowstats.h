@@ -11,7 +11,8 @@
  * rowstats_selfcond, topk_logprobs and stash_converged_logprobs share a grow-only scratch
  * buffer per device: a call queued on another stream than the previous one
  * first waits, on the device, for that previous call (an event wait), so
- * calls from several streams run one after another.
+ * calls from several streams run one after another. rowstats_run_noalloc
+ * has a fixed scratch array of its own (see there).
  *
  * All functions return ROWSTATS_OK (0) or a negative rowstats_status; they
  * never abort and never throw. Argument checks run before any HIP call, so
@@ -40,10 +41,15 @@ typedef enum rowstats_status {
                                row in co-resident waves at once and the device
                                cannot hold them (vocab above about 4.2 million on
                                one MI355X) */
-  ROWSTATS_ERR_DEVICE = -7  /* a kernel flagged a failure (a bounded wait ran out,
+  ROWSTATS_ERR_DEVICE = -7, /* a kernel flagged a failure (a bounded wait ran out,
                                or a stash index argument was out of range);
                                reported by rowstats_check_device */
+  ROWSTATS_ERR_SCRATCH = -8 /* rowstats_run_noalloc: the call needs more scratch
+                               than ROWSTATS_NOALLOC_SCRATCH_BYTES */
 } rowstats_status;
+
+/* Size of the fixed scratch array of rowstats_run_noalloc (64 MiB per GPU). */
+#define ROWSTATS_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
 typedef enum rowstats_probs_dtype {
   ROWSTATS_PROBS_NONE = 0,
@@ -88,6 +94,29 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows,
                  int64_t vocab, const float *temps, int64_t canvas_len,
                  uint64_t seed, int probs_dtype, int64_t *argmax,
                  int64_t *sample, float *entropy, void *probs, void *stream);
+
+/*
+ * rowstats_run without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, outputs and errors as
+ * rowstats_run, computed by the same kernels; it calls no hipMalloc,
+ * hipFree or other allocating routine. Its scratch is a file-scope
+ * __device__ array of ROWSTATS_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process ends. A call needs
+ *   256 + G * 256 + rows * ceil(vocab / 2048) * 64 + rows * 16 bytes
+ * (G = the row groups of the launch, at most 4096 / ceil(vocab / 2048));
+ * more returns ROWSTATS_ERR_SCRATCH before anything is queued. At vocab
+ * 262144 that is up to 8000 rows per call.
+ * Every call on a GPU shares that GPU's array and leaves its contents for
+ * the next one (no per-call clearing is needed: its words carry the call's
+ * epoch). Calls of this entry point that overlap in time on one GPU (two
+ * streams, two threads) race on the array: queue them on one stream.
+ */
+int rowstats_run_noalloc(const float *logits, int64_t row_stride, int64_t rows,
+                         int64_t vocab, const float *temps, int64_t canvas_len,
+                         uint64_t seed, int probs_dtype, int64_t *argmax,
+                         int64_t *sample, float *entropy, void *probs,
+                         void *stream);
 
 /*
  * The row statistics of rowstats_run (without probs) and the

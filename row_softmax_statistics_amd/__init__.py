@@ -23,13 +23,17 @@ ROWSTATS_OK = 0
 STATUS_NAMES = {
     -1: "ROWSTATS_ERR_NULL", -2: "ROWSTATS_ERR_SHAPE", -3: "ROWSTATS_ERR_K",
     -4: "ROWSTATS_ERR_DTYPE", -5: "ROWSTATS_ERR_HIP", -6: "ROWSTATS_ERR_COOP",
-    -7: "ROWSTATS_ERR_DEVICE",
+    -7: "ROWSTATS_ERR_DEVICE", -8: "ROWSTATS_ERR_SCRATCH",
 }
 PROBS_CODES = {None: 0, torch.bfloat16: 1, torch.float16: 2}
 
 # Entry points declared in include/rowstats.h, with their ctypes signatures.
 _SIGNATURES = {
     "rowstats_run": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "rowstats_run_noalloc": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
@@ -175,6 +179,17 @@ def sample_row_stats(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int,
     preallocated ``(argmax, sample, entropy, probs)`` tensors.
     """
     return _rowstats_call("rowstats_run", logits, temps, canvas_len, seed, probs_dtype, out)
+
+
+def sample_row_stats_noalloc(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int,
+                             seed: int, probs_dtype: torch.dtype | None, out):
+    """``sample_row_stats`` through the allocation-free entry point: the
+    caller passes every output in ``out``; the library uses its fixed
+    per-GPU scratch array (see rowstats_run_noalloc in include/rowstats.h)."""
+    if out is None:
+        raise ValueError("the allocation-free call needs preallocated outputs")
+    return _rowstats_call("rowstats_run_noalloc", logits, temps, canvas_len, seed, probs_dtype,
+                          out)
 
 
 def selfcond_embed(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int, seed: int,

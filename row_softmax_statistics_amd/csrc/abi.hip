@@ -17,9 +17,17 @@ using namespace rowstats;
 
 namespace {
 
-// Error words of the scratch: {report bits, epoch of the last call whose
-// wait gave up}. Host code reaches them through hipGetSymbolAddress.
-static __device__ __align__(16) uint32_t err_words[2];
+// Scratch of rowstats_run_noalloc, one copy per GPU the library runs on,
+// held until the process ends: zero when the code object is loaded, then
+// only ever told apart by the epoch tags of its words (as the grow-only
+// scratch below). Host code reaches it only through the address
+// hipGetSymbolAddress gives for the current device.
+constexpr size_t kNoAllocScratchBytes = ROWSTATS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint64_t scratch[kNoAllocScratchBytes / 8];
+
+// Error words {report bits, epoch of the last call whose wait gave up} of
+// the grow-only scratch [0] and of the fixed array above [1].
+static __device__ __align__(16) uint32_t err_words[2][2];
 
 thread_local std::string g_last_error;
 
@@ -64,6 +72,7 @@ struct DeviceState {
   int resident[2][3] = {};  // row-stats blocks per CU by [vector path][probs dtype]
   int topk_resident[2] = {};
   Area grow;                // grow-only, shared by rowstats_run, topk_logprobs and the stash
+  Area fixed;               // the fixed array of rowstats_run_noalloc
   // The stream of the last call on the grow-only scratch; a call on another
   // stream first waits (on the device) for the work queued there so far.
   hipStream_t last_stream = nullptr;
@@ -91,8 +100,8 @@ hipError_t zero_async(uint32_t *p, size_t n, hipStream_t s) {
 }
 
 // Per-device set-up, once per device with it current: occupancy of every
-// kernel variant and the device address of the error words. Allocates
-// nothing.
+// kernel variant and the device addresses of the fixed scratch array and
+// the error words. Allocates nothing.
 int device_state(DeviceState **out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -112,10 +121,15 @@ int device_state(DeviceState **out) {
       e = topk_resident_blocks(vec != 0, &d.topk_resident[vec]);
       if (e != hipSuccess) return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     }
-    void *err = nullptr;
+    void *fixed = nullptr, *err = nullptr;
+    e = hipGetSymbolAddress(&fixed, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
     e = hipGetSymbolAddress(&err, HIP_SYMBOL(err_words));
     if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(error words)");
+    d.fixed.base = fixed;
+    d.fixed.bytes = kNoAllocScratchBytes;
     d.grow.err = static_cast<uint32_t *>(err);
+    d.fixed.err = static_cast<uint32_t *>(err) + 2;
     d.ready = true;
   }
   *out = &d;
@@ -253,8 +267,8 @@ int plan_and_launch_topk(DeviceState &d, TopKParams &p, hipStream_t s) {
 }
 
 // Checks and launch plan of a row-statistics call, shared by rowstats_run
-// and rowstats_selfcond: fills p except the scratch pointers and the epoch,
-// and returns the grid and the scratch bytes the call needs.
+// and rowstats_run_noalloc: fills p except the scratch pointers and the
+// epoch, and returns the grid and the scratch bytes the call needs.
 int plan_rowstats(const DeviceState &d, const float *logits, int64_t row_stride, int64_t rows,
                   int64_t vocab, const float *temps, int64_t canvas_len, uint64_t seed,
                   int probs_dtype, int64_t *argmax, int64_t *sample, float *entropy, void *probs,
@@ -357,6 +371,38 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows, int64_t 
   if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
   d->grow.epoch = p.epoch;
   return note_stream(*d, s);
+}
+
+int rowstats_run_noalloc(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
+                         const float *temps, int64_t canvas_len, uint64_t seed, int probs_dtype,
+                         int64_t *argmax, int64_t *sample, float *entropy, void *probs,
+                         void *stream) {
+  g_last_error.clear();
+  int rc = check_rowstats_args(logits, row_stride, rows, vocab, temps, canvas_len, probs_dtype,
+                               argmax, sample, entropy, probs);
+  if (rc || rows == 0) return rc;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState *d = nullptr;
+  if ((rc = device_state(&d))) return rc;
+  RowStatsParams p;
+  int64_t grid = 0;
+  size_t need = 0, head_bytes = 0, tuple_bytes = 0;
+  if ((rc = plan_rowstats(*d, logits, row_stride, rows, vocab, temps, canvas_len, seed, probs_dtype,
+                          argmax, sample, entropy, probs, p, &grid, &need, &head_bytes,
+                          &tuple_bytes)))
+    return rc;
+  if (need > d->fixed.bytes)
+    return fail(ROWSTATS_ERR_SCRATCH,
+                "%lld rows of %d chunks need %zu bytes of scratch; the fixed array holds %zu",
+                (long long)rows, p.C, need, d->fixed.bytes);
+  if ((rc = next_epoch(d->fixed, s, &p.epoch))) return rc;
+  set_scratch(p, d->fixed, head_bytes, tuple_bytes);
+  hipError_t e = rowstats_launch(p, probs_dtype, (int)grid, s);
+  if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
+  d->fixed.epoch = p.epoch;
+  return ROWSTATS_OK;
 }
 
 int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
@@ -550,7 +596,7 @@ int rowstats_check_device(void *stream) {
   int rc = device_state(&d);
   if (rc) return rc;
   uint32_t flag = 0;
-  for (Area *a : {&d->grow}) {
+  for (Area *a : {&d->grow, &d->fixed}) {
     uint32_t f = 0;
     e = hipMemcpy(&f, a->err, sizeof f, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpy(error flag)");

@@ -41,7 +41,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["rowstats_run",
+    assert declared_functions() == sorted(["rowstats_run", "rowstats_run_noalloc",
                                            "rowstats_selfcond",
                                            "topk_logprobs", "stash_converged_logprobs",
                                            "rowstats_last_error", "rowstats_check_device",
@@ -85,13 +85,13 @@ def topk(logits=FAKE, stride=8, rows=4, vocab=8, temps=FAKE, canvas=2, keep=FAKE
     (dict(dtype=1, probs=NULL), ERR_NULL),
     (dict(dtype=2, probs=NULL), ERR_NULL),
 ])
-@pytest.mark.parametrize("entry", ["rowstats_run"])
+@pytest.mark.parametrize("entry", ["rowstats_run", "rowstats_run_noalloc"])
 def test_rowstats_run_rejects(kwargs, code, entry):
     assert run(entry=entry, **kwargs) == code
     assert rs.last_error() != ""
 
 
-@pytest.mark.parametrize("entry", ["rowstats_run"])
+@pytest.mark.parametrize("entry", ["rowstats_run", "rowstats_run_noalloc"])
 def test_rowstats_run_zero_rows_is_a_no_op(entry):
     # nothing is dereferenced and no HIP call is made
     assert run(rows=0, logits=NULL, temps=NULL, argmax=NULL, sample=NULL, entropy=NULL,
@@ -161,6 +161,8 @@ def test_binding_refuses_cpu_tensors():
         rs.sample_row_stats(x, torch.ones(1), 2, 0)
     with pytest.raises(ValueError):
         rs.topk_logprobs(x, torch.ones(1), 2, torch.ones(1, dtype=torch.uint8), 2)
+    with pytest.raises(ValueError):
+        rs.sample_row_stats_noalloc(x, torch.ones(1), 2, 0, None, None)
 
 
 def stash(logits=FAKE, stride=8, lrows=8, vocab=8, canvas=2, m=3, src=FAKE, slots=FAKE,

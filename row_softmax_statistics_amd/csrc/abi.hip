@@ -414,13 +414,13 @@ int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows, int
                                ROWSTATS_PROBS_NONE, argmax, sample, entropy, nullptr);
   if (rc || rows == 0) return rc;
   if (!embed || !out) return fail(ROWSTATS_ERR_NULL, "embed or out is NULL");
-  if (d < kSelfCondTileN || d % kSelfCondTileN != 0 || d > (1 << 20))
+  if (d < kSelfCondDMultiple || d % kSelfCondDMultiple != 0 || d > (1 << 20))
     return fail(ROWSTATS_ERR_SHAPE, "d must be a multiple of %d in [%d, 2^20], got %lld",
-                kSelfCondTileN, kSelfCondTileN, (long long)d);
+                kSelfCondDMultiple, kSelfCondDMultiple, (long long)d);
   if ((reinterpret_cast<uintptr_t>(embed) & 15) || (reinterpret_cast<uintptr_t>(out) & 15))
     return fail(ROWSTATS_ERR_SHAPE, "embed and out must be 16-byte aligned");
   const int64_t m_tiles = (rows + kSelfCondTileM - 1) / kSelfCondTileM;
-  const int64_t n_tiles = d / kSelfCondTileN;
+  const int64_t n_tiles = (d + kSelfCondTileN - 1) / kSelfCondTileN;
   if ((int64_t)kSelfCondSplits * m_tiles * n_tiles > 0x7FFFFFFFLL)
     return fail(ROWSTATS_ERR_SHAPE, "rows %lld x d %lld is too large", (long long)rows,
                 (long long)d);

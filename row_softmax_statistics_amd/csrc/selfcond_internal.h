@@ -8,10 +8,12 @@ namespace rowstats {
 
 // GEMM tiling of the self-conditioning product: workgroups of 8 waves, each
 // computing a kSelfCondTileM x kSelfCondTileN tile of out over one of
-// kSelfCondSplits vocab ranges.
+// kSelfCondSplits vocab ranges. d is a multiple of kSelfCondDMultiple; the
+// last column tile may be half full.
 constexpr int kSelfCondThreads = 512;
-constexpr int kSelfCondTileM = 256;
-constexpr int kSelfCondTileN = 256;
+constexpr int kSelfCondTileM = 128;
+constexpr int kSelfCondTileN = 512;
+constexpr int kSelfCondDMultiple = 256;
 constexpr int kSelfCondSplits = 8;
 constexpr int kSelfCondStepK = 32;
 
@@ -20,7 +22,7 @@ struct SelfCondParams {
   int64_t ld;
   int64_t rows;
   int32_t vocab;
-  int32_t d;            // columns of E and out, a multiple of kSelfCondTileN
+  int32_t d;            // columns of E and out, a multiple of kSelfCondDMultiple
   const float *temps;
   uint32_t slot_mul;    // row / canvas_len = (row * slot_mul) >> slot_shift
   uint32_t slot_shift;

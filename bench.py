@@ -17,8 +17,14 @@ and no arithmetic (row_softmax_statistics_amd/csrc/ceiling): the fraction of
 the 8 TB/s peak that a read of the C2 logits, and a read plus a bf16 write of
 half the bytes, reach with each structure.
 
+--profile-run runs every workload once more with a fixed number of launches
+(in the order PROFILE_PLAN lists) for rocprofv3; --summarize DIR then reads
+that run's kernel-trace or counter CSV from DIR and prints, per workload and
+kernel, the launch statistics (or the mean counter value per launch).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others]
-       [--no-cpu] [--only C2|C3|C4|C5|S4] [--calib-copy] [--ceiling]
+       [--no-cpu] [--only C2|C3|C4|C5|S4|SC] [--calib-copy] [--ceiling]
+       [--profile-run] [--summarize DIR]
 """
 from __future__ import annotations
 
@@ -302,6 +308,79 @@ def bench_stash(w, steps, warmup):
             "kept_rows_per_s": kept / ms * 1e3}
 
 
+# Workloads of --profile-run in launch order, with the kernels one call
+# launches (substrings of the names rocprofv3 records).
+PROFILE_PLAN = [
+    ("C2", ["rowstats_kernel<1, true>"]),
+    ("C3", ["rowstats_kernel<0, true>"]),
+    ("C5", ["rowstats_kernel<1, true>"]),
+    ("C4", ["kept_rows_kernel", "topk_kernel<true>"]),
+    ("S4", ["stash_rows_kernel", "topk_kernel<true>"]),
+    ("SC", ["rowstats_kernel<0, true>", "selfcond_gemm_kernel<true>", "selfcond_reduce_kernel"]),
+]
+PROFILE_LAUNCHES = 21  # per workload: 1 untimed + 20 timed calls
+
+
+def profile_run():
+    """Every workload of PROFILE_PLAN, PROFILE_LAUNCHES calls each, in order."""
+    import torch
+    import synthetic as syn
+    import row_softmax_statistics_amd as rs
+    dev = "cuda:0"
+    for name, _ in PROFILE_PLAN:
+        w = syn.stash_c4(dev) if name == "S4" else syn.c2(dev) if name == "SC" else \
+            syn.WORKLOADS[name](dev)
+        r = bench_topk(w, PROFILE_LAUNCHES - 1, 1) if name == "C4" else \
+            bench_stash(w, PROFILE_LAUNCHES - 1, 1) if name == "S4" else \
+            bench_selfcond(w, SELFCOND_D, PROFILE_LAUNCHES - 1, 1) if name == "SC" else \
+            bench_rowstats(w, PROFILE_LAUNCHES - 1, 1)
+        print(json.dumps({"workload": name, **{k: round(v, 4) if isinstance(v, float) else v
+                                               for k, v in r.items()}}), flush=True)
+        del w
+        torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    rs.release()
+
+
+def summarize(directory: str):
+    """Per-workload summary of a --profile-run under rocprofv3: the kernel
+    dispatches of this library, in order, are matched to PROFILE_PLAN (for
+    a counter run, separately for each counter)."""
+    import csv
+    import statistics
+    counters = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    traces = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    src = counters[0] if counters else traces[0]
+    with open(src) as fh:
+        rows = [r for r in csv.DictReader(fh) if "rowstats::" in r["Kernel_Name"]]
+    key = "Dispatch_Id" if counters else "Correlation_Id"
+    names = sorted({r["Counter_Name"] for r in rows}) if counters else ["duration (ns)"]
+    seq = []
+    for name, kernels in PROFILE_PLAN:
+        for _ in range(PROFILE_LAUNCHES):
+            seq.extend((name, k) for k in kernels)
+    print(f"# {os.path.basename(src)}; {PROFILE_LAUNCHES} calls per workload (the first "
+          f"untimed), source_hash {source_hash()}")
+    print("# workload | kernel | quantity | dispatches | mean | median | min | max"
+          + (" (counters: value per dispatch)" if counters else ""))
+    for cname in names:
+        sel = [r for r in rows if not counters or r["Counter_Name"] == cname]
+        sel.sort(key=lambda r: int(r[key]))
+        if len(sel) != len(seq):
+            sys.exit(f"{src}: {len(sel)} dispatches of this library for {cname}, "
+                     f"the plan has {len(seq)}")
+        stats = {}
+        for r, (name, k) in zip(sel, seq):
+            if k not in r["Kernel_Name"]:
+                sys.exit(f"{src}: dispatch {r[key]} is {r['Kernel_Name'][:80]}, the plan has {k}")
+            v = float(r["Counter_Value"]) if counters else \
+                float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            stats.setdefault((name, k), []).append(v)
+        for (name, k), v in stats.items():
+            print(f"{name} | {k} | {cname} | {len(v)} | {statistics.fmean(v):.1f} | "
+                  f"{statistics.median(v):.1f} | {min(v):.1f} | {max(v):.1f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,7 +392,12 @@ def main():
     ap.add_argument("--only", choices=["C2", "C3", "C4", "C5", "S4", "SC"], default=None)
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--ceiling", action="store_true")
+    ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR", default=None)
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the method's "
               "hot path is measured on one MI355X; sharding is described, not run.",
@@ -327,6 +411,9 @@ def main():
         return
     if args.ceiling:
         ceiling(args.steps, args.warmup)
+        return
+    if args.profile_run:
+        profile_run()
         return
     dev = "cuda:0"
 

@@ -1,0 +1,68 @@
+"""bench.py --summarize on synthetic rocprofv3 CSV files (no GPU): the
+library's dispatches are matched in order to the workloads of the profile
+run, other kernels are ignored, and a dispatch out of plan is an error."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def plan_names():
+    out = []
+    for name, kernels in bench.PROFILE_PLAN:
+        for _ in range(bench.PROFILE_LAUNCHES):
+            out.extend((name, k) for k in kernels)
+    return out
+
+
+def write_trace(path, entries):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Correlation_Id", "Kernel_Name", "Start_Timestamp",
+                                           "End_Timestamp"])
+        w.writeheader()
+        for i, (name, dur) in enumerate(entries):
+            w.writerow({"Correlation_Id": i + 1, "Kernel_Name": name, "Start_Timestamp": 1000 * i,
+                        "End_Timestamp": 1000 * i + dur})
+
+
+def run(directory):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize",
+                           str(directory)], capture_output=True, text=True)
+
+
+def test_durations_per_workload(tmp_path):
+    entries = []
+    for n, (w, k) in enumerate(plan_names()):
+        entries.append(("void at::native::fill_kernel(int)", 5))  # torch's own kernels interleave
+        entries.append((f"void rowstats::{k}(rowstats::RowStatsParams)",
+                        100 + 10 * [x for x, _ in bench.PROFILE_PLAN].index(w)))
+    write_trace(tmp_path / "t_kernel_trace.csv", entries)
+    r = run(tmp_path)
+    assert r.returncode == 0, r.stderr
+    rows = [l.split(" | ") for l in r.stdout.splitlines() if not l.startswith("#")]
+    got = {(w, k): (int(n), float(mean)) for w, k, _, n, mean, *_ in rows}
+    for i, (w, kernels) in enumerate(bench.PROFILE_PLAN):
+        for k in kernels:
+            assert got[(w, k)] == (bench.PROFILE_LAUNCHES, 100.0 + 10 * i)
+
+
+def test_a_dispatch_out_of_plan_is_an_error(tmp_path):
+    names = plan_names()
+    entries = [(f"void rowstats::{k}(x)", 100) for _, k in names]
+    entries[3] = ("void rowstats::topk_kernel<true>(x)", 100)
+    write_trace(tmp_path / "t_kernel_trace.csv", entries)
+    r = run(tmp_path)
+    assert r.returncode != 0 and "the plan has" in r.stderr
+
+
+def test_a_missing_dispatch_is_an_error(tmp_path):
+    entries = [(f"void rowstats::{k}(x)", 100) for _, k in plan_names()][:-1]
+    write_trace(tmp_path / "t_kernel_trace.csv", entries)
+    r = run(tmp_path)
+    assert r.returncode != 0 and "dispatches of this library" in r.stderr

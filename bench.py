@@ -138,17 +138,18 @@ def bench_rowstats(w, steps, warmup, keep_out=False):
     return r
 
 
-def bench_selfcond(w, d, steps, warmup):
-    """rowstats_selfcond over the workload's logits with a seeded bf16
-    [vocab, d] embedding table: the statistics plus the bf16 softmax times the
-    table. Work per call: 2 rows vocab d flops on the matrix cores; bytes:
-    logits read twice (statistics, then the product's A operand), the table
-    read once, 20 B of statistics and 4 d B of product per row."""
+def bench_selfcond(w, d, steps, warmup, dtype=None):
+    """rowstats_selfcond over the workload's logits with a seeded [vocab, d]
+    embedding table in the model dtype (bf16 unless ``dtype``): the
+    statistics plus the softmax in that dtype times the table. Work per call:
+    2 rows vocab d flops on the matrix cores; bytes: logits read twice
+    (statistics, then the product's A operand), the table read once, 20 B of
+    statistics and 4 d B of product per row."""
     import torch
     import row_softmax_statistics_amd as rs
     import synthetic as syn
     dev = w.logits.device
-    embed = syn.embedding(w.vocab, d, seed=21, device=dev)
+    embed = syn.embedding(w.vocab, d, seed=21, device=dev, dtype=dtype or torch.bfloat16)
     out = (torch.empty(w.rows, dtype=torch.int64, device=dev),
            torch.empty(w.rows, dtype=torch.int64, device=dev),
            torch.empty(w.rows, dtype=torch.float32, device=dev),
@@ -316,7 +317,7 @@ PROFILE_PLAN = [
     ("C5", ["rowstats_kernel<1, true>"]),
     ("C4", ["kept_rows_kernel", "topk_kernel<true>"]),
     ("S4", ["stash_rows_kernel", "topk_kernel<true>"]),
-    ("SC", ["rowstats_kernel<0, true>", "selfcond_gemm_kernel<true>", "selfcond_reduce_kernel"]),
+    ("SC", ["rowstats_kernel<0, true>", "selfcond_gemm_kernel<true, false>", "selfcond_reduce_kernel"]),
 ]
 PROFILE_LAUNCHES = 21  # per workload: 1 untimed + 20 timed calls
 
@@ -463,6 +464,10 @@ def main():
         sc = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in sc.items()}
         line["selfcond"] = {"workload": f"C2 logits x bf16 embedding [262144, {SELFCOND_D}]",
                             "bound": "mfma", "peak_tflops": MFMA_BF16_PEAK_TFLOPS, **sc}
+        # the same with the fp16 model dtype (fp16 matrix cores, the same dense peak)
+        sc16 = bench_selfcond(w, SELFCOND_D, max(5, args.steps // 4), 2, torch.float16)
+        line["selfcond"]["fp16"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                    for k, v in sc16.items() if k in ("ms", "tflops", "mfma_frac")}
     del w
     torch.cuda.empty_cache()
     # the three V = 262144 row-statistics workloads the 75 % target covers,

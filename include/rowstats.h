@@ -121,29 +121,31 @@ int rowstats_run_noalloc(const float *logits, int64_t row_stride, int64_t rows,
 /*
  * The row statistics of rowstats_run (without probs) and the
  * self-conditioning input of the denoise step: the softmax of each row in
- * bf16 (the model dtype) times the token embedding table, computed on the
- * matrix cores without writing the probabilities,
- *   out[r, j] = sum_c bf16(softmax(s_r))[c] * E[c, j],
- * bf16(p) being the probabilities rowstats_run writes with
- * ROWSTATS_PROBS_BF16 (each within one bf16 unit of the exact rounding).
+ * the model dtype (bf16 or fp16) times the token embedding table, computed
+ * on the matrix cores without writing the probabilities,
+ *   out[r, j] = sum_c q_r[c] * E[c, j],   q_r = dtype(softmax(s_r)),
+ * q_r being the probabilities rowstats_run writes with the same probs_dtype
+ * (each within one unit of the exact rounding).
  * Defined by: diffusion_gemma_sampler page, module docstring (the softmax is
  * produced in the model dtype for the self-conditioning matmul); the
  * statistics as for rowstats_run.
  *
  *   logits ... seed, argmax, sample, entropy   as for rowstats_run.
- *   embed       bf16 [vocab, d] row-major (row c is token c's embedding),
- *               16-byte aligned.
+ *   dtype       ROWSTATS_PROBS_BF16 or ROWSTATS_PROBS_FP16: the model dtype,
+ *               of the probabilities and of embed.
+ *   embed       [vocab, d] row-major in that dtype (row c is token c's
+ *               embedding), 16-byte aligned.
  *   d           embedding width: a multiple of 256, 256 <= d <= 2^20.
  *   out         fp32 [rows, d] row-major, 16-byte aligned: fp32 sums of the
- *               bf16 products, added in a fixed order (repeat calls give
- *               the same bits).
+ *               products (exact in fp32), added in a fixed order (repeat
+ *               calls give the same bits).
  *   Scratch: the grow-only buffer also holds 8 partial [rows, d] fp32
- *   products. Errors as for rowstats_run; ROWSTATS_ERR_SHAPE also for a bad
- *   d or alignment.
+ *   products. Errors as for rowstats_run; ROWSTATS_ERR_DTYPE for another
+ *   dtype, ROWSTATS_ERR_SHAPE also for a bad d or alignment.
  */
 int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows,
                       int64_t vocab, const float *temps, int64_t canvas_len,
-                      uint64_t seed, const void *embed, int64_t d,
+                      uint64_t seed, int dtype, const void *embed, int64_t d,
                       int64_t *argmax, int64_t *sample, float *entropy,
                       float *out, void *stream);
 

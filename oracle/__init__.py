@@ -202,22 +202,31 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
         np.float64)
 
 
+def fp16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE half bit patterns (uint16) -> float64 values (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
 def selfcond(logits: np.ndarray, row_ids, temps, canvas_len: int, embed_bits: np.ndarray,
-             block: int = 16384) -> np.ndarray:
+             block: int = 16384, dtype: int = PROBS_BF16) -> np.ndarray:
     """Self-conditioning input of the given rows (diffusion_gemma_sampler page,
     module docstring: the softmax in the model dtype feeds the self-conditioning
-    matmul): out[i, :] = sum_c bf16(p_i)[c] * E[c, :], where bf16(p_i) are this
-    oracle's probabilities of row ``row_ids[i]`` rounded once to bf16
-    (``rowstats`` with PROBS_BF16) and ``embed_bits`` is E as bf16 bit patterns
-    [vocab, d]. Products and sums in float64, the vocab taken ``block``
-    columns at a time (a float64 matrix product per block).
+    matmul): out[i, :] = sum_c q_i[c] * E[c, :], where q_i are this oracle's
+    probabilities of row ``row_ids[i]`` rounded once to the model dtype
+    (``rowstats`` with PROBS_BF16 or PROBS_FP16, ``dtype``) and
+    ``embed_bits`` is E as bit patterns of the same dtype [vocab, d]. Products
+    and sums in float64, the vocab taken ``block`` columns at a time (a
+    float64 matrix product per block).
     """
-    ref = rowstats(logits, row_ids, temps, canvas_len, 0, PROBS_BF16)
-    p = bf16_to_f64(ref["probs"])
+    if dtype not in (PROBS_BF16, PROBS_FP16):
+        raise ValueError("dtype must be PROBS_BF16 or PROBS_FP16")
+    to_f64 = bf16_to_f64 if dtype == PROBS_BF16 else fp16_to_f64
+    ref = rowstats(logits, row_ids, temps, canvas_len, 0, dtype)
+    p = to_f64(ref["probs"])
     vocab, d = embed_bits.shape
     if vocab != p.shape[1]:
         raise ValueError("embed must have one row per logits column")
     out = np.zeros((p.shape[0], d), np.float64)
     for c0 in range(0, vocab, block):
-        out += p[:, c0:c0 + block] @ bf16_to_f64(embed_bits[c0:c0 + block])
+        out += p[:, c0:c0 + block] @ to_f64(embed_bits[c0:c0 + block])
     return out

@@ -39,8 +39,8 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "rowstats_selfcond": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
-        ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+        ctypes.c_int64, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "topk_logprobs": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -195,9 +195,10 @@ def sample_row_stats_noalloc(logits: torch.Tensor, temps: torch.Tensor, canvas_l
 def selfcond_embed(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int, seed: int,
                    embed: torch.Tensor, *, out=None):
     """The row statistics (as ``sample_row_stats`` without probs) and the
-    self-conditioning input: each row's softmax in bf16 times ``embed``
-    (bf16 [vocab, d], d a multiple of 256), accumulated in fp32, computed
-    without writing the probabilities.
+    self-conditioning input: each row's softmax in the model dtype times
+    ``embed`` ([vocab, d] in bfloat16 or float16, which sets that dtype; d a
+    multiple of 256), accumulated in fp32, computed without writing the
+    probabilities.
 
     Returns ``(argmax int64, sample int64, entropy fp32, out fp32 [rows, d])``.
     ``out`` may pass preallocated ``(argmax, sample, entropy, out)``.
@@ -206,9 +207,10 @@ def selfcond_embed(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int, s
     rows, vocab = logits.shape
     dev = logits.device
     _check_temps(temps, rows, canvas_len, dev)
-    if (embed.dtype != torch.bfloat16 or embed.device != dev or embed.dim() != 2
-            or embed.shape[0] != vocab or not embed.is_contiguous()):
-        raise ValueError("embed must be a contiguous bfloat16 [vocab, d] tensor on the logits' device")
+    if (embed.dtype not in (torch.bfloat16, torch.float16) or embed.device != dev
+            or embed.dim() != 2 or embed.shape[0] != vocab or not embed.is_contiguous()):
+        raise ValueError("embed must be a contiguous bfloat16 or float16 [vocab, d] tensor on "
+                         "the logits' device")
     d = embed.shape[1]
     if out is None:
         out = (torch.empty(rows, dtype=torch.int64, device=dev),
@@ -222,8 +224,8 @@ def selfcond_embed(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int, s
     _check_out(res, "out", (rows, d), torch.float32, dev)
     rc = lib().rowstats_selfcond(
         _ptr(logits), logits.stride(0) if rows > 1 else vocab, rows, vocab, _ptr(temps),
-        canvas_len, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(embed), d, _ptr(argmax),
-        _ptr(sample), _ptr(entropy), _ptr(res), _stream_ptr(dev))
+        canvas_len, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), PROBS_CODES[embed.dtype],
+        _ptr(embed), d, _ptr(argmax), _ptr(sample), _ptr(entropy), _ptr(res), _stream_ptr(dev))
     _check(rc, "rowstats_selfcond")
     return argmax, sample, entropy, res
 

@@ -406,13 +406,15 @@ int rowstats_run_noalloc(const float *logits, int64_t row_stride, int64_t rows, 
 }
 
 int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows, int64_t vocab,
-                      const float *temps, int64_t canvas_len, uint64_t seed, const void *embed,
-                      int64_t d, int64_t *argmax, int64_t *sample, float *entropy, float *out,
-                      void *stream) {
+                      const float *temps, int64_t canvas_len, uint64_t seed, int dtype,
+                      const void *embed, int64_t d, int64_t *argmax, int64_t *sample,
+                      float *entropy, float *out, void *stream) {
   g_last_error.clear();
   int rc = check_rowstats_args(logits, row_stride, rows, vocab, temps, canvas_len,
                                ROWSTATS_PROBS_NONE, argmax, sample, entropy, nullptr);
   if (rc || rows == 0) return rc;
+  if (dtype != ROWSTATS_PROBS_BF16 && dtype != ROWSTATS_PROBS_FP16)
+    return fail(ROWSTATS_ERR_DTYPE, "dtype must be ROWSTATS_PROBS_BF16 or _FP16, got %d", dtype);
   if (!embed || !out) return fail(ROWSTATS_ERR_NULL, "embed or out is NULL");
   if (d < kSelfCondDMultiple || d % kSelfCondDMultiple != 0 || d > (1 << 20))
     return fail(ROWSTATS_ERR_SHAPE, "d must be a multiple of %d in [%d, 2^20], got %lld",
@@ -464,6 +466,7 @@ int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows, int
   q.m_tiles = (int32_t)m_tiles;
   q.n_tiles = (int32_t)n_tiles;
   q.vec_ok = ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) && (row_stride % 4 == 0);
+  q.f16 = dtype == ROWSTATS_PROBS_FP16;
   e = selfcond_launch(q, s);
   if (e != hipSuccess) return fail_hip(e, "self-conditioning kernel launch");
   dev->grow.epoch = p.epoch;

@@ -27,13 +27,14 @@ struct SelfCondParams {
   uint32_t slot_mul;    // row / canvas_len = (row * slot_mul) >> slot_shift
   uint32_t slot_shift;
   const uint64_t *rowres;  // [rows] row results {m, 1 / S} of the row-statistics kernel
-  const uint16_t *E;       // bf16 [vocab, d], 16-byte aligned
+  const uint16_t *E;       // bf16 or fp16 (f16) [vocab, d], 16-byte aligned
   float *partial;          // [kSelfCondSplits, rows, d] fp32 scratch
   float *out;              // [rows, d] fp32, 16-byte aligned
   int32_t k_per_split;     // vocab columns of one range, a multiple of kSelfCondStepK
   int32_t m_tiles;
   int32_t n_tiles;
   int32_t vec_ok;          // logits 16-byte aligned and ld % 4 == 0
+  int32_t f16;             // model dtype fp16 (else bf16): probabilities and E
 };
 
 // Queues the GEMM over all ranges and the fixed-order sum of the partials.

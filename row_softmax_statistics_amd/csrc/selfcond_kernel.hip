@@ -31,6 +31,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 namespace rowstats {
 namespace {
 
@@ -43,6 +45,8 @@ constexpr int kEPitch = kTileN + 32;        // LDS row pitch (bf16) of the E til
 constexpr float kLog2e = 1.44269504088896340736f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -50,9 +54,13 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+// Two probabilities rounded to nearest-even in the model dtype (bf16, or fp16
+// with F16), packed a in the low half.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_p(float a, float b) {
   const f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // The staged operands of one thread for one step of 32 vocab columns:
@@ -109,7 +117,7 @@ __device__ __forceinline__ void load_tail(const float *xr, int32_t xk, const uin
 // bf16 probabilities of the staged logits into the P tile (row t / 4,
 // columns 8 (t % 4) ..); the E rows into the E tile as they are (row k of
 // the tile is vocab row k of the step).
-template <ScaleMode MODE>
+template <bool F16, ScaleMode MODE>
 __device__ __forceinline__ void store_stage(const RowConst &rcst, const Stage &st, uint16_t *sP,
                                             uint16_t *sE, int t) {
   uint32_t w[4];
@@ -127,7 +135,7 @@ __device__ __forceinline__ void store_stage(const RowConst &rcst, const Stage &s
       const float dm = fmaxf(s - rcst.m, -FLT_MAX);
       v[h] = __builtin_amdgcn_exp2f(fmaf(dm, kLog2e, 32.0f)) * rcst.inv_s;
     }
-    w[i] = pack_bf16(v[0], v[1]);
+    w[i] = pack_p<F16>(v[0], v[1]);
   }
   *reinterpret_cast<uint4 *>(sP + (t >> 2) * kPitch + 8 * (t & 3)) =
       make_uint4(w[0], w[1], w[2], w[3]);
@@ -144,6 +152,7 @@ __device__ __forceinline__ void store_stage(const RowConst &rcst, const Stage &s
 // lanes, lane j names 4 consecutive elements (row j / 4, columns 4 (j % 4) ..
 // of a 4 x 16 block) and receives element j % 4 of the rows named by lanes
 // j / 4, 4 + j / 4, 8 + j / 4, 12 + j / 4, i.e. column j of the block.
+template <bool F16>
 __device__ __forceinline__ void mfma_step(const uint16_t *cP, const uint16_t *cE, int wm, int wn,
                                           int lane, f32x16 (&acc)[2][4]) {
   // this lane's element of the 4 x 16 blocks: rows 8 (lane / 32) + (lane % 16) / 4,
@@ -153,10 +162,11 @@ __device__ __forceinline__ void mfma_step(const uint16_t *cP, const uint16_t *cE
 #pragma unroll
   for (int kk = 0; kk < kStepK; kk += 16) {
     const int kq = kk + 8 * (lane >> 5);
-    bf16x8 a[2], e[4];
+    using Op = std::conditional_t<F16, f16x8, bf16x8>;
+    Op a[2], e[4];
 #pragma unroll
     for (int bm = 0; bm < 2; ++bm)
-      a[bm] = *reinterpret_cast<const bf16x8 *>(cP + (64 * wm + 32 * bm + (lane & 31)) * kPitch + kq);
+      a[bm] = *reinterpret_cast<const Op *>(cP + (64 * wm + 32 * bm + (lane & 31)) * kPitch + kq);
 #pragma unroll
     for (int bn = 0; bn < 4; ++bn) {
       const uint16_t *q = eb + kk * kEPitch + 32 * bn;
@@ -165,13 +175,16 @@ __device__ __forceinline__ void mfma_step(const uint16_t *cP, const uint16_t *cE
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4 *)(__attribute__((address_space(3))) const uint16_t *)(q + 4 * kEPitch));
       const i16x4 both[2] = {lo, hi};
-      e[bn] = __builtin_bit_cast(bf16x8, both);
+      e[bn] = __builtin_bit_cast(Op, both);
     }
 #pragma unroll
     for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn)
-        acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bm], e[bn], acc[bm][bn], 0, 0, 0);
+        if constexpr (F16)
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[bm], e[bn], acc[bm][bn], 0, 0, 0);
+        else
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bm], e[bn], acc[bm][bn], 0, 0, 0);
   }
 }
 
@@ -181,7 +194,7 @@ __device__ __forceinline__ void mfma_step(const uint16_t *cP, const uint16_t *cE
 // (the last full step again past the end) and does the MFMA work on buffer
 // i % 2; waves 0-3 do the MFMA work first, waves 4-7 last, so that the two
 // waves sharing a SIMD overlap their matrix and vector work.
-template <bool VEC, ScaleMode MODE, bool MFMA_FIRST>
+template <bool VEC, bool F16, ScaleMode MODE, bool MFMA_FIRST>
 __device__ __forceinline__ void full_steps(int nfull, const float *xr, const uint16_t *er,
                                            int64_t d, const RowConst &rcst, Stage &st,
                                            uint16_t (*sP)[kTileM * kPitch],
@@ -190,15 +203,15 @@ __device__ __forceinline__ void full_steps(int nfull, const float *xr, const uin
   const int lane = t & 63;
   for (int i = 0; i < nfull; ++i) {
     const int j = min(i + 2, nfull - 1);
-    if constexpr (MFMA_FIRST) mfma_step(sP[i & 1], sE[i & 1], wm, wn, lane, acc);
-    store_stage<MODE>(rcst, st, sP[(i + 1) & 1], sE[(i + 1) & 1], t);
+    if constexpr (MFMA_FIRST) mfma_step<F16>(sP[i & 1], sE[i & 1], wm, wn, lane, acc);
+    store_stage<F16, MODE>(rcst, st, sP[(i + 1) & 1], sE[(i + 1) & 1], t);
     load_full<VEC>(xr + (int64_t)j * kStepK, er + (int64_t)j * kStepK * d, d, st);
-    if constexpr (!MFMA_FIRST) mfma_step(sP[i & 1], sE[i & 1], wm, wn, lane, acc);
+    if constexpr (!MFMA_FIRST) mfma_step<F16>(sP[i & 1], sE[i & 1], wm, wn, lane, acc);
     __syncthreads();
   }
 }
 
-template <bool VEC, ScaleMode MODE>
+template <bool VEC, bool F16, ScaleMode MODE>
 __device__ __forceinline__ void gemm_range(int nfull, bool tail, int32_t kb, int32_t ke,
                                            const float *xr, const uint16_t *er, int64_t d,
                                            const RowConst &rcst, uint16_t (*sP)[kTileM * kPitch],
@@ -207,26 +220,26 @@ __device__ __forceinline__ void gemm_range(int nfull, bool tail, int32_t kb, int
   Stage st;
   if (nfull > 0) {
     load_full<VEC>(xr, er, d, st);
-    store_stage<MODE>(rcst, st, sP[0], sE[0], t);
+    store_stage<F16, MODE>(rcst, st, sP[0], sE[0], t);
     const int j = min(1, nfull - 1);
     load_full<VEC>(xr + (int64_t)j * kStepK, er + (int64_t)j * kStepK * d, d, st);
   }
   __syncthreads();
   if (t < 256)
-    full_steps<VEC, MODE, true>(nfull, xr, er, d, rcst, st, sP, sE, t, wm, wn, acc);
+    full_steps<VEC, F16, MODE, true>(nfull, xr, er, d, rcst, st, sP, sE, t, wm, wn, acc);
   else
-    full_steps<VEC, MODE, false>(nfull, xr, er, d, rcst, st, sP, sE, t, wm, wn, acc);
+    full_steps<VEC, F16, MODE, false>(nfull, xr, er, d, rcst, st, sP, sE, t, wm, wn, acc);
   if (tail) {
     const int32_t k0 = kb + nfull * kStepK;
     load_tail(xr + (int64_t)nfull * kStepK, k0 + 8 * (t & 3), er + (int64_t)nfull * kStepK * d,
               k0 + 4 * (t >> 6), d, ke, st);
-    store_stage<MODE>(rcst, st, sP[nfull & 1], sE[nfull & 1], t);
+    store_stage<F16, MODE>(rcst, st, sP[nfull & 1], sE[nfull & 1], t);
     __syncthreads();
-    mfma_step(sP[nfull & 1], sE[nfull & 1], wm, wn, t & 63, acc);
+    mfma_step<F16>(sP[nfull & 1], sE[nfull & 1], wm, wn, t & 63, acc);
   }
 }
 
-template <bool VEC>
+template <bool VEC, bool F16>
 __global__ __launch_bounds__(kThreads, 1) void selfcond_gemm_kernel(SelfCondParams p) {
   __shared__ __align__(16) uint16_t sP[2][kTileM * kPitch];
   __shared__ __align__(16) uint16_t sE[2][kStepK * kEPitch];
@@ -276,11 +289,11 @@ __global__ __launch_bounds__(kThreads, 1) void selfcond_gemm_kernel(SelfCondPara
   const bool all_one = __ballot(tc != 1.0f) == 0;
   const bool all_fast = __ballot(tc >= 2.0f) == 0;
   if (all_one)
-    gemm_range<VEC, kScaleOne>(nfull, tail, kb, ke, xr, er, p.d, rcst, sP, sE, t, wm, wn, acc);
+    gemm_range<VEC, F16, kScaleOne>(nfull, tail, kb, ke, xr, er, p.d, rcst, sP, sE, t, wm, wn, acc);
   else if (all_fast)
-    gemm_range<VEC, kScaleFast>(nfull, tail, kb, ke, xr, er, p.d, rcst, sP, sE, t, wm, wn, acc);
+    gemm_range<VEC, F16, kScaleFast>(nfull, tail, kb, ke, xr, er, p.d, rcst, sP, sE, t, wm, wn, acc);
   else
-    gemm_range<VEC, kScaleAny>(nfull, tail, kb, ke, xr, er, p.d, rcst, sP, sE, t, wm, wn, acc);
+    gemm_range<VEC, F16, kScaleAny>(nfull, tail, kb, ke, xr, er, p.d, rcst, sP, sE, t, wm, wn, acc);
 
   // partial tile: register i of block (bm, bn) is row 8 (i / 4) + 4 (lane / 32)
   // + i % 4, column lane % 32 of the block
@@ -323,10 +336,14 @@ __global__ __launch_bounds__(256) void selfcond_reduce_kernel(const float *parti
 hipError_t selfcond_launch(const SelfCondParams &p, hipStream_t stream) {
   const int64_t grid = (int64_t)kSelfCondSplits * p.m_tiles * p.n_tiles;
   SelfCondParams arg = p;
-  if (p.vec_ok)
-    selfcond_gemm_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(arg);
-  else
-    selfcond_gemm_kernel<false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(arg);
+  const dim3 g((unsigned)grid), b(kThreads);
+  if (p.f16) {
+    if (p.vec_ok) selfcond_gemm_kernel<true, true><<<g, b, 0, stream>>>(arg);
+    else selfcond_gemm_kernel<false, true><<<g, b, 0, stream>>>(arg);
+  } else {
+    if (p.vec_ok) selfcond_gemm_kernel<true, false><<<g, b, 0, stream>>>(arg);
+    else selfcond_gemm_kernel<false, false><<<g, b, 0, stream>>>(arg);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n4 = p.rows * (int64_t)p.d / 4;

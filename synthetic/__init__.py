@@ -396,13 +396,14 @@ def stash_c4(device="cpu", K=20) -> StashWorkload:
 WORKLOADS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5}
 
 
-def embedding(vocab: int, d: int, seed: int, device="cpu", ints: bool = False) -> torch.Tensor:
-    """A seeded bf16 token-embedding table [vocab, d] for the self-conditioning
-    product: N(0, 1) values rounded to bf16, or (ints) integers in [-4, 4],
-    which bf16 holds exactly."""
+def embedding(vocab: int, d: int, seed: int, device="cpu", ints: bool = False,
+              dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """A seeded token-embedding table [vocab, d] for the self-conditioning
+    product, in the model dtype (bfloat16 or float16): N(0, 1) values
+    rounded to it, or (ints) integers in [-4, 4], which both hold exactly."""
     g = _gen(seed, device)
     if ints:
         e = torch.randint(-4, 5, (vocab, d), generator=g, device=device).to(torch.float32)
     else:
         e = torch.randn(vocab, d, generator=g, device=device, dtype=torch.float32)
-    return e.to(torch.bfloat16)
+    return e.to(dtype)

@@ -166,10 +166,11 @@ def check_properties(w, out):
 # Self-conditioning product (rowstats_selfcond). The kernel forms each
 # probability in fp32 from s - m, a fused multiply-add, exp2 and 1 / S; its
 # relative error stays below about 2^-15.8 (s - m down to -92, where bf16
-# ends), so its bf16 value can differ from the oracle's only where the exact
-# probability lies within SELFCOND_EPS of a rounding boundary, and then by one
-# unit. The fp32 sums of each of the 8 vocab ranges, then of the ranges, add
-# at most (K_range + 9) 2^-24 sum |p E| (every product exact in fp32).
+# ends), so its value in the model dtype (bf16 or fp16) can differ from the
+# oracle's only where the exact probability lies within SELFCOND_EPS of a
+# rounding boundary, and then by one unit. The fp32 sums of each of the 8
+# vocab ranges, then of the ranges, add at most (K_range + 9) 2^-24 sum |p E|
+# (every product of two bf16 or two fp16 values is exact in fp32).
 SELFCOND_EPS = 2.0 ** -14
 SELFCOND_SPLITS = 8
 
@@ -185,12 +186,22 @@ def bf16_ulp(q: np.ndarray) -> np.ndarray:
     return np.where(q >= 2.0 ** -126, 2.0 ** (e - 7), 2.0 ** -133)
 
 
-def selfcond_bound(x: np.ndarray, rows, temps, canvas_len: int, embed_bits: np.ndarray):
-    """Per-element bound of |gpu - oracle| for the rows' products (see above)."""
+def fp16_ulp(q: np.ndarray) -> np.ndarray:
+    """Unit in the last place of fp16 values q >= 0 (2^-24 below 2^-14)."""
+    e = np.floor(np.log2(np.maximum(q, 2.0 ** -14)))
+    return np.where(q >= 2.0 ** -14, 2.0 ** (e - 10), 2.0 ** -24)
+
+
+def selfcond_bound(x: np.ndarray, rows, temps, canvas_len: int, embed_bits: np.ndarray,
+                   f16: bool = False):
+    """Per-element bound of |gpu - oracle| for the rows' products (see above);
+    f16: the model dtype is fp16 (else bf16)."""
     rows = np.asarray(rows, dtype=np.int64)
-    ref = oracle.rowstats(x, rows, temps, canvas_len, 0, oracle.PROBS_BF16)
-    q = oracle.bf16_to_f64(ref["probs"])
-    ulp = bf16_ulp(q)
+    code = oracle.PROBS_FP16 if f16 else oracle.PROBS_BF16
+    to_f64 = oracle.fp16_to_f64 if f16 else oracle.bf16_to_f64
+    ref = oracle.rowstats(x, rows, temps, canvas_len, 0, code)
+    q = to_f64(ref["probs"])
+    ulp = fp16_ulp(q) if f16 else bf16_ulp(q)
     w = np.empty_like(q)
     for i, r in enumerate(rows):
         s = oracle.scale_row(x[i], float(np.asarray(temps)[r // canvas_len])).astype(np.float64)
@@ -202,7 +213,7 @@ def selfcond_bound(x: np.ndarray, rows, temps, canvas_len: int, embed_bits: np.n
         w[i] = amb * ulp[i] + (selfcond_k_range(x.shape[1]) + 9) * 2.0 ** -24 * (q[i] + ulp[i])
     bound = np.zeros((len(rows), embed_bits.shape[1]))
     for c0 in range(0, embed_bits.shape[0], 16384):
-        bound += w[:, c0:c0 + 16384] @ np.abs(oracle.bf16_to_f64(embed_bits[c0:c0 + 16384]))
+        bound += w[:, c0:c0 + 16384] @ np.abs(to_f64(embed_bits[c0:c0 + 16384]))
     return bound + 2.0 ** -140
 
 
@@ -217,9 +228,11 @@ def compare_selfcond(w, embed: torch.Tensor, out, rows, label=""):
     x = host_rows(w.logits, rows)
     eb = embed.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     temps = w.temps.cpu().numpy()
-    ref = oracle.selfcond(x, rows, temps, w.canvas_len, eb)
+    f16 = embed.dtype == torch.float16
+    ref = oracle.selfcond(x, rows, temps, w.canvas_len, eb,
+                          dtype=oracle.PROBS_FP16 if f16 else oracle.PROBS_BF16)
     got = res[torch.as_tensor(rows, device=res.device)].double().cpu().numpy()
-    bound = selfcond_bound(x, rows, temps, w.canvas_len, eb)
+    bound = selfcond_bound(x, rows, temps, w.canvas_len, eb, f16)
     err = np.abs(got - ref)
     ratio = err / bound
     k = np.unravel_index(np.argmax(ratio), ratio.shape)

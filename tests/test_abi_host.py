@@ -117,10 +117,10 @@ def test_topk_rejects(kwargs, code):
     assert rs.last_error() != ""
 
 
-def selfcond(logits=FAKE, stride=8, rows=4, vocab=8, temps=FAKE, canvas=2, seed=1,
+def selfcond(logits=FAKE, stride=8, rows=4, vocab=8, temps=FAKE, canvas=2, seed=1, dtype=1,
              embed=FAKE, d=256, argmax=FAKE, sample=FAKE, entropy=FAKE, out=FAKE):
-    return rs.lib().rowstats_selfcond(logits, stride, rows, vocab, temps, canvas, seed, embed, d,
-                                      argmax, sample, entropy, out, NULL)
+    return rs.lib().rowstats_selfcond(logits, stride, rows, vocab, temps, canvas, seed, dtype,
+                                      embed, d, argmax, sample, entropy, out, NULL)
 
 
 @pytest.mark.parametrize("kwargs,code", [
@@ -128,6 +128,8 @@ def selfcond(logits=FAKE, stride=8, rows=4, vocab=8, temps=FAKE, canvas=2, seed=
     (dict(vocab=0), ERR_SHAPE),
     (dict(stride=7), ERR_SHAPE),
     (dict(canvas=0), ERR_SHAPE),
+    (dict(dtype=0), ERR_DTYPE),
+    (dict(dtype=3), ERR_DTYPE),
     (dict(d=0), ERR_SHAPE),
     (dict(d=128), ERR_SHAPE),
     (dict(d=300), ERR_SHAPE),

@@ -1,5 +1,6 @@
-"""Parity of rowstats_selfcond (the bf16 softmax times the embedding table,
-on the matrix cores) with the oracle, through the C ABI.
+"""Parity of rowstats_selfcond (the softmax in the model dtype, bf16 or fp16,
+times the embedding table, on the matrix cores) with the oracle, through the
+C ABI.
 
 The statistics must equal rowstats_run's; the product must lie within the
 bound derived in tests/parity.py (one bf16 unit on probabilities within
@@ -38,6 +39,35 @@ def test_small_shapes(rows, vocab, d, pad):
     out = run(w, embed)
     worst = compare_selfcond(w, embed, out, range(rows), f"selfcond {rows}x{vocab} d={d}")
     record(f"selfcond {rows}x{vocab} d={d}", worst_error_over_bound=round(worst, 4))
+    done()
+
+
+@pytest.mark.parametrize("rows,vocab,d,pad", [
+    (5, 31, 256, 3), (33, 2049, 256, 1), (257, 20000, 512, 4), (40, 70001, 768, 0),
+    (3, 262144, 256, 0)])
+def test_small_shapes_fp16(rows, vocab, d, pad):
+    # the fp16 model dtype: probabilities and table in IEEE half, fp16 matrix cores
+    w = syn.random_case(DEV, rows=rows, vocab=vocab, canvas_len=3, seed=vocab + d + 7,
+                        ld=vocab + pad, t_choices=(0.0, 0.6, 1.0, 98.0))
+    embed = syn.embedding(vocab, d, seed=vocab + 1, device=DEV, dtype=torch.float16)
+    out = run(w, embed)
+    worst = compare_selfcond(w, embed, out, range(rows), f"selfcond fp16 {rows}x{vocab} d={d}")
+    record(f"selfcond fp16 {rows}x{vocab} d={d}", worst_error_over_bound=round(worst, 4))
+    done()
+
+
+def test_fp16_closed_forms():
+    # uniform rows: p = 2^-12 exactly, small-integer E: the column mean bit for
+    # bit; greedy rows: the argmax's embedding bit for bit
+    vocab, d = 4096, 512
+    x = torch.full((3, vocab), 0.5, device=DEV)
+    embed = syn.embedding(vocab, d, seed=19, device=DEV, ints=True, dtype=torch.float16)
+    _, _, _, out = rs.selfcond_embed(x, torch.tensor([1.0, 0.4, 7.0], device=DEV), 1, 5, embed)
+    assert torch.equal(out, embed.float().mean(dim=0).expand(3, d))
+    w = syn.random_case(DEV, rows=20, vocab=30000, canvas_len=5, seed=18, t_choices=(0.0,))
+    e2 = syn.embedding(w.vocab, 768, seed=20, device=DEV, dtype=torch.float16)
+    a, _, _, out2 = run(w, e2)
+    assert torch.equal(out2, e2[a].float())
     done()
 
 
@@ -101,6 +131,15 @@ def test_c2_full_size_d2560():
     g = torch.nonzero(greedy).flatten()
     assert torch.equal(out[3][g], embed[out[0][g]].float())
     record("selfcond C2 d=2560", rows_compared=len(rows), greedy_rows_exact=int(g.numel()),
+           worst_error_over_bound=round(worst, 4))
+    del out, embed
+    # the fp16 model dtype at the same size: one seeded row per slot
+    embed = syn.embedding(w.vocab, 2560, seed=23, device=DEV, dtype=torch.float16)
+    out = run(w, embed)
+    rows16 = (256 * np.arange(16) + rng.integers(0, 256, 16)).tolist()
+    worst = compare_selfcond(w, embed, out, rows16, "selfcond fp16 C2 d=2560")
+    assert torch.equal(out[3][g], embed[out[0][g]].float())
+    record("selfcond fp16 C2 d=2560", rows_compared=len(rows16), greedy_rows_exact=int(g.numel()),
            worst_error_over_bound=round(worst, 4))
     del out, embed, w
     done()

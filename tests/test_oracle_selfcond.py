@@ -104,3 +104,61 @@ def test_vocab_permutation_and_linearity():
     perm = rng.permutation(vocab)
     np.testing.assert_allclose(oracle.selfcond(x[:, perm].copy(), [0, 1, 2], [0.9], 3, e1[perm]),
                                a, rtol=1e-13, atol=1e-15)
+
+
+# --- fp16 model dtype (the same product with probabilities and E in IEEE half)
+def fp16_bits(a) -> np.ndarray:
+    """IEEE half bit patterns of float values, rounded to nearest-even by numpy."""
+    return np.asarray(a, np.float32).astype(np.float16).view(np.uint16)
+
+
+def test_fp16_uniform_rows_give_the_column_mean():
+    # p = 2^-12 is exact in fp16 too
+    vocab, d = 4096, 16
+    rng = np.random.default_rng(11)
+    e = rng.integers(-4, 5, size=(vocab, d)).astype(np.float32)
+    out = oracle.selfcond(np.full((2, vocab), -3.0, np.float32), [0, 1], [0.7, 1.0], 1,
+                          fp16_bits(e), dtype=oracle.PROBS_FP16)
+    assert np.array_equal(out, np.repeat(e.astype(np.float64).mean(axis=0)[None], 2, axis=0))
+
+
+def test_fp16_greedy_ties_share_the_mass():
+    # 1/3 rounded to fp16 (11 significant bits) differs from its bf16 rounding
+    vocab, d, k = 200, 6, 3
+    rng = np.random.default_rng(12)
+    e = rng.integers(-4, 5, size=(vocab, d)).astype(np.float32)
+    x = np.zeros((1, vocab), np.float32)
+    cols = np.array([3, 90, 150])
+    x[0, cols] = 1.0
+    out = oracle.selfcond(x, [0], [0.0], 1, fp16_bits(e), dtype=oracle.PROBS_FP16)
+    share = float(np.float16(1.0 / k))
+    assert share != oracle.bf16_to_f64(bf16_bits([1.0 / k]))[0]
+    assert np.array_equal(out[0], share * e[cols].astype(np.float64).sum(axis=0))
+
+
+def test_fp16_brute_force_small_and_subnormal_probabilities():
+    # one dominant column drives the others' probabilities into the fp16
+    # subnormal range (below 2^-14), where they keep a few bits or flush to 0
+    rng = np.random.default_rng(13)
+    vocab, d, rows = 40, 5, 4
+    x = (rng.standard_normal((rows, vocab)) * 0.5).astype(np.float32)
+    x[:, 7] += 12.0
+    e = rng.standard_normal((vocab, d)).astype(np.float32)
+    eb = fp16_bits(e)
+    ev = eb.view(np.float16).astype(np.float64)
+    out = oracle.selfcond(x, np.arange(rows), [1.0, 0.9], 2, eb, block=16, dtype=oracle.PROBS_FP16)
+    probs = oracle.rowstats(x, np.arange(rows), [1.0, 0.9], 2, 0, oracle.PROBS_FP16)["probs"]
+    p = probs.view(np.float16).astype(np.float64)
+    assert np.any((p > 0) & (p < 2.0 ** -14)), "the case must reach fp16 subnormals"
+    for r in range(rows):
+        for j in range(d):
+            acc = 0.0
+            for c in range(vocab):
+                acc += p[r, c] * ev[c, j]
+            assert abs(out[r, j] - acc) <= 1e-15 * (1 + abs(acc))
+
+
+def test_dtype_is_checked():
+    with pytest.raises(ValueError):
+        oracle.selfcond(np.zeros((1, 4), np.float32), [0], [1.0], 1, np.zeros((4, 2), np.uint16),
+                        dtype=oracle.PROBS_NONE)

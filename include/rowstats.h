@@ -8,8 +8,9 @@
  * after a call returns. Work is queued asynchronously on `stream` (a
  * hipStream_t passed as void*, NULL = the default stream): buffers must stay
  * alive until that stream has been synchronised. rowstats_run,
- * rowstats_selfcond, topk_logprobs and stash_converged_logprobs share a grow-only scratch
- * buffer per device: a call queued on another stream than the previous one
+ * rowstats_selfcond, rowstats_selfcond_product, topk_logprobs and
+ * stash_converged_logprobs share grow-only scratch buffers per device: a call
+ * queued on another stream than the previous one
  * first waits, on the device, for that previous call (an event wait), so
  * calls from several streams run one after another. rowstats_run_noalloc
  * has a fixed scratch array of its own (see there).
@@ -139,8 +140,8 @@ int rowstats_run_noalloc(const float *logits, int64_t row_stride, int64_t rows,
  *   out         fp32 [rows, d] row-major, 16-byte aligned: fp32 sums of the
  *               products (exact in fp32), added in a fixed order (repeat
  *               calls give the same bits).
- *   Scratch: the grow-only buffer also holds 8 partial [rows, d] fp32
- *   products. Errors as for rowstats_run; ROWSTATS_ERR_DTYPE for another
+ *   Scratch: the grow-only scratch, and a grow-only buffer of 8 partial
+ *   [rows, d] fp32 products. Errors as for rowstats_run; ROWSTATS_ERR_DTYPE for another
  *   dtype, ROWSTATS_ERR_SHAPE also for a bad d or alignment.
  */
 int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows,
@@ -148,6 +149,57 @@ int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows,
                       uint64_t seed, int dtype, const void *embed, int64_t d,
                       int64_t *argmax, int64_t *sample, float *entropy,
                       float *out, void *stream);
+
+/*
+ * The self-conditioning input from given probabilities, for callers that
+ * keep the probabilities (rowstats_run with probs) and the embedding table
+ * in the packed order below: out = P E on the matrix cores, E read straight
+ * into matrix-core registers (no pass through LDS), P through LDS.
+ * Defined by: diffusion_gemma_sampler page, module docstring (the softmax in
+ * the model dtype feeds the self-conditioning matmul).
+ *
+ * rowstats_packed_embed_bytes: bytes of the packed table of a [vocab, d]
+ *   embedding, ceil(vocab / 128) * 128 * d * 2; or ROWSTATS_ERR_SHAPE for a
+ *   vocab outside [1, 2^31 - 1 - 65536] or a d that is not a multiple of 256
+ *   in [256, 2^20].
+ *
+ * rowstats_pack_embed: queues the packing of `embed` into `packed`, once per
+ *   table (the table is a weight; repeat products reuse the packed copy).
+ *   embed       [vocab, d] row-major, 2-byte elements (bf16 or fp16 as
+ *               `dtype` says; the packing moves bits only), 2-byte aligned.
+ *   packed      rowstats_packed_embed_bytes(vocab, d) bytes, 16-byte
+ *               aligned, caller-owned: blocks of 32 vocab rows x 32 columns,
+ *               block (b, j) at element (b * d / 32 + j) * 1024; inside it,
+ *               element h * 512 + l * 8 + i is E[32 b + 16 h + 8 (l / 32) + i]
+ *               [32 j + l % 32] (h < 2, l < 64, i < 8), 0 past the last row.
+ *   Errors: ROWSTATS_ERR_SHAPE (shape, alignment), _DTYPE, _NULL, _HIP.
+ *
+ * rowstats_selfcond_product:
+ *   probs       [rows, vocab] probabilities in `dtype`, element (r, c) at
+ *               probs[r * probs_stride + c], probs_stride >= vocab; 2-byte
+ *               aligned (16-byte aligned rows take the vector path).
+ *   rows        0 returns at once; <= 2^31 - 1.
+ *   vocab, d    as for rowstats_packed_embed_bytes.
+ *   dtype       ROWSTATS_PROBS_BF16 or ROWSTATS_PROBS_FP16: of probs and of
+ *               the packed table.
+ *   packed      the table packed by rowstats_pack_embed with the same vocab
+ *               and d.
+ *   out         fp32 [rows, d] row-major, 16-byte aligned:
+ *               out[r, j] = sum_c probs[r, c] * E[c, j], products exact in
+ *               fp32, summed in fp32 in a fixed order (repeat calls give the
+ *               same bits).
+ *   Scratch: the library's grow-only buffer of partial products (8 [rows, d]
+ *   fp32 tiles), shared with rowstats_selfcond and ordered with the other
+ *   calls as described at the top. Errors: ROWSTATS_ERR_SHAPE, _DTYPE,
+ *   _NULL, _HIP.
+ */
+int64_t rowstats_packed_embed_bytes(int64_t vocab, int64_t d);
+int rowstats_pack_embed(const void *embed, int64_t vocab, int64_t d, int dtype,
+                        void *packed, void *stream);
+int rowstats_selfcond_product(const void *probs, int64_t probs_stride,
+                              int64_t rows, int64_t vocab, int dtype,
+                              const void *packed, int64_t d, float *out,
+                              void *stream);
 
 /*
  * Top-K logprobs of the rows of kept slots.

@@ -10,7 +10,8 @@ docstring; ``sample_row_stats`` and ``sample_row_stats_reference``;
 arithmetic lives in ``rowstats_oracle.c`` (plain C, fp32 divide then double
 reductions); this module marshals numpy arrays through ctypes, and
 ``selfcond`` multiplies the oracle's bf16 probabilities by an embedding table
-with a float64 matrix product.
+with a float64 matrix product (``probs_product``, which also serves given
+probabilities).
 """
 from __future__ import annotations
 
@@ -220,12 +221,26 @@ def selfcond(logits: np.ndarray, row_ids, temps, canvas_len: int, embed_bits: np
     """
     if dtype not in (PROBS_BF16, PROBS_FP16):
         raise ValueError("dtype must be PROBS_BF16 or PROBS_FP16")
-    to_f64 = bf16_to_f64 if dtype == PROBS_BF16 else fp16_to_f64
     ref = rowstats(logits, row_ids, temps, canvas_len, 0, dtype)
-    p = to_f64(ref["probs"])
+    return probs_product(ref["probs"], embed_bits, block, dtype)
+
+
+def probs_product(probs_bits: np.ndarray, embed_bits: np.ndarray, block: int = 16384,
+                  dtype: int = PROBS_BF16) -> np.ndarray:
+    """The self-conditioning matmul of given probabilities (diffusion_gemma_sampler
+    page, module docstring: the model-dtype softmax times the embedding
+    table): out[i, :] = sum_c q[i, c] * E[c, :] with ``probs_bits`` q
+    [rows, vocab] and ``embed_bits`` E [vocab, d], both bit patterns of the
+    model dtype (bf16 for PROBS_BF16, fp16 for PROBS_FP16). Products and sums
+    in float64, ``block`` vocabulary rows at a time (a float64 matrix product
+    per block)."""
+    if dtype not in (PROBS_BF16, PROBS_FP16):
+        raise ValueError("dtype must be PROBS_BF16 or PROBS_FP16")
+    to_f64 = bf16_to_f64 if dtype == PROBS_BF16 else fp16_to_f64
+    p = to_f64(np.asarray(probs_bits))
     vocab, d = embed_bits.shape
     if vocab != p.shape[1]:
-        raise ValueError("embed must have one row per logits column")
+        raise ValueError("embed must have one row per probability column")
     out = np.zeros((p.shape[0], d), np.float64)
     for c0 in range(0, vocab, block):
         out += p[:, c0:c0 + block] @ to_f64(embed_bits[c0:c0 + block])

@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import atexit
 import ctypes
+import dataclasses
 import os
 
 import torch
@@ -41,6 +42,13 @@ _SIGNATURES = {
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "rowstats_packed_embed_bytes": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int64]),
+    "rowstats_pack_embed": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_void_p]),
+    "rowstats_selfcond_product": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "topk_logprobs": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -228,6 +236,55 @@ def selfcond_embed(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int, s
         _ptr(embed), d, _ptr(argmax), _ptr(sample), _ptr(entropy), _ptr(res), _stream_ptr(dev))
     _check(rc, "rowstats_selfcond")
     return argmax, sample, entropy, res
+
+
+@dataclasses.dataclass(frozen=True)
+class PackedEmbed:
+    """An embedding table in the matrix-core order of
+    ``rowstats_pack_embed`` (``data``: uint8 device bytes)."""
+    data: torch.Tensor
+    vocab: int
+    d: int
+    dtype: torch.dtype
+
+
+def pack_embed(embed: torch.Tensor) -> PackedEmbed:
+    """Packs ``embed`` ([vocab, d] bfloat16 or float16, d a multiple of 256)
+    for ``selfcond_product``; done once per table."""
+    if (embed.dtype not in (torch.bfloat16, torch.float16) or not embed.is_cuda
+            or embed.dim() != 2 or not embed.is_contiguous()):
+        raise ValueError("embed must be a contiguous bfloat16 or float16 [vocab, d] GPU tensor")
+    vocab, d = embed.shape
+    nbytes = lib().rowstats_packed_embed_bytes(vocab, d)
+    _check(int(nbytes) if nbytes < 0 else ROWSTATS_OK, "rowstats_packed_embed_bytes")
+    data = torch.empty(nbytes, dtype=torch.uint8, device=embed.device)
+    rc = lib().rowstats_pack_embed(_ptr(embed), vocab, d, PROBS_CODES[embed.dtype], _ptr(data),
+                                   _stream_ptr(embed.device))
+    _check(rc, "rowstats_pack_embed")
+    return PackedEmbed(data, vocab, d, embed.dtype)
+
+
+def selfcond_product(probs: torch.Tensor, packed: PackedEmbed, *, out=None) -> torch.Tensor:
+    """The self-conditioning input from given probabilities: ``probs``
+    ([rows, vocab] in the packed table's dtype, unit column stride) times the
+    packed embedding table, accumulated in fp32. Returns ``out`` fp32
+    [rows, d] (``out`` may pass it preallocated)."""
+    if (probs.dim() != 2 or probs.dtype != packed.dtype or probs.device != packed.data.device
+            or probs.shape[1] != packed.vocab):
+        raise ValueError("probs must be a 2-D tensor of the packed table's dtype, device and "
+                         "vocab")
+    rows, vocab = probs.shape
+    if rows > 0 and probs.stride(1) != 1:
+        raise ValueError("probs must have unit column stride")
+    dev = probs.device
+    if out is None:
+        out = torch.empty(rows, packed.d, dtype=torch.float32, device=dev)
+    _check_out(out, "out", (rows, packed.d), torch.float32, dev)
+    rc = lib().rowstats_selfcond_product(
+        _ptr(probs), probs.stride(0) if rows > 1 else vocab, rows, vocab,
+        PROBS_CODES[probs.dtype], _ptr(packed.data), packed.d, _ptr(out), _stream_ptr(dev))
+    _check(rc, "rowstats_selfcond_product")
+    return out
 
 
 def topk_logprobs(logits: torch.Tensor, temps: torch.Tensor, canvas_len: int,

@@ -9,6 +9,7 @@
 #include <string>
 
 #include "../../include/rowstats.h"
+#include "product_internal.h"
 #include "rowstats_internal.h"
 #include "selfcond_internal.h"
 #include "topk_internal.h"
@@ -73,6 +74,9 @@ struct DeviceState {
   int topk_resident[2] = {};
   Area grow;                // grow-only, shared by rowstats_run, topk_logprobs and the stash
   Area fixed;               // the fixed array of rowstats_run_noalloc
+  // grow-only fp32 partial products of the two self-conditioning entry
+  // points (untagged data, kept apart from the tagged words of `grow`)
+  Area part;
   // The stream of the last call on the grow-only scratch; a call on another
   // stream first waits (on the device) for the work queued there so far.
   hipStream_t last_stream = nullptr;
@@ -167,6 +171,26 @@ int next_epoch(Area &a, hipStream_t s, uint32_t *epoch) {
     e = 1;
   }
   *epoch = e;
+  return ROWSTATS_OK;
+}
+
+// Grow-only buffer of the self-conditioning partial products (no zeroing:
+// every element a call reads it has written first).
+int ensure_partials(DeviceState &d, size_t bytes) {
+  Area &a = d.part;
+  if (bytes <= a.bytes) return ROWSTATS_OK;
+  hipError_t e;
+  if (a.base) {
+    e = hipFree(a.base);  // waits for the work that may still use it
+    if (e != hipSuccess) return fail_hip(e, "hipFree(partial products)");
+    a.base = nullptr;
+    a.bytes = 0;
+  }
+  size_t cap = bytes + bytes / 4;
+  cap = (cap + 255) & ~(size_t)255;
+  e = hipMalloc(&a.base, cap);
+  if (e != hipSuccess) return fail_hip(e, "hipMalloc(partial products)");
+  a.bytes = cap;
   return ROWSTATS_OK;
 }
 
@@ -438,11 +462,10 @@ int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows, int
                           ROWSTATS_PROBS_NONE, argmax, sample, entropy, nullptr, p, &grid, &need,
                           &head_bytes, &tuple_bytes)))
     return rc;
-  // the partial products follow the row-statistics scratch
-  const size_t partial_at = (need + 255) & ~(size_t)255;
   const size_t partial_bytes = (size_t)kSelfCondSplits * rows * d * sizeof(float);
   if ((rc = order_after_last(*dev, s))) return rc;
-  if ((rc = ensure_grow_scratch(*dev, partial_at + partial_bytes, s))) return rc;
+  if ((rc = ensure_grow_scratch(*dev, need, s))) return rc;
+  if ((rc = ensure_partials(*dev, partial_bytes))) return rc;
   if ((rc = next_epoch(dev->grow, s, &p.epoch))) return rc;
   set_scratch(p, dev->grow, head_bytes, tuple_bytes);
   hipError_t e = rowstats_launch(p, ROWSTATS_PROBS_NONE, (int)grid, s);
@@ -459,7 +482,7 @@ int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows, int
   q.slot_shift = p.slot_shift;
   q.rowres = p.rowres;
   q.E = static_cast<const uint16_t *>(embed);
-  q.partial = reinterpret_cast<float *>(reinterpret_cast<char *>(dev->grow.base) + partial_at);
+  q.partial = static_cast<float *>(dev->part.base);
   q.out = out;
   const int64_t per = (vocab + kSelfCondSplits - 1) / kSelfCondSplits;
   q.k_per_split = (int32_t)((per + kSelfCondStepK - 1) / kSelfCondStepK * kSelfCondStepK);
@@ -470,6 +493,83 @@ int rowstats_selfcond(const float *logits, int64_t row_stride, int64_t rows, int
   e = selfcond_launch(q, s);
   if (e != hipSuccess) return fail_hip(e, "self-conditioning kernel launch");
   dev->grow.epoch = p.epoch;
+  return note_stream(*dev, s);
+}
+
+int64_t rowstats_packed_embed_bytes(int64_t vocab, int64_t d) {
+  g_last_error.clear();
+  if (vocab < 1 || vocab > kMaxVocab)
+    return fail(ROWSTATS_ERR_SHAPE, "vocab must be in [1, %lld], got %lld", (long long)kMaxVocab,
+                (long long)vocab);
+  if (d < kProductDMultiple || d % kProductDMultiple != 0 || d > (1 << 20))
+    return fail(ROWSTATS_ERR_SHAPE, "d must be a multiple of %d in [%d, 2^20], got %lld",
+                kProductDMultiple, kProductDMultiple, (long long)d);
+  return packed_embed_bytes(vocab, d);
+}
+
+int rowstats_pack_embed(const void *embed, int64_t vocab, int64_t d, int dtype, void *packed,
+                        void *stream) {
+  const int64_t bytes = rowstats_packed_embed_bytes(vocab, d);
+  if (bytes < 0) return (int)bytes;
+  if (dtype != ROWSTATS_PROBS_BF16 && dtype != ROWSTATS_PROBS_FP16)
+    return fail(ROWSTATS_ERR_DTYPE, "dtype must be ROWSTATS_PROBS_BF16 or _FP16, got %d", dtype);
+  if (!embed || !packed) return fail(ROWSTATS_ERR_NULL, "embed or packed is NULL");
+  if ((reinterpret_cast<uintptr_t>(embed) & 1) || (reinterpret_cast<uintptr_t>(packed) & 15))
+    return fail(ROWSTATS_ERR_SHAPE, "embed must be 2-byte and packed 16-byte aligned");
+  hipError_t e = pack_embed_launch(static_cast<const uint16_t *>(embed), vocab, d,
+                                   static_cast<uint16_t *>(packed),
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "packing kernel launch");
+  return ROWSTATS_OK;
+}
+
+int rowstats_selfcond_product(const void *probs, int64_t probs_stride, int64_t rows,
+                              int64_t vocab, int dtype, const void *packed, int64_t d,
+                              float *out, void *stream) {
+  g_last_error.clear();
+  if (rows < 0 || rows > 0x7FFFFFFFLL)
+    return fail(ROWSTATS_ERR_SHAPE, "rows must be in [0, 2^31 - 1], got %lld", (long long)rows);
+  if (rows == 0) return ROWSTATS_OK;
+  if (rowstats_packed_embed_bytes(vocab, d) < 0) return ROWSTATS_ERR_SHAPE;
+  if (probs_stride < vocab)
+    return fail(ROWSTATS_ERR_SHAPE, "probs_stride %lld < vocab %lld", (long long)probs_stride,
+                (long long)vocab);
+  if (dtype != ROWSTATS_PROBS_BF16 && dtype != ROWSTATS_PROBS_FP16)
+    return fail(ROWSTATS_ERR_DTYPE, "dtype must be ROWSTATS_PROBS_BF16 or _FP16, got %d", dtype);
+  if (!probs || !packed || !out) return fail(ROWSTATS_ERR_NULL, "probs, packed or out is NULL");
+  if ((reinterpret_cast<uintptr_t>(probs) & 1) || (reinterpret_cast<uintptr_t>(packed) & 15) ||
+      (reinterpret_cast<uintptr_t>(out) & 15))
+    return fail(ROWSTATS_ERR_SHAPE, "probs must be 2-byte, packed and out 16-byte aligned");
+  const int64_t m_tiles = (rows + kProductTileM - 1) / kProductTileM;
+  const int64_t n_tiles = (d + kProductTileN - 1) / kProductTileN;
+  if ((int64_t)kProductSplits * m_tiles * n_tiles > 0x7FFFFFFFLL)
+    return fail(ROWSTATS_ERR_SHAPE, "rows %lld x d %lld is too large", (long long)rows,
+                (long long)d);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState *dev = nullptr;
+  int rc;
+  if ((rc = device_state(&dev))) return rc;
+  if ((rc = order_after_last(*dev, s))) return rc;
+  if ((rc = ensure_partials(*dev, (size_t)kProductSplits * rows * d * sizeof(float)))) return rc;
+  ProductParams q = {};
+  q.P = static_cast<const uint16_t *>(probs);
+  q.ldp = probs_stride;
+  q.rows = rows;
+  q.vocab = (int32_t)vocab;
+  q.d = (int32_t)d;
+  q.packed = static_cast<const uint16_t *>(packed);
+  q.partial = static_cast<float *>(dev->part.base);
+  q.out = out;
+  const int64_t per = (vocab + kProductSplits - 1) / kProductSplits;
+  q.k_per_split = (int32_t)((per + kProductStepK - 1) / kProductStepK * kProductStepK);
+  q.m_tiles = (int32_t)m_tiles;
+  q.n_tiles = (int32_t)n_tiles;
+  q.vec_ok = ((reinterpret_cast<uintptr_t>(probs) & 15) == 0) && (probs_stride % 8 == 0);
+  q.f16 = dtype == ROWSTATS_PROBS_FP16;
+  hipError_t e = product_launch(q, s);
+  if (e != hipSuccess) return fail_hip(e, "self-conditioning product launch");
   return note_stream(*dev, s);
 }
 
@@ -624,15 +724,18 @@ int rowstats_release(void) {
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
   for (int dev = 0; dev < kMaxDevices; ++dev) {
     DeviceState &d = g_dev[dev];
-    if (!d.ready || (!d.grow.base && !d.order_event)) continue;
+    if (!d.ready || (!d.grow.base && !d.part.base && !d.order_event)) continue;
     if ((e = hipSetDevice(dev)) != hipSuccess) return fail_hip(e, "hipSetDevice");
     if ((e = hipDeviceSynchronize()) != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
     if (d.grow.base) (void)hipFree(d.grow.base);
+    if (d.part.base) (void)hipFree(d.part.base);
     if (d.order_event) (void)hipEventDestroy(d.order_event);
     // the next call on the grow-only scratch allocates it afresh (zeroed);
     // the epoch keeps counting
     d.grow.base = nullptr;
     d.grow.bytes = 0;
+    d.part.base = nullptr;
+    d.part.bytes = 0;
     d.order_event = nullptr;
     d.has_last = false;
   }

@@ -40,4 +40,10 @@ struct SelfCondParams {
 // Queues the GEMM over all ranges and the fixed-order sum of the partials.
 hipError_t selfcond_launch(const SelfCondParams &p, hipStream_t stream);
 
+// Queues out = the sum of kSelfCondSplits partial [rows, d] fp32 products
+// (consecutive, rows * d apart), added in range order; d % 4 == 0, partial
+// and out 16-byte aligned.
+hipError_t partial_sum_launch(const float *partial, int64_t rows, int32_t d, float *out,
+                              hipStream_t stream);
+
 }  // namespace rowstats

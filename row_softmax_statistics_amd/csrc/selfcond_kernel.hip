@@ -346,11 +346,15 @@ hipError_t selfcond_launch(const SelfCondParams &p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n4 = p.rows * (int64_t)p.d / 4;
+  return partial_sum_launch(p.partial, p.rows, p.d, p.out, stream);
+}
+
+hipError_t partial_sum_launch(const float *partial, int64_t rows, int32_t d, float *out,
+                              hipStream_t stream) {
+  const int64_t n4 = rows * (int64_t)d / 4;
   int64_t blocks = (n4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  selfcond_reduce_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p.partial, n4, n4,
-                                                                           p.out);
+  selfcond_reduce_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(partial, n4, n4, out);
   return hipGetLastError();
 }
 

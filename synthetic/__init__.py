@@ -407,3 +407,24 @@ def embedding(vocab: int, d: int, seed: int, device="cpu", ints: bool = False,
     else:
         e = torch.randn(vocab, d, generator=g, device=device, dtype=torch.float32)
     return e.to(dtype)
+
+
+def probabilities(rows: int, vocab: int, seed: int, device="cpu",
+                  dtype: torch.dtype = torch.bfloat16, ld: int | None = None) -> torch.Tensor:
+    """Seeded probability-like rows [rows, vocab] in the model dtype, as input
+    of the self-conditioning product of given probabilities: log-normal
+    values exp(2.5 z), z ~ N(0, 1) (the spread of the C2 logits), divided by
+    their expected row sum vocab * e^3.125, so rows sum to about 1 with a few
+    large and many tiny entries (in fp16 most of a long row lies below the
+    normal range); one column in 16 is exactly 0. With ld > vocab the rows are views into a
+    wider [rows, ld] buffer (the padding holds NaN, which must never be read)."""
+    g = _gen(seed, device)
+    z = torch.randn(rows, vocab, generator=g, device=device, dtype=torch.float32)
+    p = torch.exp(2.5 * z) / (vocab * 22.7599)
+    zero = torch.randint(0, 16, (rows, vocab), generator=g, device=device) == 0
+    p = torch.where(zero, torch.zeros_like(p), p).to(dtype)
+    if ld is None or ld == vocab:
+        return p
+    buf = torch.full((rows, ld), float("nan"), dtype=dtype, device=device)
+    buf[:, :vocab] = p
+    return buf[:, :vocab]

@@ -173,6 +173,7 @@ def check_properties(w, out):
 # (every product of two bf16 or two fp16 values is exact in fp32).
 SELFCOND_EPS = 2.0 ** -14
 SELFCOND_SPLITS = 8
+PRODUCT_STEP = 64
 
 
 def selfcond_k_range(vocab: int) -> int:
@@ -192,10 +193,20 @@ def fp16_ulp(q: np.ndarray) -> np.ndarray:
     return np.where(q >= 2.0 ** -14, 2.0 ** (e - 10), 2.0 ** -24)
 
 
+def product_k_range(vocab: int) -> int:
+    """Vocab rows of one split range of the product of given probabilities
+    (64-row steps)."""
+    per = -(-vocab // SELFCOND_SPLITS)
+    return -(-per // PRODUCT_STEP) * PRODUCT_STEP
+
+
 def selfcond_bound(x: np.ndarray, rows, temps, canvas_len: int, embed_bits: np.ndarray,
-                   f16: bool = False):
+                   f16: bool = False, k_range: int | None = None):
     """Per-element bound of |gpu - oracle| for the rows' products (see above);
-    f16: the model dtype is fp16 (else bf16)."""
+    f16: the model dtype is fp16 (else bf16); k_range: the vocab rows of one
+    split range (default: the fused product's)."""
+    if k_range is None:
+        k_range = selfcond_k_range(x.shape[1])
     rows = np.asarray(rows, dtype=np.int64)
     code = oracle.PROBS_FP16 if f16 else oracle.PROBS_BF16
     to_f64 = oracle.fp16_to_f64 if f16 else oracle.bf16_to_f64
@@ -210,14 +221,14 @@ def selfcond_bound(x: np.ndarray, rows, temps, canvas_len: int, embed_bits: np.n
         near = np.minimum(np.abs(p - (q[i] + ulp[i] / 2)),
                           np.minimum(np.abs(p - (q[i] - ulp[i] / 2)), np.abs(p - (q[i] - ulp[i] / 4))))
         amb = near <= SELFCOND_EPS * p + 2.0 ** -149
-        w[i] = amb * ulp[i] + (selfcond_k_range(x.shape[1]) + 9) * 2.0 ** -24 * (q[i] + ulp[i])
+        w[i] = amb * ulp[i] + (k_range + 9) * 2.0 ** -24 * (q[i] + ulp[i])
     bound = np.zeros((len(rows), embed_bits.shape[1]))
     for c0 in range(0, embed_bits.shape[0], 16384):
         bound += w[:, c0:c0 + 16384] @ np.abs(to_f64(embed_bits[c0:c0 + 16384]))
     return bound + 2.0 ** -140
 
 
-def compare_selfcond(w, embed: torch.Tensor, out, rows, label=""):
+def compare_selfcond(w, embed: torch.Tensor, out, rows, label="", k_range: int | None = None):
     """Statistics as compare_rowstats (no probs) and the product within
     selfcond_bound of the oracle's; returns the worst error / bound."""
     import dataclasses
@@ -232,7 +243,36 @@ def compare_selfcond(w, embed: torch.Tensor, out, rows, label=""):
     ref = oracle.selfcond(x, rows, temps, w.canvas_len, eb,
                           dtype=oracle.PROBS_FP16 if f16 else oracle.PROBS_BF16)
     got = res[torch.as_tensor(rows, device=res.device)].double().cpu().numpy()
-    bound = selfcond_bound(x, rows, temps, w.canvas_len, eb, f16)
+    bound = selfcond_bound(x, rows, temps, w.canvas_len, eb, f16, k_range)
+    err = np.abs(got - ref)
+    ratio = err / bound
+    k = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert np.all(err <= bound), (f"{label} product off by {err[k]:.3g} (bound {bound[k]:.3g}) "
+                                  f"at row {rows[k[0]]} column {k[1]}: gpu {got[k]!r} oracle {ref[k]!r}")
+    return float(ratio.max())
+
+
+def compare_product(probs: torch.Tensor, embed: torch.Tensor, out: torch.Tensor, rows,
+                    label=""):
+    """The product of given probabilities against oracle.probs_product: every
+    product of two bf16 (fp16) values is exact in fp32, and each output is a
+    chain of at most k_range + 9 fp32 additions (one split range, then the 8
+    partials), so |gpu - oracle| <= (k_range + 9) 2^-24 sum_c |q_c| |e_cj|.
+    Returns the worst error / bound."""
+    rows = np.asarray(rows, dtype=np.int64)
+    idx = torch.as_tensor(rows, device=probs.device)
+    f16 = probs.dtype == torch.float16
+    code = oracle.PROBS_FP16 if f16 else oracle.PROBS_BF16
+    to_f64 = oracle.fp16_to_f64 if f16 else oracle.bf16_to_f64
+    qb = probs_bits(probs.index_select(0, idx))
+    eb = embed.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.probs_product(qb, eb, dtype=code)
+    w = (product_k_range(probs.shape[1]) + 9) * 2.0 ** -24 * np.abs(to_f64(qb))
+    bound = np.zeros_like(ref)
+    for c0 in range(0, eb.shape[0], 16384):
+        bound += w[:, c0:c0 + 16384] @ np.abs(to_f64(eb[c0:c0 + 16384]))
+    bound += 2.0 ** -140
+    got = out.index_select(0, idx).double().cpu().numpy()
     err = np.abs(got - ref)
     ratio = err / bound
     k = np.unravel_index(np.argmax(ratio), ratio.shape)

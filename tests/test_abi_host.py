@@ -42,7 +42,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["rowstats_run", "rowstats_run_noalloc",
-                                           "rowstats_selfcond",
+                                           "rowstats_selfcond", "rowstats_packed_embed_bytes",
+                                           "rowstats_pack_embed", "rowstats_selfcond_product",
                                            "topk_logprobs", "stash_converged_logprobs",
                                            "rowstats_last_error", "rowstats_check_device",
                                            "rowstats_release"])
@@ -150,6 +151,66 @@ def test_selfcond_rejects(kwargs, code):
 def test_selfcond_zero_rows_is_a_no_op():
     assert selfcond(rows=0, logits=NULL, temps=NULL, embed=NULL, out=NULL, argmax=NULL,
                     sample=NULL, entropy=NULL) == OK
+
+
+def test_packed_embed_bytes():
+    lib = rs.lib()
+    # vocab rows padded to a multiple of 128, 2 bytes per element
+    assert lib.rowstats_packed_embed_bytes(262144, 2560) == 262144 * 2560 * 2
+    assert lib.rowstats_packed_embed_bytes(1, 256) == 128 * 256 * 2
+    assert lib.rowstats_packed_embed_bytes(129, 512) == 256 * 512 * 2
+    for vocab, d in ((0, 256), (2 ** 31, 256), (100, 0), (100, 128), (100, 300), (100, 2 ** 21)):
+        assert lib.rowstats_packed_embed_bytes(vocab, d) == ERR_SHAPE
+        assert rs.last_error() != ""
+
+
+def pack(embed=FAKE, vocab=100, d=256, dtype=1, packed=FAKE):
+    return rs.lib().rowstats_pack_embed(embed, vocab, d, dtype, packed, NULL)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(vocab=0), ERR_SHAPE),
+    (dict(d=200), ERR_SHAPE),
+    (dict(dtype=0), ERR_DTYPE),
+    (dict(dtype=3), ERR_DTYPE),
+    (dict(embed=NULL), ERR_NULL),
+    (dict(packed=NULL), ERR_NULL),
+    (dict(embed=ctypes.c_void_p(0x1001)), ERR_SHAPE),   # odd address
+    (dict(packed=ctypes.c_void_p(0x1008)), ERR_SHAPE),  # not 16-byte aligned
+])
+def test_pack_embed_rejects(kwargs, code):
+    assert pack(**kwargs) == code
+    assert rs.last_error() != ""
+
+
+def product(probs=FAKE, stride=8, rows=4, vocab=8, dtype=1, packed=FAKE, d=256, out=FAKE):
+    return rs.lib().rowstats_selfcond_product(probs, stride, rows, vocab, dtype, packed, d, out,
+                                              NULL)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(rows=-1), ERR_SHAPE),
+    (dict(rows=2 ** 31), ERR_SHAPE),
+    (dict(vocab=0), ERR_SHAPE),
+    (dict(stride=7), ERR_SHAPE),
+    (dict(d=128), ERR_SHAPE),
+    (dict(d=2 ** 21), ERR_SHAPE),
+    (dict(dtype=0), ERR_DTYPE),
+    (dict(dtype=3), ERR_DTYPE),
+    (dict(probs=NULL), ERR_NULL),
+    (dict(packed=NULL), ERR_NULL),
+    (dict(out=NULL), ERR_NULL),
+    (dict(probs=ctypes.c_void_p(0x1001)), ERR_SHAPE),
+    (dict(packed=ctypes.c_void_p(0x1004)), ERR_SHAPE),
+    (dict(out=ctypes.c_void_p(0x1008)), ERR_SHAPE),
+])
+def test_selfcond_product_rejects(kwargs, code):
+    assert product(**kwargs) == code
+    assert rs.last_error() != ""
+
+
+def test_selfcond_product_zero_rows_is_a_no_op():
+    assert product(rows=0, probs=NULL, packed=NULL, out=NULL) == OK
 
 
 def test_topk_zero_rows_is_a_no_op():

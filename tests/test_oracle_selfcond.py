@@ -162,3 +162,61 @@ def test_dtype_is_checked():
     with pytest.raises(ValueError):
         oracle.selfcond(np.zeros((1, 4), np.float32), [0], [1.0], 1, np.zeros((4, 2), np.uint16),
                         dtype=oracle.PROBS_NONE)
+
+
+# --- the product of given probabilities (oracle.probs_product)
+def test_product_one_hot_rows_pick_embedding_rows():
+    # q[i] = 1 at column c_i: out[i] = E[c_i] exactly, whatever E holds
+    rng = np.random.default_rng(21)
+    vocab, d, rows = 300, 40, 7
+    e = rng.standard_normal((vocab, d)).astype(np.float32)
+    eb = bf16_bits(e)
+    cols = rng.integers(0, vocab, size=rows)
+    q = np.zeros((rows, vocab), np.float32)
+    q[np.arange(rows), cols] = 1.0
+    out = oracle.probs_product(bf16_bits(q), eb, block=64)
+    assert np.array_equal(out, oracle.bf16_to_f64(eb)[cols])
+
+
+def test_product_brute_force_non_square_signed_and_subnormal():
+    # explicit sums with rows != vocab != d (a transposed operand fails),
+    # signed values (a dropped sign fails) and bf16 subnormals in both operands
+    rng = np.random.default_rng(22)
+    rows, vocab, d = 3, 11, 5
+    q = rng.standard_normal((rows, vocab)).astype(np.float32)
+    q[0, 2] = 3.0e-39
+    e = rng.standard_normal((vocab, d)).astype(np.float32)
+    e[4, 1] = -5.0e-39
+    qb, eb = bf16_bits(q), bf16_bits(e)
+    qv, ev = oracle.bf16_to_f64(qb), oracle.bf16_to_f64(eb)
+    assert qv[0, 2] != 0.0 and abs(qv[0, 2]) < 2.0 ** -126
+    out = oracle.probs_product(qb, eb, block=4)
+    for r in range(rows):
+        for j in range(d):
+            acc = 0.0
+            for c in range(vocab):
+                acc += qv[r, c] * ev[c, j]
+            assert abs(out[r, j] - acc) <= 1e-15 * (1 + abs(acc))
+
+
+def test_product_fp16_closed_form():
+    # fp16 q = 1/4 on four columns of small integers: the exact column means
+    vocab, d = 64, 6
+    rng = np.random.default_rng(23)
+    e = rng.integers(-8, 9, size=(vocab, d)).astype(np.float32)
+    q = np.zeros((2, vocab), np.float32)
+    q[0, [1, 9, 17, 60]] = 0.25
+    q[1, [0, 63, 5, 6]] = 0.25
+    out = oracle.probs_product(fp16_bits(q), fp16_bits(e), block=16, dtype=oracle.PROBS_FP16)
+    want = np.stack([e[[1, 9, 17, 60]].mean(axis=0), e[[0, 63, 5, 6]].mean(axis=0)])
+    assert np.array_equal(out, want.astype(np.float64))
+
+
+def test_selfcond_is_the_product_of_the_oracle_probabilities():
+    rng = np.random.default_rng(24)
+    vocab, d = 500, 8
+    x = (rng.standard_normal((4, vocab)) * 2).astype(np.float32)
+    eb = bf16_bits(rng.standard_normal((vocab, d)))
+    probs = oracle.rowstats(x, np.arange(4), [0.8, 0.0], 2, 0, oracle.PROBS_BF16)["probs"]
+    assert np.array_equal(oracle.selfcond(x, np.arange(4), [0.8, 0.0], 2, eb),
+                          oracle.probs_product(probs, eb))

@@ -23,7 +23,7 @@ that run's kernel-trace or counter CSV from DIR and prints, per workload and
 kernel, the launch statistics (or the mean counter value per launch).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others]
-       [--no-cpu] [--only C2|C3|C4|C5|S4|SC] [--calib-copy] [--ceiling]
+       [--no-cpu] [--only C2|C3|C4|C5|S4|SC|SP] [--calib-copy] [--ceiling]
        [--profile-run] [--summarize DIR]
 """
 from __future__ import annotations
@@ -166,6 +166,48 @@ def bench_selfcond(w, d, steps, warmup, dtype=None):
     return {"ms": ms, "wall_ms": wall, "d": d, "tflops": flops / ms / 1e9,
             "mfma_frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, "bytes": nbytes,
             "gbs": nbytes / ms / 1e6}
+
+
+def bench_selfcond_product(w, d, steps, warmup, dtype=None):
+    """The self-conditioning input through materialized probabilities:
+    rowstats_run writes the workload's probabilities in the model dtype (bf16
+    unless ``dtype``), then rowstats_selfcond_product multiplies them by a
+    seeded [vocab, d] table packed once beforehand (a weight: packed at load
+    time, outside the timed calls). A step is both calls. Also times the
+    product call alone. Work per step: 2 rows vocab d flops on the matrix
+    cores; bytes: logits read once, probabilities written and read back, the
+    table read once, 20 B of statistics and 4 d B of product per row."""
+    import torch
+    import row_softmax_statistics_amd as rs
+    import synthetic as syn
+    dev = w.logits.device
+    dtype = dtype or torch.bfloat16
+    embed = syn.embedding(w.vocab, d, seed=21, device=dev, dtype=dtype)
+    packed = rs.pack_embed(embed)
+    del embed
+    stats = (torch.empty(w.rows, dtype=torch.int64, device=dev),
+             torch.empty(w.rows, dtype=torch.int64, device=dev),
+             torch.empty(w.rows, dtype=torch.float32, device=dev),
+             torch.empty(w.rows, w.vocab, dtype=dtype, device=dev))
+    res = torch.empty(w.rows, d, dtype=torch.float32, device=dev)
+
+    def step():
+        rs.sample_row_stats(w.logits, w.temps, w.canvas_len, w.seed, dtype, out=stats)
+        rs.selfcond_product(stats[3], packed, out=res)
+
+    def product():
+        rs.selfcond_product(stats[3], packed, out=res)
+
+    ms, wall = time_launches(step, steps, warmup)
+    pms, _ = time_launches(product, steps, warmup)
+    rs.check_device()
+    flops = 2.0 * w.rows * w.vocab * d
+    nbytes = 8 * w.rows * w.vocab + 2 * w.vocab * d + (20 + 4 * d) * w.rows
+    del packed, stats, res
+    return {"ms": ms, "wall_ms": wall, "d": d, "tflops": flops / ms / 1e9,
+            "mfma_frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, "bytes": nbytes,
+            "gbs": nbytes / ms / 1e6, "product_ms": pms, "product_tflops": flops / pms / 1e9,
+            "product_mfma_frac": flops / pms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
 
 
 def bench_topk(w, steps, warmup):
@@ -318,6 +360,9 @@ PROFILE_PLAN = [
     ("C4", ["kept_rows_kernel", "topk_kernel<true>"]),
     ("S4", ["stash_rows_kernel", "topk_kernel<true>"]),
     ("SC", ["rowstats_kernel<0, true>", "selfcond_gemm_kernel<true, false>", "selfcond_reduce_kernel"]),
+    ("SP", ["rowstats_kernel<1, true>", "product_gemm_kernel<true, false>", "selfcond_reduce_kernel"]),
+    # (the product calls alone that bench_selfcond_product times after SP's steps)
+    ("SP product", ["product_gemm_kernel<true, false>", "selfcond_reduce_kernel"]),
 ]
 PROFILE_LAUNCHES = 21  # per workload: 1 untimed + 20 timed calls
 
@@ -329,11 +374,14 @@ def profile_run():
     import row_softmax_statistics_amd as rs
     dev = "cuda:0"
     for name, _ in PROFILE_PLAN:
-        w = syn.stash_c4(dev) if name == "S4" else syn.c2(dev) if name == "SC" else \
+        if name == "SP product":
+            continue  # launched by the SP entry
+        w = syn.stash_c4(dev) if name == "S4" else syn.c2(dev) if name in ("SC", "SP") else \
             syn.WORKLOADS[name](dev)
         r = bench_topk(w, PROFILE_LAUNCHES - 1, 1) if name == "C4" else \
             bench_stash(w, PROFILE_LAUNCHES - 1, 1) if name == "S4" else \
             bench_selfcond(w, SELFCOND_D, PROFILE_LAUNCHES - 1, 1) if name == "SC" else \
+            bench_selfcond_product(w, SELFCOND_D, PROFILE_LAUNCHES - 1, 1) if name == "SP" else \
             bench_rowstats(w, PROFILE_LAUNCHES - 1, 1)
         print(json.dumps({"workload": name, **{k: round(v, 4) if isinstance(v, float) else v
                                                for k, v in r.items()}}), flush=True)
@@ -353,7 +401,9 @@ def summarize(directory: str):
     traces = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
     src = counters[0] if counters else traces[0]
     with open(src) as fh:
-        rows = [r for r in csv.DictReader(fh) if "rowstats::" in r["Kernel_Name"]]
+        # the one-time packing of the embedding table is not part of any step
+        rows = [r for r in csv.DictReader(fh) if "rowstats::" in r["Kernel_Name"]
+                and "pack_embed_kernel" not in r["Kernel_Name"]]
     key = "Dispatch_Id" if counters else "Correlation_Id"
     names = sorted({r["Counter_Name"] for r in rows}) if counters else ["duration (ns)"]
     seq = []
@@ -390,7 +440,7 @@ def main():
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--only", choices=["C2", "C3", "C4", "C5", "S4", "SC"], default=None)
+    ap.add_argument("--only", choices=["C2", "C3", "C4", "C5", "S4", "SC", "SP"], default=None)
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--ceiling", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
@@ -420,11 +470,12 @@ def main():
 
     if args.only:
         w = syn.stash_c4(dev) if args.only == "S4" else \
-            syn.c2(dev) if args.only == "SC" else syn.WORKLOADS[args.only](dev)
+            syn.c2(dev) if args.only in ("SC", "SP") else syn.WORKLOADS[args.only](dev)
         r = bench_topk(w, args.steps, args.warmup) if args.only == "C4" else \
             bench_stash(w, args.steps, args.warmup) if args.only == "S4" else \
             bench_selfcond(w, SELFCOND_D, args.steps, args.warmup) if args.only == "SC" else \
-            bench_rowstats(w, args.steps, args.warmup)
+            bench_selfcond_product(w, SELFCOND_D, args.steps, args.warmup) if args.only == "SP" \
+            else bench_rowstats(w, args.steps, args.warmup)
         print(json.dumps({"workload": args.only, **{k: round(v, 4) if isinstance(v, float) else v
                                                      for k, v in r.items()}}), flush=True)
         import row_softmax_statistics_amd as rs
@@ -468,6 +519,10 @@ def main():
         sc16 = bench_selfcond(w, SELFCOND_D, max(5, args.steps // 4), 2, torch.float16)
         line["selfcond"]["fp16"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                     for k, v in sc16.items() if k in ("ms", "tflops", "mfma_frac")}
+        # the same input through materialized probabilities and a packed table
+        sp = bench_selfcond_product(w, SELFCOND_D, max(5, args.steps // 4), 2)
+        line["selfcond"]["materialized"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                            for k, v in sp.items()}
     del w
     torch.cuda.empty_cache()
     # the three V = 262144 row-statistics workloads the 75 % target covers,

@@ -66,3 +66,15 @@ def test_a_missing_dispatch_is_an_error(tmp_path):
     write_trace(tmp_path / "t_kernel_trace.csv", entries)
     r = run(tmp_path)
     assert r.returncode != 0 and "dispatches of this library" in r.stderr
+
+
+def test_the_one_time_table_packing_is_not_a_step(tmp_path):
+    # the embedding table is packed once before the product's timed calls
+    names = plan_names()
+    entries = [(f"void rowstats::{k}(x)", 100) for _, k in names]
+    at = next(i for i, (w, _) in enumerate(names) if w == "SP")
+    entries.insert(at, ("void rowstats::(anonymous namespace)::pack_embed_kernel(x)", 7))
+    write_trace(tmp_path / "t_kernel_trace.csv", entries)
+    r = run(tmp_path)
+    assert r.returncode == 0, r.stderr
+    assert "pack_embed" not in r.stdout

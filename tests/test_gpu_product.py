@@ -139,7 +139,7 @@ def test_from_logits_through_rowstats_probs(rows, vocab, d, pad, dtype):
 def test_c2_full_size_d2560():
     # the C2 logits (4096 x 262144) with bf16 probs and a 262144 x 2560 table:
     # sampled rows against the oracle, every greedy row against its argmax's
-    # embedding, and the product equal to rowstats_selfcond's on greedy rows
+    # embedding
     w = syn.c2(DEV)
     argmax, sample, entropy, probs = rs.sample_row_stats(w.logits, w.temps, w.canvas_len,
                                                          w.seed, torch.bfloat16)
@@ -156,4 +156,37 @@ def test_c2_full_size_d2560():
     assert torch.equal(out[g], embed[argmax[g]].float())
     record("probs->product C2 d=2560", rows_compared=len(rows), greedy_rows_exact=int(g.numel()),
            worst_error_over_bound=round(worst, 4))
+    done()
+
+
+def test_calls_on_two_streams_are_ordered():
+    # both products use the library's one partial-product buffer; calls that
+    # alternate between two streams (a larger one in between) give the
+    # results of one stream
+    w = syn.random_case(DEV, rows=300, vocab=50000, canvas_len=5, seed=42,
+                        t_choices=(0.0, 0.7, 1.0), probs_dtype=torch.bfloat16)
+    e = syn.embedding(w.vocab, 512, seed=43, device=DEV)
+    packed = rs.pack_embed(e)
+    probs = rs.sample_row_stats(w.logits, w.temps, w.canvas_len, w.seed, torch.bfloat16)[3]
+    big = syn.probabilities(700, w.vocab, seed=44, device=DEV)
+    ref_sc = rs.selfcond_embed(w.logits, w.temps, w.canvas_len, w.seed, e)
+    ref_p = rs.selfcond_product(probs, packed)
+    ref_big = rs.selfcond_product(big, packed)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for it in range(3):
+        a, b = (s1, s2) if it % 2 == 0 else (s2, s1)
+        with torch.cuda.stream(a):
+            sc = rs.selfcond_embed(w.logits, w.temps, w.canvas_len, w.seed, e)
+        with torch.cuda.stream(b):
+            p = rs.selfcond_product(probs, packed)
+        with torch.cuda.stream(a):
+            g = rs.selfcond_product(big, packed)
+        outs.append((sc, p, g))
+    torch.cuda.synchronize()
+    for sc, p, g in outs:
+        for x, y in zip(sc, ref_sc):
+            assert torch.equal(x, y)
+        assert torch.equal(p, ref_p) and torch.equal(g, ref_big)
     done()

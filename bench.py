@@ -229,6 +229,18 @@ def bench_topk(w, steps, warmup):
             "kept_rows_per_s": kept / ms * 1e3}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "" if unknown."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(w, n_rows: int, gpu_out=None, min_seconds: float = 10.0,
                  max_passes: int = 20):
     """The oracle, as it is, on a seeded sample of the workload's rows,
@@ -253,7 +265,7 @@ def cpu_baseline(w, n_rows: int, gpu_out=None, min_seconds: float = 10.0,
         passes += 1
     nbytes = algorithmic_bytes(len(rows), w.vocab, 0 if code == 0 else 2) * passes
     res = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-           "kind": "oracle", "rows_per_s": round(len(rows) * passes / dt, 1),
+           "kind": "oracle", "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(), "rows_per_s": round(len(rows) * passes / dt, 1),
            "seconds": round(dt, 2), "passes": passes,
            "sample": f"{len(rows)} seeded rows of {w.name} ({w.rows} x {w.vocab}, full rows), "
                      f"{passes} passes"}
@@ -283,7 +295,8 @@ def calib_copy(steps=5):
 
 
 CEILING_MODES = {0: ("lds_dma_read", 0), 1: ("lds_dma_read_write8", 2),
-                 2: ("lds_dma_read_write16", 2), 3: ("vgpr_read", 0), 4: ("vgpr_read_write16", 2)}
+                 2: ("lds_dma_read_write16", 2), 3: ("vgpr_read", 0), 4: ("vgpr_read_write16", 2),
+                 5: ("vgpr_read_write8", 2)}
 
 
 def ceiling(steps=20, warmup=3, rows=4096, vocab=262144):

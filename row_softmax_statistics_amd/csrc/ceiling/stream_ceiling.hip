@@ -20,6 +20,8 @@
 //                the current chunk is consumed
 //   kVgprWrite16 kVgprRead with lane l loading quads 2 l, 2 l + 1 of each 128
 //                and storing 16 bytes per pair
+//   kVgprWrite8  kVgprRead + the probs kernels' store pattern (lane l holds
+//                quads j 64 + l and stores 8 bytes per quad)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,7 +33,14 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kChunkBytes = 8192;
 constexpr int kStream = 2;  // cache policy: streaming (nt)
 
-enum Mode { kDmaRead = 0, kDmaWrite8 = 1, kDmaWrite16 = 2, kVgprRead = 3, kVgprWrite16 = 4 };
+enum Mode {
+  kDmaRead = 0,
+  kDmaWrite8 = 1,
+  kDmaWrite16 = 2,
+  kVgprRead = 3,
+  kVgprWrite16 = 4,
+  kVgprWrite8 = 5
+};
 
 using Rsrc = __amdgpu_buffer_rsrc_t;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(kThreads, OCC) void stream_kernel(const float *src,
       else store_half<MODE == kDmaWrite16>(dst + c * (kChunkBytes / 4), v);
     }
   } else {
-    constexpr bool kPairs = MODE == kVgprWrite16;
+    constexpr bool kPairs = MODE == kVgprWrite16;  // (kVgprWrite8: quads j 64 + l)
     const uint32_t voff = (kPairs ? 32u : 16u) * (uint32_t)lane();
     auto load = [&](f32x4 (&v)[8], int64_t c) {
       const Rsrc r = rsrc(chunk_src(c < n_chunks ? c : 0), c < n_chunks ? kChunkBytes : 0u);
@@ -197,11 +206,11 @@ __global__ __launch_bounds__(kThreads, OCC) void stream_kernel(const float *src,
     for (; c < n_chunks; c += 2 * W) {
       load(b, c + W);
       if constexpr (MODE == kVgprRead) acc ^= fold(a);
-      else store_half<true>(dst + c * (kChunkBytes / 4), a);
+      else store_half<kPairs>(dst + c * (kChunkBytes / 4), a);
       if (c + W >= n_chunks) break;
       load(a, c + 2 * W);
       if constexpr (MODE == kVgprRead) acc ^= fold(b);
-      else store_half<true>(dst + (c + W) * (kChunkBytes / 4), b);
+      else store_half<kPairs>(dst + (c + W) * (kChunkBytes / 4), b);
     }
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the reads alive; never true for the inputs used
@@ -220,6 +229,7 @@ const void *select(int mode, int occ) {
     case kDmaWrite16: return two ? kernel_of<kDmaWrite16, 2>() : kernel_of<kDmaWrite16, 4>();
     case kVgprRead: return two ? kernel_of<kVgprRead, 2>() : kernel_of<kVgprRead, 4>();
     case kVgprWrite16: return two ? kernel_of<kVgprWrite16, 2>() : kernel_of<kVgprWrite16, 4>();
+    case kVgprWrite8: return two ? kernel_of<kVgprWrite8, 2>() : kernel_of<kVgprWrite8, 4>();
     default: return nullptr;
   }
 }
@@ -228,7 +238,7 @@ const void *select(int mode, int occ) {
 
 extern "C" {
 
-// One launch of mode `mode` (0..4, see above) at `occ` (2 or 4) waves per
+// One launch of mode `mode` (0..5, see above) at `occ` (2 or 4) waves per
 // SIMD over n_chunks chunks of 8 KiB at src (device, 16-byte aligned),
 // writing 4 KiB per chunk at dst for the write modes. The grid is every
 // workgroup the device holds at that occupancy. Returns 0, or -1 for a bad

@@ -32,7 +32,8 @@ def done():
 @pytest.mark.parametrize("rows,vocab,d,ld", [
     (1, 1, 256, None), (5, 31, 256, 33), (7, 100, 512, None), (33, 2049, 256, None),
     (65, 5000, 256, 5003), (129, 4097, 768, 4104), (300, 20000, 512, None),
-    (40, 70001, 768, None), (3, 262144, 256, None)])
+    (40, 70001, 768, None), (3, 262144, 256, None), (17, 3000, 4096, None),
+    (9, 5000, 1280, 5008)])
 def test_given_probabilities(rows, vocab, d, ld, dtype):
     # odd strides and odd vocab take the element-load path, the others the
     # 16-byte path; 64-row steps leave ragged ends in most ranges

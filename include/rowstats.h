@@ -35,7 +35,8 @@ typedef enum rowstats_status {
   ROWSTATS_ERR_SHAPE = -2,  /* rows < 0, or (rows > 0 and: rows > 2^31 - 1,
                                vocab < 1, vocab > 2^31 - 1 - 65536,
                                row_stride < vocab, canvas_len < 1) */
-  ROWSTATS_ERR_K = -3,      /* K < 1 (num_topk < 0), K > vocab or K > 64 */
+  ROWSTATS_ERR_K = -3,      /* K < 1 or K > vocab; for the stash num_topk < 0,
+                               num_topk > vocab or num_topk > 64 */
   ROWSTATS_ERR_DTYPE = -4,  /* probs_dtype is not one of rowstats_probs_dtype */
   ROWSTATS_ERR_HIP = -5,    /* a HIP call failed (allocation, launch); see last_error */
   ROWSTATS_ERR_COOP = -6,   /* rowstats_run keeps the ceil(vocab / 2048) chunks of a
@@ -212,7 +213,9 @@ int rowstats_selfcond_product(const void *probs, int64_t probs_stride,
  *   logits, row_stride, rows, vocab, temps, canvas_len  as for rowstats_run;
  *               T <= 0 is clamped to 1e-10 like the entropy's temperature.
  *   keep_mask   uint8 [ceil(rows / canvas_len)]: nonzero = slot kept.
- *   K           1 <= K <= min(vocab, 64).
+ *   K           1 <= K <= vocab. K <= 64 runs the one-pass kernel (every row
+ *               read once); larger K runs a separate kernel, one workgroup per
+ *               kept row, that reads the row 2 + 6 times per 4096 keys.
  *   out_vals    fp32 [rows, K] row-major: out_vals[r, k] = s - log Z at the
  *               column of rank k (descending value, ties to lower column),
  *               log Z = log sum_c exp(s_c).

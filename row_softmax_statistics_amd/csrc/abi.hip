@@ -290,6 +290,28 @@ int plan_and_launch_topk(DeviceState &d, TopKParams &p, hipStream_t s) {
   return note_stream(d, s);
 }
 
+// Scratch layout and launches of the top-K path for K > kTopKMax: the
+// kept-row list and temperatures after the scratch head (whose row-claim
+// counters the pre-pass zeroes, as for every top-K call).
+int plan_and_launch_topk_wide(DeviceState &d, TopKParams &p, hipStream_t s) {
+  auto align16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
+  const size_t temp_bytes = align16((size_t)p.rows * sizeof(float));
+  const size_t kept_bytes = align16(((size_t)p.rows + 1) * sizeof(int64_t));
+  int rc = order_after_last(d, s);
+  if (rc) return rc;
+  if ((rc = ensure_grow_scratch(d, kScratchHead + temp_bytes + kept_bytes, s))) return rc;
+  char *base = reinterpret_cast<char *>(d.grow.base);
+  p.counters = reinterpret_cast<uint32_t *>(base);
+  base += kScratchHead;
+  p.kept_temp = reinterpret_cast<float *>(base);
+  base += temp_bytes;
+  p.kept = reinterpret_cast<int64_t *>(base);
+  p.err_flag = d.grow.err;
+  hipError_t e = topk_wide_launch(p, s);
+  if (e != hipSuccess) return fail_hip(e, "top-K kernel launch");
+  return note_stream(d, s);
+}
+
 // Checks and launch plan of a row-statistics call, shared by rowstats_run
 // and rowstats_run_noalloc: fills p except the scratch pointers and the
 // epoch, and returns the grid and the scratch bytes the call needs.
@@ -583,7 +605,6 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   if (rc) return rc;
   if (K < 1 || (int64_t)K > vocab)
     return fail(ROWSTATS_ERR_K, "K must be in [1, vocab=%lld], got %d", (long long)vocab, K);
-  if (K > kTopKMax) return fail(ROWSTATS_ERR_K, "K must be <= %d, got %d", kTopKMax, K);
   if (!keep_mask) return fail(ROWSTATS_ERR_NULL, "keep_mask is NULL");
   if (!out_vals || !out_idx) return fail(ROWSTATS_ERR_NULL, "an output pointer is NULL");
 
@@ -607,6 +628,7 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows, int64_t
   p.out_vals = out_vals;
   p.out_idx = out_idx;
 
+  if (K > kTopKMax) return plan_and_launch_topk_wide(*d, p, s);
   return plan_and_launch_topk(*d, p, s);
 }
 

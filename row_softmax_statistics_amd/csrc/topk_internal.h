@@ -66,5 +66,13 @@ struct TopKParams {
 hipError_t topk_resident_blocks(bool vec, int *blocks_per_cu);
 // Queues the kept-row pre-pass and the top-K kernel (cooperative) on `stream`.
 hipError_t topk_launch(const TopKParams &p, int grid, hipStream_t stream);
+// Queues the kept-row pre-pass alone (p.keep, p.temps, p.rows, p.canvas_len,
+// p.kept, p.kept_temp, p.counters).
+hipError_t kept_rows_launch(const TopKParams &p, hipStream_t stream);
+// K > kTopKMax (up to the vocabulary): the kept-row pre-pass and one
+// workgroup per kept position (p.rows of them, the surplus returns at once);
+// uses p.logits, p.ld, p.vocab, p.vec_ok, p.K, p.out_vals, p.out_idx and the
+// pre-pass outputs.
+hipError_t topk_wide_launch(const TopKParams &p, hipStream_t stream);
 
 }  // namespace rowstats

@@ -855,6 +855,13 @@ hipError_t topk_resident_blocks(bool vec, int *blocks_per_cu) {
                                                       0);
 }
 
+hipError_t kept_rows_launch(const TopKParams &p, hipStream_t stream) {
+  kept_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(p.keep, p.temps, p.rows,
+                                                                p.canvas_len, p.kept, p.kept_temp,
+                                                                p.counters);
+  return hipGetLastError();
+}
+
 hipError_t topk_launch(const TopKParams &p, int grid, hipStream_t stream) {
   if (p.stash)
     stash_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(p);

@@ -1,0 +1,316 @@
+// Top-K logprobs for K above what the one-pass top-K kernel holds (K > 64,
+// up to the vocabulary): one workgroup per kept row, exact, in passes over
+// the row.
+//
+// Method: vLLM API page "diffusion_gemma_sampler", stash_converged_logprobs
+// docstring (kept rows divided by their temperature; the K largest, ties to
+// the lower id) and the _lp_topk_kernel docstring (keys ordered by value,
+// then by lower index, so the top-K is unique).
+//
+// Per row (1024 threads, four consecutive columns per thread and tile):
+//   1. the row maximum m of s = x / Tc, then S = sum exp(s - m) (two passes);
+//   2. in batches of up to kBatch keys below the previous batch's smallest:
+//      the value v of the batch's last key by a radix select over the 32-bit
+//      order-preserving value keys (four passes of 8-bit histograms in LDS),
+//      then the keys above v (one pass, unordered) and the first keys equal
+//      to v in column order (one pass with a workgroup scan per tile), a
+//      bitonic sort of the batch in LDS (64-bit keys: value, then lower
+//      column) and the batch's logprobs (s - m) - log S in rank order.
+// The kernel is a fallback for large K: it reads each row 2 + 6 times per
+// batch and has no place in the one-pass budget of the main top-K kernel.
+#include "topk_internal.h"
+
+#include "chunk_common.h"
+#include "device_common.h"
+#include "device_math.h"
+
+#include <float.h>
+
+namespace rowstats {
+namespace {
+
+constexpr int kWideThreads = 1024;
+constexpr int kWideWaves = kWideThreads / kWave;
+constexpr int kTile = 4 * kWideThreads;  // columns per pass step
+constexpr int kBatch = 4096;             // keys sorted in LDS at a time
+
+// Unsigned order-preserving keys: value key (sign bit flipped) and the
+// 64-bit key with 0x7FFFFFFF - column in the low word.
+__device__ __forceinline__ uint32_t ukey32(float s) { return (uint32_t)key32(s) ^ 0x80000000u; }
+__device__ __forceinline__ uint64_t ukey64(uint32_t k, int32_t col) {
+  return ((uint64_t)k << 32) | (uint64_t)(uint32_t)(0x7FFFFFFF - col);
+}
+__device__ __forceinline__ float ukey_value(uint64_t k) {
+  return key32_value((int32_t)((uint32_t)(k >> 32) ^ 0x80000000u));
+}
+__device__ __forceinline__ int32_t ukey_col(uint64_t k) {
+  return 0x7FFFFFFF - (int32_t)(uint32_t)(k & 0xFFFFFFFFu);
+}
+
+struct WideShared {
+  uint64_t keys[kBatch];
+  uint32_t hist[256];
+  double red_d[kWideWaves];
+  float red_f[kWideWaves];
+  uint32_t red_u[kWideWaves];
+  uint32_t count;     // keys above v collected so far
+  uint32_t digit;     // the bin the radix select picked
+  uint32_t rank;      // rank left inside that bin
+};
+
+// Scaled values of this thread's four columns c0 .. c0 + 3 of row xrow
+// (columns at or past V report `valid` false).
+template <bool VEC>
+__device__ __forceinline__ void load4(const float *xrow, int32_t c0, int32_t V, const Recip &rc,
+                                      float tc, float (&s)[4], bool (&valid)[4]) {
+  float x[4];
+  if (VEC && c0 + 4 <= V) {
+    const float4 q = *reinterpret_cast<const float4 *>(xrow + c0);
+    x[0] = q.x;
+    x[1] = q.y;
+    x[2] = q.z;
+    x[3] = q.w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) valid[i] = true;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      valid[i] = c0 + i < V;
+      x[i] = valid[i] ? xrow[c0 + i] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = scale_any(x[i], rc, tc);
+}
+
+__device__ __forceinline__ float block_max(float v, WideShared &sh) {
+  v = wave_max_f32(v);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) sh.red_f[w] = v;
+  __syncthreads();
+  float r = sh.red_f[0];
+  for (int i = 1; i < kWideWaves; ++i) r = fmaxf(r, sh.red_f[i]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ double block_sum(double v, WideShared &sh) {
+  v = wave_allreduce(v, SumD());
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) sh.red_d[w] = v;
+  __syncthreads();
+  double r = 0.0;
+  for (int i = 0; i < kWideWaves; ++i) r += sh.red_d[i];
+  __syncthreads();
+  return r;
+}
+
+// Exclusive prefix of v over the workgroup (thread order) and the total.
+__device__ __forceinline__ uint32_t block_prefix(uint32_t v, uint32_t &total, WideShared &sh) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, (unsigned)d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) sh.red_u[w] = incl;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+  for (int i = 0; i < kWideWaves; ++i) {
+    if (i < w) off += sh.red_u[i];
+    tot += sh.red_u[i];
+  }
+  __syncthreads();
+  total = tot;
+  return off + incl - v;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
+  __shared__ WideShared sh;
+  const int64_t pos = blockIdx.x;
+  if (pos >= p.kept[p.rows]) return;
+  const int t = threadIdx.x;
+  const int64_t row = p.kept[pos];
+  const float tc = clamp_temp(p.kept_temp[pos]);
+  const Recip rc = recip_of(tc);
+  const float *xrow = p.logits + row * p.ld;
+  const int32_t V = p.vocab;
+  const int K = p.K;
+
+  // ---- 1. row maximum and S = sum exp(s - m) ----
+  float mt = -INFINITY;
+  for (int32_t base = 0; base < V; base += kTile) {
+    float s[4];
+    bool ok[4];
+    load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (ok[i]) mt = fmaxf(mt, s[i]);
+  }
+  const float m = block_max(mt, sh);
+  float st = 0.0f;
+  for (int32_t base = 0; base < V; base += kTile) {
+    float s[4];
+    bool ok[4];
+    load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (ok[i]) st += __builtin_amdgcn_exp2f(fmaxf(s[i] - m, -FLT_MAX) * 1.44269504088896340736f);
+  }
+  const double log_s = log_d(block_sum((double)st, sh));
+
+  // ---- 2. batches of keys in descending order ----
+  uint64_t bound = ~0ull;  // keys of this batch are below it
+  bool bounded = false;
+  for (int done = 0; done < K;) {
+    const int nb = min(K - done, kBatch);
+    auto allowed = [&](uint32_t k, int32_t c) { return !bounded || ukey64(k, c) < bound; };
+    // radix select: v = value key of the nb-th largest allowed key
+    uint32_t prefix = 0;
+    uint32_t rank = (uint32_t)nb;  // 1-based rank from the top inside the current prefix
+    for (int d = 0; d < 4; ++d) {
+      const int shift = 24 - 8 * d;
+      for (int i = t; i < 256; i += kWideThreads) sh.hist[i] = 0u;
+      __syncthreads();
+      for (int32_t base = 0; base < V; base += kTile) {
+        float s[4];
+        bool ok[4];
+        load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t k = ukey32(s[i]);
+          const bool match = ((uint64_t)k >> (shift + 8)) == (uint64_t)prefix;
+          if (ok[i] && match && allowed(k, base + 4 * t + i))
+            atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      if (t < kWave) {
+        // bins 255 - 4 t .. 252 - 4 t, from the top
+        const int lane = t;
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c[i] = sh.hist[255 - 4 * lane - i];
+          sum += c[i];
+        }
+        uint32_t incl = sum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t v = __shfl_up(incl, (unsigned)o, kWave);
+          if (lane >= o) incl += v;
+        }
+        uint32_t before = incl - sum;  // keys in higher bins
+        if (before < rank && incl >= rank) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (before < rank && before + c[i] >= rank) {
+              sh.digit = 255u - 4u * (uint32_t)lane - (uint32_t)i;
+              sh.rank = rank - before;
+            }
+            before += c[i];
+          }
+        }
+      }
+      __syncthreads();
+      prefix = (prefix << 8) | sh.digit;
+      rank = sh.rank;
+      __syncthreads();
+    }
+    const uint32_t v = prefix;
+    const uint32_t need = rank;  // keys equal to v that belong to the batch
+    const uint32_t above = (uint32_t)nb - need;
+
+    // keys above v, in any order
+    if (t == 0) sh.count = 0u;
+    __syncthreads();
+    for (int32_t base = 0; base < V; base += kTile) {
+      float s[4];
+      bool ok[4];
+      load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t k = ukey32(s[i]);
+        const int32_t c = base + 4 * t + i;
+        if (ok[i] && k > v && allowed(k, c)) {
+          const uint32_t at = atomicAdd(&sh.count, 1u);
+          if (at < above) sh.keys[at] = ukey64(k, c);  // (exactly `above` such keys)
+        }
+      }
+    }
+    // the first `need` keys equal to v, in column order
+    uint32_t taken = 0;
+    for (int32_t base = 0; base < V && taken < need; base += kTile) {
+      float s[4];
+      bool ok[4];
+      load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
+      bool tie[4];
+      uint32_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tie[i] = ok[i] && ukey32(s[i]) == v && allowed(v, base + 4 * t + i);
+        mine += tie[i] ? 1u : 0u;
+      }
+      uint32_t total;
+      uint32_t at = taken + block_prefix(mine, total, sh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (tie[i]) {
+          if (at < need) sh.keys[above + at] = ukey64(v, base + 4 * t + i);
+          ++at;
+        }
+      }
+      taken += total;
+    }
+    // pad to a power of two and sort descending
+    int n2 = 64;
+    while (n2 < nb) n2 <<= 1;
+    for (int i = nb + t; i < n2; i += kWideThreads) sh.keys[i] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = t; i < n2 / 2; i += kWideThreads) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool desc = (lo & size) == 0;
+          const uint64_t a = sh.keys[lo], b = sh.keys[hi];
+          if ((a < b) == desc) {
+            sh.keys[lo] = b;
+            sh.keys[hi] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // the batch's logprobs, in rank order
+    for (int i = t; i < nb; i += kWideThreads) {
+      const uint64_t k = sh.keys[i];
+      const float s = ukey_value(k);
+      const int64_t o = row * (int64_t)K + done + i;
+      p.out_idx[o] = ukey_col(k);
+      p.out_vals[o] = (float)(((double)s - (double)m) - log_s);
+    }
+    bound = sh.keys[nb - 1];
+    bounded = true;
+    done += nb;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t topk_wide_launch(const TopKParams &p, hipStream_t stream) {
+  hipError_t e = kept_rows_launch(p, stream);
+  if (e != hipSuccess) return e;
+  TopKParams arg = p;
+  if (p.vec_ok)
+    topk_wide_kernel<true><<<dim3((unsigned)p.rows), dim3(kWideThreads), 0, stream>>>(arg);
+  else
+    topk_wide_kernel<false><<<dim3((unsigned)p.rows), dim3(kWideThreads), 0, stream>>>(arg);
+  return hipGetLastError();
+}
+
+}  // namespace rowstats

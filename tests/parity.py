@@ -132,7 +132,9 @@ def compare_topk(w, vals, idx, rows, label=""):
     assert bad.size == 0, f"{label} top-K indices differ on row {rows[bad[0]]}: gpu {gi[bad[0]]} oracle {ref_i[bad[0]]}"
     kv = gv[keep].astype(np.float64)
     rv = ref_v[keep].astype(np.float64)
-    err = np.abs(kv - rv)
+    # equal values (a -inf logit's logprob is -inf on both sides) are exact
+    with np.errstate(invalid="ignore"):
+        err = np.where(kv == rv, 0.0, np.abs(kv - rv))
     tol = LOGPROB_TOL * np.maximum(1.0, np.abs(rv))
     assert np.all(err <= tol), f"{label} logprobs off by {err.max():.3g}"
 

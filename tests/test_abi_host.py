@@ -102,7 +102,7 @@ def test_rowstats_run_zero_rows_is_a_no_op(entry):
 @pytest.mark.parametrize("kwargs,code", [
     (dict(K=0), ERR_K),
     (dict(K=9), ERR_K),
-    (dict(K=65, vocab=100, stride=100), ERR_K),
+    (dict(K=101, vocab=100, stride=100), ERR_K),
     (dict(rows=-2), ERR_SHAPE),
     (dict(rows=2**31), ERR_SHAPE),
     (dict(vocab=0), ERR_SHAPE),

@@ -35,8 +35,8 @@ typedef enum rowstats_status {
   ROWSTATS_ERR_SHAPE = -2,  /* rows < 0, or (rows > 0 and: rows > 2^31 - 1,
                                vocab < 1, vocab > 2^31 - 1 - 65536,
                                row_stride < vocab, canvas_len < 1) */
-  ROWSTATS_ERR_K = -3,      /* K < 1 or K > vocab; for the stash num_topk < 0,
-                               num_topk > vocab or num_topk > 64 */
+  ROWSTATS_ERR_K = -3,      /* K < 1 or K > vocab; for the stash num_topk < 0
+                               or num_topk > vocab */
   ROWSTATS_ERR_DTYPE = -4,  /* probs_dtype is not one of rowstats_probs_dtype */
   ROWSTATS_ERR_HIP = -5,    /* a HIP call failed (allocation, launch); see last_error */
   ROWSTATS_ERR_COOP = -6,   /* rowstats_run keeps the ceil(vocab / 2048) chunks of a
@@ -253,7 +253,10 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows,
  *   keep        uint8 [m]: nonzero = converged, written.
  *   temps       fp32 [m]: s = x / max(temps[j], 1e-10f) (IEEE fp32 division;
  *               T <= 0 uses 1e-10 as in rowstats_run's entropy).
- *   num_topk    0 <= num_topk <= min(vocab, 64).
+ *   num_topk    0 <= num_topk <= vocab. Up to 64 the stash runs on the
+ *               one-pass top-K kernel; above 64 on the workgroup-per-row
+ *               kernel of topk_logprobs (the row read 2 + 6 times per 4096
+ *               keys).
  *   num_token_ids, token_ids, token_ids_stride  NULL token_ids: no request
  *               has ids. Otherwise int32 num_token_ids [m] and token_ids
  *               [m, token_ids_stride] (row j at token_ids + j * stride):

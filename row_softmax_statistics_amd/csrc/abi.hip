@@ -290,22 +290,31 @@ int plan_and_launch_topk(DeviceState &d, TopKParams &p, hipStream_t s) {
   return note_stream(d, s);
 }
 
-// Scratch layout and launches of the top-K path for K > kTopKMax: the
-// kept-row list and temperatures after the scratch head (whose row-claim
-// counters the pre-pass zeroes, as for every top-K call).
+// Scratch layout and launches of the top-K path for K > kTopKMax (and the
+// stash for num_topk > kTopKMax): the kept-row list, temperatures and, for
+// the stash, stash rows and requests after the scratch head (whose
+// row-claim counters the pre-pass zeroes, as for every top-K call).
 int plan_and_launch_topk_wide(DeviceState &d, TopKParams &p, hipStream_t s) {
   auto align16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
   const size_t temp_bytes = align16((size_t)p.rows * sizeof(float));
   const size_t kept_bytes = align16(((size_t)p.rows + 1) * sizeof(int64_t));
+  const size_t dst_bytes = p.stash ? (size_t)p.rows * sizeof(int64_t) : 0;
+  const size_t req_bytes = p.stash ? align16((size_t)p.rows * sizeof(int32_t)) : 0;
   int rc = order_after_last(d, s);
   if (rc) return rc;
-  if ((rc = ensure_grow_scratch(d, kScratchHead + temp_bytes + kept_bytes, s))) return rc;
+  if ((rc = ensure_grow_scratch(d, kScratchHead + temp_bytes + kept_bytes + dst_bytes + req_bytes,
+                                s)))
+    return rc;
   char *base = reinterpret_cast<char *>(d.grow.base);
   p.counters = reinterpret_cast<uint32_t *>(base);
   base += kScratchHead;
   p.kept_temp = reinterpret_cast<float *>(base);
   base += temp_bytes;
   p.kept = reinterpret_cast<int64_t *>(base);
+  base += kept_bytes;
+  p.kept_dst = p.stash ? reinterpret_cast<int64_t *>(base) : nullptr;
+  base += dst_bytes;
+  p.kept_req = p.stash ? reinterpret_cast<int32_t *>(base) : nullptr;
   p.err_flag = d.grow.err;
   hipError_t e = topk_wide_launch(p, s);
   if (e != hipSuccess) return fail_hip(e, "top-K kernel launch");
@@ -650,9 +659,9 @@ int stash_converged_logprobs(const float *logits, int64_t row_stride, int64_t lo
   if (canvas_len > 0x7FFFFFFFLL / m)
     return fail(ROWSTATS_ERR_SHAPE, "m * canvas_len must be <= 2^31 - 1, got %lld * %lld",
                 (long long)m, (long long)canvas_len);
-  if (num_topk < 0 || (int64_t)num_topk > vocab || num_topk > kTopKMax)
-    return fail(ROWSTATS_ERR_K, "num_topk must be in [0, min(vocab=%lld, %d)], got %d",
-                (long long)vocab, kTopKMax, num_topk);
+  if (num_topk < 0 || (int64_t)num_topk > vocab)
+    return fail(ROWSTATS_ERR_K, "num_topk must be in [0, vocab=%lld], got %d", (long long)vocab,
+                num_topk);
   if ((int64_t)stash_width < (int64_t)num_topk + 1)
     return fail(ROWSTATS_ERR_SHAPE, "stash_width %d < num_topk + 1 = %d", stash_width,
                 num_topk + 1);
@@ -708,6 +717,7 @@ int stash_converged_logprobs(const float *logits, int64_t row_stride, int64_t lo
   p.out_ids32 = out_ids;
   p.out_lp = out_logprobs;
   p.out_ranks = out_ranks;
+  if (num_topk > kTopKMax) return plan_and_launch_topk_wide(*d, p, s);
   return plan_and_launch_topk(*d, p, s);
 }
 

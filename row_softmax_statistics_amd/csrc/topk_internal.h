@@ -69,10 +69,13 @@ hipError_t topk_launch(const TopKParams &p, int grid, hipStream_t stream);
 // Queues the kept-row pre-pass alone (p.keep, p.temps, p.rows, p.canvas_len,
 // p.kept, p.kept_temp, p.counters).
 hipError_t kept_rows_launch(const TopKParams &p, hipStream_t stream);
-// K > kTopKMax (up to the vocabulary): the kept-row pre-pass and one
-// workgroup per kept position (p.rows of them, the surplus returns at once);
-// uses p.logits, p.ld, p.vocab, p.vec_ok, p.K, p.out_vals, p.out_idx and the
-// pre-pass outputs.
+// Queues the stash's kept-row pre-pass alone (the stash fields, p.kept,
+// p.kept_temp, p.kept_dst, p.kept_req, p.counters, p.err_flag).
+hipError_t stash_rows_launch(const TopKParams &p, hipStream_t stream);
+// K > kTopKMax (up to the vocabulary), or a stash with K_out > kTopKMax: the
+// kept-row pre-pass and one workgroup per kept position (p.rows of them, the
+// surplus returns at once); uses p.logits, p.ld, p.vocab, p.vec_ok, p.K,
+// p.out_vals, p.out_idx (or the stash fields) and the pre-pass outputs.
 hipError_t topk_wide_launch(const TopKParams &p, hipStream_t stream);
 
 }  // namespace rowstats

@@ -862,6 +862,11 @@ hipError_t kept_rows_launch(const TopKParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t stash_rows_launch(const TopKParams &p, hipStream_t stream) {
+  stash_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 hipError_t topk_launch(const TopKParams &p, int grid, hipStream_t stream) {
   if (p.stash)
     stash_rows_kernel<<<dim3(1), dim3(kListThreads), 0, stream>>>(p);

@@ -16,6 +16,10 @@
 //      to v in column order (one pass with a workgroup scan per tile), a
 //      bitonic sort of the batch in LDS (64-bit keys: value, then lower
 //      column) and the batch's logprobs (s - m) - log S in rank order.
+// Stash rows (same page, stash_converged_logprobs): the sum pass also finds
+// the argmax (lowest column at m) and its rank (the columns at m); the row
+// is the argmax, then the request's token ids (gathered) or the K_out
+// largest keys (step 2), then token 0 at -inf up to the width.
 // The kernel is a fallback for large K: it reads each row 2 + 6 times per
 // batch and has no place in the one-pass budget of the main top-K kernel.
 #include "topk_internal.h"
@@ -94,6 +98,17 @@ __device__ __forceinline__ float block_max(float v, WideShared &sh) {
   return r;
 }
 
+__device__ __forceinline__ int32_t block_min(int32_t v, WideShared &sh) {
+  v = wave_allreduce(v, MinI());
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) sh.red_u[w] = (uint32_t)v;
+  __syncthreads();
+  int32_t r = (int32_t)sh.red_u[0];
+  for (int i = 1; i < kWideWaves; ++i) r = min(r, (int32_t)sh.red_u[i]);
+  __syncthreads();
+  return r;
+}
+
 __device__ __forceinline__ double block_sum(double v, WideShared &sh) {
   v = wave_allreduce(v, SumD());
   const int w = threadIdx.x / kWave;
@@ -138,7 +153,7 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
   const Recip rc = recip_of(tc);
   const float *xrow = p.logits + row * p.ld;
   const int32_t V = p.vocab;
-  const int K = p.K;
+  int K = p.K;
 
   // ---- 1. row maximum and S = sum exp(s - m) ----
   float mt = -INFINITY;
@@ -151,16 +166,74 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
       if (ok[i]) mt = fmaxf(mt, s[i]);
   }
   const float m = block_max(mt, sh);
+  const uint32_t km = ukey32(m);
   float st = 0.0f;
+  uint32_t at_max = 0;        // columns whose key is m's (-0 == +0)
+  int32_t first = INT32_MAX;  // the lowest of them
   for (int32_t base = 0; base < V; base += kTile) {
     float s[4];
     bool ok[4];
     load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (ok[i]) st += __builtin_amdgcn_exp2f(fmaxf(s[i] - m, -FLT_MAX) * 1.44269504088896340736f);
+    for (int i = 0; i < 4; ++i) {
+      if (ok[i]) {
+        st += __builtin_amdgcn_exp2f(fmaxf(s[i] - m, -FLT_MAX) * 1.44269504088896340736f);
+        if (ukey32(s[i]) == km) {
+          ++at_max;
+          first = min(first, base + 4 * t + i);
+        }
+      }
+    }
   }
   const double log_s = log_d(block_sum((double)st, sh));
+
+  // stash rows: argmax, rank, token ids and padding here, the top keys below
+  int32_t *oid = nullptr;
+  float *olp = nullptr;
+  const bool logits_mode = p.stash && p.logits_mode != 0;
+  auto value = [&](float s) -> float {
+    return logits_mode ? s : (float)(((double)s - (double)m) - log_s);
+  };
+  if (p.stash) {
+    uint32_t ties;
+    block_prefix(at_max, ties, sh);
+    const int32_t arg = block_min(first, sh);
+    const int64_t dst = p.kept_dst[pos];
+    const int32_t j = p.kept_req[pos];
+    const int32_t W = p.width;
+    oid = p.out_ids32 + dst * W;
+    olp = p.out_lp + dst * W;
+    int n = p.K_out;
+    bool by_ids = false;
+    if (p.ids != nullptr) {
+      const int32_t c = p.num_ids[j];
+      if (c > 0) {
+        by_ids = true;
+        n = (int)min((int64_t)min(c, W - 1), p.ids_stride);
+      }
+    }
+    if (t == 0) {
+      oid[0] = arg;
+      olp[0] = value(key32_value((int32_t)(km ^ 0x80000000u)));
+      p.out_ranks[dst] = (int32_t)ties;
+    }
+    if (by_ids) {
+      const int32_t *idr = p.ids + (int64_t)j * p.ids_stride;
+      for (int i = t; i < n; i += kWideThreads) {
+        const int32_t id = idr[i];
+        float v = -INFINITY;
+        if (id >= 0 && id < V) v = value(scale_any(xrow[id], rc, tc));
+        else atomicOr(p.err_flag, kErrIndex);
+        oid[1 + i] = id;
+        olp[1 + i] = v;
+      }
+    }
+    for (int c = 1 + n + t; c < W; c += kWideThreads) {
+      oid[c] = 0;
+      olp[c] = -INFINITY;
+    }
+    K = by_ids ? 0 : n;
+  }
 
   // ---- 2. batches of keys in descending order ----
   uint64_t bound = ~0ull;  // keys of this batch are below it
@@ -285,13 +358,18 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
         __syncthreads();
       }
     }
-    // the batch's logprobs, in rank order
+    // the batch's logprobs (or a stash row's values), in rank order
     for (int i = t; i < nb; i += kWideThreads) {
       const uint64_t k = sh.keys[i];
       const float s = ukey_value(k);
-      const int64_t o = row * (int64_t)K + done + i;
-      p.out_idx[o] = ukey_col(k);
-      p.out_vals[o] = (float)(((double)s - (double)m) - log_s);
+      if (p.stash) {
+        oid[1 + done + i] = ukey_col(k);
+        olp[1 + done + i] = value(s);
+      } else {
+        const int64_t o = row * (int64_t)K + done + i;
+        p.out_idx[o] = ukey_col(k);
+        p.out_vals[o] = (float)(((double)s - (double)m) - log_s);
+      }
     }
     bound = sh.keys[nb - 1];
     bounded = true;
@@ -303,7 +381,7 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
 }  // namespace
 
 hipError_t topk_wide_launch(const TopKParams &p, hipStream_t stream) {
-  hipError_t e = kept_rows_launch(p, stream);
+  hipError_t e = p.stash ? stash_rows_launch(p, stream) : kept_rows_launch(p, stream);
   if (e != hipSuccess) return e;
   TopKParams arg = p;
   if (p.vec_ok)

@@ -245,8 +245,9 @@ def stash(logits=FAKE, stride=8, lrows=8, vocab=8, canvas=2, m=3, src=FAKE, slot
     (dict(m=2**30, canvas=4, positions=4), ERR_SHAPE),
     (dict(K=-1), ERR_K),
     (dict(K=9), ERR_K),
-    (dict(K=65, vocab=100, stride=100, width=70), ERR_K),
+    (dict(K=101, vocab=100, stride=100, width=110), ERR_K),
     (dict(width=2), ERR_SHAPE),        # num_topk + 1 <= width
+    (dict(K=65, vocab=100, stride=100, width=65), ERR_SHAPE),
     (dict(n_slots=0), ERR_SHAPE),
     (dict(positions=1), ERR_SHAPE),    # positions >= canvas_len
     (dict(logits=NULL), ERR_NULL),

@@ -83,14 +83,29 @@ def test_stash_small(vocab, K, with_ids, logits_mode, pad):
     check(w, f"stash V={vocab} K={K} ids={with_ids} logits={logits_mode}")
 
 
-@pytest.mark.parametrize("K", [0, 2, 20])
+LARGE_K = [  # vocab, K, with_ids, logits_mode, ld pad: num_topk above 64
+    (65, 65, False, False, 0), (100, 65, True, False, 0), (300, 300, False, True, 1),
+    (4097, 300, True, False, 3), (5000, 4096, False, False, 0), (5000, 4097, True, True, 0),
+    (20000, 9000, False, False, 0), (70001, 128, True, False, 5),
+]
+
+
+@pytest.mark.parametrize("vocab,K,with_ids,logits_mode,pad", LARGE_K)
+def test_stash_large_k(vocab, K, with_ids, logits_mode, pad):
+    # the workgroup-per-row kernel writes these stash rows
+    w = syn.stash_case(DEV, m=5, canvas_len=3, vocab=vocab, K=K, seed=vocab + K,
+                       ld=vocab + pad, with_ids=with_ids, logits_mode=logits_mode)
+    check(w, f"stash V={vocab} K={K} ids={with_ids} logits={logits_mode}")
+
+
+@pytest.mark.parametrize("K", [0, 2, 20, 200])
 def test_stash_ties(K):
     # quantised values: exact duplicates of the maximum are common
     w = syn.stash_case(DEV, m=8, canvas_len=5, vocab=3000, K=K, seed=50 + K, ties=True, std=1.0)
     check(w, f"stash ties K={K}")
 
 
-@pytest.mark.parametrize("K", [0, 3, 64])
+@pytest.mark.parametrize("K", [0, 3, 64, 100, 8999])
 def test_stash_equal_rows_and_spans(K):
     """All-equal rows (every key ties at the maximum: the rank counts the
     whole row), rows with long -inf spans, and a row that is -inf but one
@@ -125,8 +140,9 @@ def test_stash_wider_positions():
     check(w, "stash positions=7")
 
 
-def test_stash_bad_indices_are_skipped_and_flagged():
-    w = syn.stash_case(DEV, m=5, canvas_len=4, vocab=700, K=3, seed=80, with_ids=True)
+@pytest.mark.parametrize("K", [3, 80])
+def test_stash_bad_indices_are_skipped_and_flagged(K):
+    w = syn.stash_case(DEV, m=5, canvas_len=4, vocab=700, K=K, seed=80, with_ids=True)
     w.keep.fill_(1)
     w.valid.fill_(4)
     w.num_ids.zero_()
@@ -191,6 +207,17 @@ def _oracle_positions(w, picks, x):
     return tuple(np.concatenate([q[k] for q in parts]) for k in range(3))
 
 
+def _compare_positions(w, g, blk, label):
+    src = w.src.cpu().numpy()
+    slots = w.slots.cpu().numpy()
+    rows = [int(src[j]) * w.canvas_len + p for j, p in blk]
+    o = _oracle_positions(w, blk, host_rows(w.logits, rows))
+    gsel = (np.stack([g[0][slots[j], p] for j, p in blk])[:, None],
+            np.stack([g[1][slots[j], p] for j, p in blk])[:, None],
+            np.array([g[2][slots[j], p] for j, p in blk])[:, None])
+    compare(gsel, o, False, label)
+
+
 def test_stash_c4_full_size():
     """The S4 stash (C4's 4096 x 262144 logits): every kept position checked
     against the oracle, 256 positions at a time."""
@@ -204,13 +231,7 @@ def test_stash_c4_full_size():
     picks = [(int(j), p) for j in np.flatnonzero(keep)
              for p in range(min(int(valid[j]), w.canvas_len))]
     for b in range(0, len(picks), 256):
-        blk = picks[b:b + 256]
-        rows = [int(src[j]) * w.canvas_len + p for j, p in blk]
-        o = _oracle_positions(w, blk, host_rows(w.logits, rows))
-        gsel = (np.stack([g[0][slots[j], p] for j, p in blk])[:, None],
-                np.stack([g[1][slots[j], p] for j, p in blk])[:, None],
-                np.array([g[2][slots[j], p] for j, p in blk])[:, None])
-        compare(gsel, o, False, f"S4 positions {b}+")
+        _compare_positions(w, g, picks[b:b + 256], f"S4 positions {b}+")
     record("S4", kept_positions=len(picks), compared="all kept positions")
     # positions past valid and slots of dropped requests keep their sentinel
     for j in range(w.m):
@@ -220,4 +241,26 @@ def test_stash_c4_full_size():
     for sl in range(w.n_slots):
         if sl not in used:
             assert np.all(g[0][sl] == SENT_ID)
+    torch.cuda.empty_cache()
+
+
+def test_stash_c4_full_size_num_topk_1000():
+    """The S4 stash with num_topk = 1000 (the workgroup-per-row kernel):
+    64 sampled kept positions against the oracle, the others' sentinels."""
+    w = syn.stash_c4(DEV, K=1000)
+    g = run_gpu(w)
+    rs.check_device()
+    keep = w.keep.cpu().numpy()
+    valid = w.valid.cpu().numpy()
+    slots = w.slots.cpu().numpy()
+    picks = [(int(j), p) for j in np.flatnonzero(keep)
+             for p in range(min(int(valid[j]), w.canvas_len))]
+    rng = np.random.default_rng(31)
+    blk = [picks[i] for i in sorted(rng.choice(len(picks), 64, replace=False))]
+    _compare_positions(w, g, blk, "S4 num_topk=1000")
+    record("S4 num_topk=1000", kept_positions=len(picks), compared=len(blk))
+    for j in range(w.m):
+        n = min(int(valid[j]), w.canvas_len) if keep[j] else 0
+        assert np.all(g[2][slots[j], :n] >= 1)
+        assert np.all(g[2][slots[j], n:] == SENT_ID)
     torch.cuda.empty_cache()

@@ -174,7 +174,9 @@ def bench_selfcond_product(w, d, steps, warmup, dtype=None):
     unless ``dtype``), then rowstats_selfcond_product multiplies them by a
     seeded [vocab, d] table packed once beforehand (a weight: packed at load
     time, outside the timed calls). A step is both calls. Also times the
-    product call alone. Work per step: 2 rows vocab d flops on the matrix
+    product call alone, and for context torch.matmul (the vendor GEMM
+    library) on the same probabilities and table, stored [vocab, d] and
+    [d, vocab] (bf16 out). Work per step: 2 rows vocab d flops on the matrix
     cores; bytes: logits read once, probabilities written and read back, the
     table read once, 20 B of statistics and 4 d B of product per row."""
     import torch
@@ -184,7 +186,6 @@ def bench_selfcond_product(w, d, steps, warmup, dtype=None):
     dtype = dtype or torch.bfloat16
     embed = syn.embedding(w.vocab, d, seed=21, device=dev, dtype=dtype)
     packed = rs.pack_embed(embed)
-    del embed
     stats = (torch.empty(w.rows, dtype=torch.int64, device=dev),
              torch.empty(w.rows, dtype=torch.int64, device=dev),
              torch.empty(w.rows, dtype=torch.float32, device=dev),
@@ -201,13 +202,22 @@ def bench_selfcond_product(w, d, steps, warmup, dtype=None):
     ms, wall = time_launches(step, steps, warmup)
     pms, _ = time_launches(product, steps, warmup)
     rs.check_device()
+    lib_vd, _ = time_launches(lambda: torch.matmul(stats[3], embed), steps, warmup)
+    embed_t = embed.t().contiguous()
+    del embed
+    lib_dv, _ = time_launches(lambda: torch.matmul(stats[3], embed_t.t()), steps, warmup)
+    del embed_t
     flops = 2.0 * w.rows * w.vocab * d
     nbytes = 8 * w.rows * w.vocab + 2 * w.vocab * d + (20 + 4 * d) * w.rows
     del packed, stats, res
     return {"ms": ms, "wall_ms": wall, "d": d, "tflops": flops / ms / 1e9,
             "mfma_frac": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, "bytes": nbytes,
             "gbs": nbytes / ms / 1e6, "product_ms": pms, "product_tflops": flops / pms / 1e9,
-            "product_mfma_frac": flops / pms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+            "product_mfma_frac": flops / pms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+            "library": {"what": "torch.matmul of the same probabilities and table, bf16 out",
+                        "table_vocab_by_d_ms": round(lib_vd, 4),
+                        "table_d_by_vocab_ms": round(lib_dv, 4),
+                        "table_d_by_vocab_tflops": round(flops / lib_dv / 1e9, 1)}}
 
 
 def bench_topk(w, steps, warmup):

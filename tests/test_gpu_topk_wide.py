@@ -95,3 +95,42 @@ def test_repeat_calls_are_bit_identical():
     a, b = run(w), run(w)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     done()
+
+
+def test_calls_on_two_streams_are_ordered():
+    # the workgroup-per-row path shares the scratch head and the kept-row
+    # lists with the other entry points: calls alternating between two
+    # streams (row statistics, a one-pass top-K and a stash in between)
+    # give the results of one stream
+    w = case(rows=12, vocab=20000, canvas=3, K=700, seed=19, ties=True)
+    ref = run(w)
+    sw = syn.stash_case(DEV, m=5, canvas_len=3, vocab=5000, K=90, seed=20)
+    ids = torch.full((sw.n_slots, sw.positions, sw.width), -7, dtype=torch.int32, device=DEV)
+    lp = torch.full((sw.n_slots, sw.positions, sw.width), 7.0, device=DEV)
+    rk = torch.full((sw.n_slots, sw.positions), -7, dtype=torch.int32, device=DEV)
+
+    def stash():
+        rs.stash_converged_logprobs(sw.logits, sw.canvas_len, sw.src, sw.slots, sw.keep,
+                                    sw.valid, sw.temps, sw.K, sw.num_ids, sw.ids, ids, lp, rk,
+                                    sw.logits_mode)
+        return ids.clone(), lp.clone(), rk.clone()
+
+    ref_stash = stash()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for it in range(3):
+        a, b = (s1, s2) if it % 2 == 0 else (s2, s1)
+        with torch.cuda.stream(a):
+            rs.sample_row_stats(w.logits, w.temps, w.canvas_len, 5, torch.bfloat16)
+            got = run(w)
+        with torch.cuda.stream(b):
+            rs.topk_logprobs(w.logits, w.temps, w.canvas_len, w.keep_mask, 20)
+            got_stash = stash()
+        outs.append((got, got_stash))
+    torch.cuda.synchronize()
+    for got, got_stash in outs:
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+        for x, y in zip(got_stash, ref_stash):
+            assert torch.equal(x, y)
+    done()

@@ -19,9 +19,12 @@
 // chunk's K largest keys in rank order. The blocks of the threshold rule
 // are the 64 lanes (32 columns each): with v_K the K-th largest lane
 // maximum, only columns with s >= v_K can be in the chunk's top-K (about
-// K + a few on typical rows). They are listed in LDS and ranked exactly
-// (rank = number of larger keys). A chunk where the rule leaves too many
-// columns (long runs of equal values) takes K rounds of exact extraction.
+// K + a few on typical rows). For K above 32, where the K-th largest of 64
+// lane maxima falls deep into the chunk, v_K is the K-th largest of the
+// lanes' two largest values instead (again K distinct columns reach it).
+// The candidates are listed in LDS and ranked exactly (rank = number of
+// larger keys). A chunk where the rule leaves too many columns (long runs
+// of equal values) takes K rounds of exact extraction.
 //
 // One member per row (the merger, rotating) reads the row's C records one
 // row later: the headers give log Z; the K-th largest of the lanes' largest
@@ -51,6 +54,8 @@ constexpr int kCandKeys = 256;
 constexpr int kListPad = 8;
 constexpr int kCandCap = kCandKeys - kListPad;
 constexpr uint64_t kSignBit = 0x8000000000000000ull;
+// From this K on the chunk threshold uses the lanes' two largest values.
+constexpr int kTwoPerLaneFrom = 33;
 
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
@@ -106,6 +111,17 @@ __device__ __forceinline__ U wave_kth_largest(U u, int k) {
   for (int b = 8 * (int)sizeof(U) - 1; b >= 0; --b) {
     const U c = res | ((U)1 << b);
     res = (__popcll(__ballot(u >= c)) >= k) ? c : res;
+  }
+  return res;
+}
+
+// The same over two values per lane (1 <= k <= 128).
+__device__ __forceinline__ uint32_t wave_kth_largest2(uint32_t u, uint32_t w, int k) {
+  uint32_t res = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = res | (1u << b);
+    res = (__popcll(__ballot(u >= c)) + __popcll(__ballot(w >= c)) >= k) ? c : res;
   }
   return res;
 }
@@ -248,8 +264,21 @@ __device__ __forceinline__ void reduce_chunk_topk(const TopKParams &p, int64_t r
     }
   }
 
-  // ---- threshold: the K-th largest lane maximum ----
-  const uint32_t uk = wave_kth_largest<uint32_t>((uint32_t)key32(mt) ^ 0x80000000u, K);
+  // ---- threshold: the K-th largest lane maximum (or of the lanes' two
+  // largest values) ----
+  uint32_t uk;
+  if (K < kTwoPerLaneFrom) {
+    uk = wave_kth_largest<uint32_t>((uint32_t)key32(mt) ^ 0x80000000u, K);
+  } else {
+    float a = -INFINITY, b = -INFINITY;  // the lane's largest and second largest
+#pragma unroll
+    for (int k = 0; k < 4 * kQ; ++k) {
+      const float x = comp(v[k >> 2], k & 3);
+      b = __builtin_amdgcn_fmed3f(a, b, x);
+      a = fmaxf(a, x);
+    }
+    uk = wave_kth_largest2((uint32_t)key32(a) ^ 0x80000000u, (uint32_t)key32(b) ^ 0x80000000u, K);
+  }
   const float vk = key32_value((int32_t)(uk ^ 0x80000000u));
   // Bit 31 - k of cm: element k is a candidate (s >= v_K). With v_K > -inf
   // the K lanes whose maxima reach v_K give at least K candidates, all real

@@ -376,7 +376,9 @@ def _check_untouched(w, vals, idx):
 
 @pytest.mark.parametrize("vocab,K", [(1, 1), (2, 2), (5, 3), (20, 20), (64, 20), (100, 64),
                                      (4097, 20), (16385, 5), (40000, 20), (40000, 64),
-                                     (70001, 1)])
+                                     (70001, 1),
+                                     # two values per lane in the chunk threshold
+                                     (40000, 33), (40000, 48), (4097, 63), (70001, 40)])
 @pytest.mark.parametrize("ties", [False, True], ids=["plain", "ties"])
 def test_topk_small(vocab, K, ties):
     w = _topk_case(rows=9, vocab=vocab, canvas=3, K=K, seed=vocab + K, ties=ties,
@@ -387,8 +389,9 @@ def test_topk_small(vocab, K, ties):
     done()
 
 
-def test_topk_adversarial_rows():
-    vocab, K = 40000, 20
+@pytest.mark.parametrize("K", [20, 50])
+def test_topk_adversarial_rows(K):
+    vocab = 40000
     w = _topk_case(rows=6, vocab=vocab, canvas=1, K=K, seed=3)
     w.keep_mask = torch.ones(6, dtype=torch.uint8, device=DEV)
     w.logits[0] = 1.5                       # every lane max ties: overflow path
@@ -398,7 +401,7 @@ def test_topk_adversarial_rows():
     w.logits[3, 5000:5300] = 9.0             # 300 duplicates of the max
     w.logits[4] = torch.linspace(-1, 1, vocab, device=DEV)
     vals, idx = _run_topk(w)
-    compare_topk(w, vals, idx, range(w.rows), "topk adversarial")
+    compare_topk(w, vals, idx, range(w.rows), f"topk adversarial K={K}")
     done()
 
 
@@ -427,9 +430,10 @@ def test_scaling_ranges(temp):
     out = gpu_rowstats(w)
     compare_rowstats(w, out, range(rows), f"magnitudes T={temp}")
     w.keep_mask = torch.ones(rows, dtype=torch.uint8, device=DEV)
-    w.K = 9
-    vals, idx = _run_topk(w)
-    compare_topk(w, vals, idx, range(rows), f"topk magnitudes T={temp}")
+    for K in (9, 45):
+        w.K = K
+        vals, idx = _run_topk(w)
+        compare_topk(w, vals, idx, range(rows), f"topk magnitudes T={temp} K={K}")
     done()
 
 
@@ -450,13 +454,16 @@ def test_topk_one_wave_groups():
     done()
 
 
-def test_c4_topk_full_size():
-    w = syn.c4(DEV)
+@pytest.mark.parametrize("K", [20, 64])
+def test_c4_topk_full_size(K):
+    # K = 64 takes the two-values-per-lane chunk threshold
+    w = syn.c4(DEV, K=K)
     vals, idx = _run_topk(w)
     _check_untouched(w, vals, idx)
     kept_rows = [r for r in range(w.rows) if int(w.keep_mask[r // w.canvas_len])]
     for b in range(0, len(kept_rows), 256):
-        compare_topk(w, vals, idx, kept_rows[b:b + 256], f"C4 kept rows {b}+")
-    record("C4", rows=w.rows, kept_rows=len(kept_rows), compared="all kept rows")
+        compare_topk(w, vals, idx, kept_rows[b:b + 256], f"C4 K={K} kept rows {b}+")
+    record("C4" if K == 20 else f"C4 K={K}", rows=w.rows, kept_rows=len(kept_rows),
+           compared="all kept rows")
     del vals, idx, w
     done()

@@ -215,7 +215,7 @@ int rowstats_selfcond_product(const void *probs, int64_t probs_stride,
  *   keep_mask   uint8 [ceil(rows / canvas_len)]: nonzero = slot kept.
  *   K           1 <= K <= vocab. K <= 64 runs the one-pass kernel (every row
  *               read once); larger K runs a separate kernel, one workgroup per
- *               kept row, that reads the row 2 + 6 times per 4096 keys.
+ *               kept row, that reads the row 4 times per 4096 keys.
  *   out_vals    fp32 [rows, K] row-major: out_vals[r, k] = s - log Z at the
  *               column of rank k (descending value, ties to lower column),
  *               log Z = log sum_c exp(s_c).
@@ -255,7 +255,7 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows,
  *               T <= 0 uses 1e-10 as in rowstats_run's entropy).
  *   num_topk    0 <= num_topk <= vocab. Up to 64 the stash runs on the
  *               one-pass top-K kernel; above 64 on the workgroup-per-row
- *               kernel of topk_logprobs (the row read 2 + 6 times per 4096
+ *               kernel of topk_logprobs (the row read 4 times per 4096
  *               keys).
  *   num_token_ids, token_ids, token_ids_stride  NULL token_ids: no request
  *               has ids. Otherwise int32 num_token_ids [m] and token_ids

@@ -7,21 +7,23 @@
 // the lower id) and the _lp_topk_kernel docstring (keys ordered by value,
 // then by lower index, so the top-K is unique).
 //
-// Per row (1024 threads, four consecutive columns per thread and tile):
-//   1. the row maximum m of s = x / Tc, then S = sum exp(s - m) (two passes);
-//   2. in batches of up to kBatch keys below the previous batch's smallest:
-//      the value v of the batch's last key by a radix select over the 32-bit
-//      order-preserving value keys (four passes of 8-bit histograms in LDS),
-//      then the keys above v (one pass, unordered) and the first keys equal
-//      to v in column order (one pass with a workgroup scan per tile), a
-//      bitonic sort of the batch in LDS (64-bit keys: value, then lower
+// Per row (1024 threads, four consecutive columns per thread and tile), in
+// batches of up to kBatch keys below the previous batch's smallest:
+//   1. the value v of the batch's last key by a radix select over the
+//      32-bit order-preserving value keys: digits of 11, 11 and 10 bits,
+//      one pass over the row each with a histogram in LDS; the first batch's
+//      first pass also forms the row maximum m and S = sum exp(s - m)
+//      (online: each thread rescales its sum when its maximum rises);
+//   2. one pass collecting the keys above v (unordered) and the first keys
+//      equal to v in column order (a workgroup scan per tile);
+//   3. a bitonic sort of the batch in LDS (64-bit keys: value, then lower
 //      column) and the batch's logprobs (s - m) - log S in rank order.
-// Stash rows (same page, stash_converged_logprobs): the sum pass also finds
-// the argmax (lowest column at m) and its rank (the columns at m); the row
-// is the argmax, then the request's token ids (gathered) or the K_out
-// largest keys (step 2), then token 0 at -inf up to the width.
-// The kernel is a fallback for large K: it reads each row 2 + 6 times per
-// batch and has no place in the one-pass budget of the main top-K kernel.
+// So K <= 4096 reads the row 4 times. The kernel is a fallback for large K,
+// outside the one-pass budget of the main top-K kernel.
+// Stash rows (same page, stash_converged_logprobs): the first pass also
+// finds the argmax (lowest column at m) and its rank (the columns at m); the
+// row is the argmax, then the request's token ids (gathered) or the K_out
+// largest keys, then token 0 at -inf up to the width.
 #include "topk_internal.h"
 
 #include "chunk_common.h"
@@ -51,9 +53,13 @@ __device__ __forceinline__ int32_t ukey_col(uint64_t k) {
   return 0x7FFFFFFF - (int32_t)(uint32_t)(k & 0xFFFFFFFFu);
 }
 
+constexpr int kDigitBits[3] = {11, 11, 10};  // radix digits, from the top
+constexpr int kDigitShift[3] = {21, 10, 0};
+constexpr int kBins = 2048;
+
 struct WideShared {
   uint64_t keys[kBatch];
-  uint32_t hist[256];
+  uint32_t hist[kBins];
   double red_d[kWideWaves];
   float red_f[kWideWaves];
   uint32_t red_u[kWideWaves];
@@ -142,6 +148,26 @@ __device__ __forceinline__ uint32_t block_prefix(uint32_t v, uint32_t &total, Wi
   return off + incl - v;
 }
 
+// The digit of the radix select from the histogram of one pass: the bin
+// (from the top) where the count of higher keys first reaches `rank`, and
+// the rank left inside it. Thread t scans bins nb - 1 - 2 t and nb - 2 - 2 t.
+__device__ __forceinline__ void pick_digit(int nb, uint32_t rank, WideShared &sh) {
+  const int t = threadIdx.x;
+  const int hi = nb - 1 - 2 * t;
+  const uint32_t c0 = hi >= 0 ? sh.hist[hi] : 0u;
+  const uint32_t c1 = hi >= 1 ? sh.hist[hi - 1] : 0u;
+  uint32_t total;
+  const uint32_t before = block_prefix(c0 + c1, total, sh);  // keys in higher bins
+  if (before < rank && before + c0 >= rank) {
+    sh.digit = (uint32_t)hi;
+    sh.rank = rank - before;
+  } else if (before + c0 < rank && before + c0 + c1 >= rank) {
+    sh.digit = (uint32_t)(hi - 1);
+    sh.rank = rank - before - c0;
+  }
+  __syncthreads();
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
   __shared__ WideShared sh;
@@ -153,39 +179,54 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
   const Recip rc = recip_of(tc);
   const float *xrow = p.logits + row * p.ld;
   const int32_t V = p.vocab;
+  constexpr float kL2e = 1.44269504088896340736f;
   int K = p.K;
 
-  // ---- 1. row maximum and S = sum exp(s - m) ----
-  float mt = -INFINITY;
-  for (int32_t base = 0; base < V; base += kTile) {
-    float s[4];
-    bool ok[4];
-    load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (ok[i]) mt = fmaxf(mt, s[i]);
-  }
-  const float m = block_max(mt, sh);
-  const uint32_t km = ukey32(m);
-  float st = 0.0f;
-  uint32_t at_max = 0;        // columns whose key is m's (-0 == +0)
+  // ---- first pass: m, S (online), the stash's argmax and rank, and the
+  // histogram of the first digit of every key ----
+  for (int i = t; i < kBins; i += kWideThreads) sh.hist[i] = 0u;
+  __syncthreads();
+  float mt = -INFINITY, st = 0.0f;
+  uint32_t at_max = 0;        // columns whose key is mt's (-0 == +0)
   int32_t first = INT32_MAX;  // the lowest of them
   for (int32_t base = 0; base < V; base += kTile) {
     float s[4];
     bool ok[4];
-    load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
+    const int32_t c0 = base + 4 * t;
+    load4<VEC>(xrow, c0, V, rc, tc, s, ok);
+    float m4 = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (ok[i]) {
-        st += __builtin_amdgcn_exp2f(fmaxf(s[i] - m, -FLT_MAX) * 1.44269504088896340736f);
-        if (ukey32(s[i]) == km) {
+        m4 = fmaxf(m4, s[i]);
+        atomicAdd(&sh.hist[ukey32(s[i]) >> kDigitShift[0]], 1u);
+      }
+    }
+    if (m4 > mt) {
+      st *= __builtin_amdgcn_exp2f(fmaxf(mt - m4, -FLT_MAX) * kL2e);
+      if (p.stash && ukey32(m4) != ukey32(mt)) {
+        at_max = 0;
+        first = INT32_MAX;
+      }
+      mt = m4;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (ok[i]) {
+        st += __builtin_amdgcn_exp2f(fmaxf(s[i] - mt, -FLT_MAX) * kL2e);
+        if (p.stash && ukey32(s[i]) == ukey32(mt)) {
           ++at_max;
-          first = min(first, base + 4 * t + i);
+          first = min(first, c0 + i);
         }
       }
     }
   }
-  const double log_s = log_d(block_sum((double)st, sh));
+  const float m = block_max(mt, sh);
+  const uint32_t km = ukey32(m);
+  const bool mine = mt != -INFINITY && ukey32(mt) == km;  // this thread's maximum is the row's
+  const double part =
+      mt == -INFINITY ? 0.0 : (double)st * (double)__builtin_amdgcn_exp2f(fmaxf(mt - m, -FLT_MAX) * kL2e);
+  const double log_s = log_d(block_sum(part, sh));
 
   // stash rows: argmax, rank, token ids and padding here, the top keys below
   int32_t *oid = nullptr;
@@ -196,8 +237,8 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
   };
   if (p.stash) {
     uint32_t ties;
-    block_prefix(at_max, ties, sh);
-    const int32_t arg = block_min(first, sh);
+    block_prefix(mine ? at_max : 0u, ties, sh);
+    const int32_t arg = block_min(mine ? first : INT32_MAX, sh);
     const int64_t dst = p.kept_dst[pos];
     const int32_t j = p.kept_req[pos];
     const int32_t W = p.width;
@@ -235,7 +276,7 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
     K = by_ids ? 0 : n;
   }
 
-  // ---- 2. batches of keys in descending order ----
+  // ---- batches of keys in descending order ----
   uint64_t bound = ~0ull;  // keys of this batch are below it
   bool bounded = false;
   for (int done = 0; done < K;) {
@@ -244,52 +285,30 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
     // radix select: v = value key of the nb-th largest allowed key
     uint32_t prefix = 0;
     uint32_t rank = (uint32_t)nb;  // 1-based rank from the top inside the current prefix
-    for (int d = 0; d < 4; ++d) {
-      const int shift = 24 - 8 * d;
-      for (int i = t; i < 256; i += kWideThreads) sh.hist[i] = 0u;
-      __syncthreads();
-      for (int32_t base = 0; base < V; base += kTile) {
-        float s[4];
-        bool ok[4];
-        load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t k = ukey32(s[i]);
-          const bool match = ((uint64_t)k >> (shift + 8)) == (uint64_t)prefix;
-          if (ok[i] && match && allowed(k, base + 4 * t + i))
-            atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
-        }
-      }
-      __syncthreads();
-      if (t < kWave) {
-        // bins 255 - 4 t .. 252 - 4 t, from the top
-        const int lane = t;
-        uint32_t c[4], sum = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          c[i] = sh.hist[255 - 4 * lane - i];
-          sum += c[i];
-        }
-        uint32_t incl = sum;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const uint32_t v = __shfl_up(incl, (unsigned)o, kWave);
-          if (lane >= o) incl += v;
-        }
-        uint32_t before = incl - sum;  // keys in higher bins
-        if (before < rank && incl >= rank) {
+#pragma unroll 1
+    for (int d = 0; d < 3; ++d) {
+      const int shift = kDigitShift[d];
+      const int bins = 1 << kDigitBits[d];
+      if (d > 0 || bounded) {  // the first batch's first histogram came with m and S
+        for (int i = t; i < kBins; i += kWideThreads) sh.hist[i] = 0u;
+        __syncthreads();
+        const int hshift = shift + kDigitBits[d];  // bits above this digit
+        for (int32_t base = 0; base < V; base += kTile) {
+          float s[4];
+          bool ok[4];
+          load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            if (before < rank && before + c[i] >= rank) {
-              sh.digit = 255u - 4u * (uint32_t)lane - (uint32_t)i;
-              sh.rank = rank - before;
-            }
-            before += c[i];
+            const uint32_t k = ukey32(s[i]);
+            const bool match = ((uint64_t)k >> hshift) == (uint64_t)prefix;
+            if (ok[i] && match && allowed(k, base + 4 * t + i))
+              atomicAdd(&sh.hist[(k >> shift) & (uint32_t)(bins - 1)], 1u);
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
-      prefix = (prefix << 8) | sh.digit;
+      pick_digit(bins, rank, sh);
+      prefix = (prefix << kDigitBits[d]) | sh.digit;
       rank = sh.rank;
       __syncthreads();
     }
@@ -297,47 +316,43 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_kernel(TopKParams p) {
     const uint32_t need = rank;  // keys equal to v that belong to the batch
     const uint32_t above = (uint32_t)nb - need;
 
-    // keys above v, in any order
+    // one pass: the keys above v, in any order, and the first `need` keys
+    // equal to v, in column order
     if (t == 0) sh.count = 0u;
     __syncthreads();
+    uint32_t taken = 0;
     for (int32_t base = 0; base < V; base += kTile) {
       float s[4];
       bool ok[4];
       load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
+      bool tie[4];
+      uint32_t ties_here = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t k = ukey32(s[i]);
         const int32_t c = base + 4 * t + i;
-        if (ok[i] && k > v && allowed(k, c)) {
+        const bool in = ok[i] && allowed(k, c);
+        if (in && k > v) {
           const uint32_t at = atomicAdd(&sh.count, 1u);
           if (at < above) sh.keys[at] = ukey64(k, c);  // (exactly `above` such keys)
         }
+        tie[i] = in && k == v;
+        ties_here += tie[i] ? 1u : 0u;
       }
-    }
-    // the first `need` keys equal to v, in column order
-    uint32_t taken = 0;
-    for (int32_t base = 0; base < V && taken < need; base += kTile) {
-      float s[4];
-      bool ok[4];
-      load4<VEC>(xrow, base + 4 * t, V, rc, tc, s, ok);
-      bool tie[4];
-      uint32_t mine = 0;
+      if (taken < need) {  // uniform: the scan has a barrier
+        uint32_t total;
+        uint32_t at = taken + block_prefix(ties_here, total, sh);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        tie[i] = ok[i] && ukey32(s[i]) == v && allowed(v, base + 4 * t + i);
-        mine += tie[i] ? 1u : 0u;
-      }
-      uint32_t total;
-      uint32_t at = taken + block_prefix(mine, total, sh);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (tie[i]) {
-          if (at < need) sh.keys[above + at] = ukey64(v, base + 4 * t + i);
-          ++at;
+        for (int i = 0; i < 4; ++i) {
+          if (tie[i]) {
+            if (at < need) sh.keys[above + at] = ukey64(v, base + 4 * t + i);
+            ++at;
+          }
         }
+        taken += total;
       }
-      taken += total;
     }
+    __syncthreads();
     // pad to a power of two and sort descending
     int n2 = 64;
     while (n2 < nb) n2 <<= 1;

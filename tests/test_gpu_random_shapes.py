@@ -1,8 +1,9 @@
 """Parity with the oracle on seeded random shapes: row statistics (with bf16,
 fp16 or no probs) and top-K logprobs (K on both sides of 64) over random
 row counts, vocabularies from 1 to 300000, row strides, canvas lengths,
-value spreads, quantised ties and temperature mixes. Every row is compared;
-the shapes come from a fixed seed, so the cases are the same on every run.
+value spreads, quantised ties and temperature mixes, and stash calls with
+random request sets; every row and stash position is compared. The shapes
+come from fixed seeds, so the cases are the same on every run.
 """
 import numpy as np
 import pytest
@@ -66,3 +67,21 @@ def test_topk_random_shape(i):
     compare_topk(w, vals, idx, range(rows), label)
     rs.check_device()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_stash_random_shape(i):
+    import test_gpu_stash as ts
+    r = np.random.default_rng(9500 + i)
+    vocab = int(np.exp(r.uniform(0.0, np.log(150000.0))))
+    K = int(r.integers(0, min(vocab, 200) + 1))
+    m = int(r.integers(1, 40))
+    canvas = int(r.integers(1, 7))
+    with_ids, logits_mode, ties = (bool(r.integers(0, 2)) for _ in range(3))
+    label = (f"random stash {i}: m={m} canvas={canvas} V={vocab} K={K} ids={with_ids} "
+             f"logits={logits_mode} ties={ties}")
+    print("case", label, flush=True)
+    w = syn.stash_case(DEV, m=m, canvas_len=canvas, vocab=vocab, K=K, seed=500 + i,
+                       ld=vocab + int(r.choice([0, 1, 5])), with_ids=with_ids, ties=ties,
+                       logits_mode=logits_mode)
+    ts.check(w, label)

@@ -110,9 +110,13 @@ int rowstats_run(const float *logits, int64_t row_stride, int64_t rows,
  * more returns ROWSTATS_ERR_SCRATCH before anything is queued. At vocab
  * 262144 that is up to 8000 rows per call.
  * Every call on a GPU shares that GPU's array and leaves its contents for
- * the next one (no per-call clearing is needed: its words carry the call's
- * epoch). Calls of this entry point that overlap in time on one GPU (two
- * streams, two threads) race on the array: queue them on one stream.
+ * the next one. A call first clears the part of the array it uses with a
+ * fill kernel (no memset node), so a call captured into a HIP graph can be
+ * replayed any number of times (a replay keeps the epoch its words were
+ * tagged with at capture; the clearing keeps an earlier replay's words from
+ * passing for its own). Calls of this entry point that overlap in time on
+ * one GPU (two streams, two threads, two graphs) race on the array: queue
+ * them on one stream.
  */
 int rowstats_run_noalloc(const float *logits, int64_t row_stride, int64_t rows,
                          int64_t vocab, const float *temps, int64_t canvas_len,

@@ -454,7 +454,14 @@ int rowstats_run_noalloc(const float *logits, int64_t row_stride, int64_t rows, 
                 (long long)rows, p.C, need, d->fixed.bytes);
   if ((rc = next_epoch(d->fixed, s, &p.epoch))) return rc;
   set_scratch(p, d->fixed, head_bytes, tuple_bytes);
-  hipError_t e = rowstats_launch(p, probs_dtype, (int)grid, s);
+  // The part of the array this call uses, and the failed-epoch word, start
+  // at zero (fill kernels, no memset node): a captured call replays with the
+  // epoch of its capture, and the clearing keeps the words of an earlier
+  // replay from passing for this one's.
+  hipError_t e = zero_async(reinterpret_cast<uint32_t *>(d->fixed.base), need / 4, s);
+  if (e == hipSuccess) e = zero_async(d->fixed.err + 1, 1, s);
+  if (e != hipSuccess) return fail_hip(e, "clearing the fixed scratch");
+  e = rowstats_launch(p, probs_dtype, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "row-stats kernel launch");
   d->fixed.epoch = p.epoch;
   return ROWSTATS_OK;

@@ -5,7 +5,9 @@ Both run the same kernels, so the outputs must be bit-identical; the first
 call is also compared with the oracle on a sample of rows. Two calls in a
 row on the fixed scratch array, the second smaller than the first (the
 array keeps the first call's contents), then a call that needs more than
-the array holds, which must be refused before anything is queued.
+the array holds, which must be refused before anything is queued. And a
+call captured into a graph, replayed three times on new logits with eager
+calls in between: every replay must give rowstats_run's bits.
 """
 import ctypes
 
@@ -70,3 +72,27 @@ def test_noalloc_refuses_more_than_the_array():
                                        fake, null, null)
     assert rc == -8, (rc, rs.last_error())
     assert "scratch" in rs.last_error()
+
+
+@pytest.mark.parametrize("rows,vocab", [(64, 30000), (600, 262144)])
+def test_noalloc_graph_replays_match_eager(rows, vocab):
+    w = syn.random_case(DEV, rows=rows, vocab=vocab, canvas_len=4, seed=77,
+                        t_choices=(0.0, 0.7, 1.0), probs_dtype=torch.bfloat16)
+    x = w.logits.clone()  # the captured call reads this buffer on every replay
+    outs = _outputs(w)
+    rs.sample_row_stats_noalloc(x, w.temps, w.canvas_len, w.seed, w.probs_dtype, outs)
+    rs.check_device()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rs.sample_row_stats_noalloc(x, w.temps, w.canvas_len, w.seed, w.probs_dtype, outs)
+    for it in range(3):
+        x.copy_(syn.random_case(DEV, rows=rows, vocab=vocab, canvas_len=4, seed=100 + it).logits)
+        ref = rs.sample_row_stats(x, w.temps, w.canvas_len, w.seed, w.probs_dtype)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rs.check_device()
+        for a, b in zip(ref, outs):
+            assert torch.equal(_bits(a), _bits(b)), f"replay {it}"
+    del g
+    torch.cuda.empty_cache()

@@ -1,6 +1,8 @@
-"""bench.py --summarize on synthetic rocprofv3 CSV files (no GPU): the
-library's dispatches are matched in order to the workloads of the profile
-run, other kernels are ignored, and a dispatch out of plan is an error."""
+"""bench.py on the host (no GPU): --summarize on synthetic rocprofv3 CSV
+files (the library's dispatches are matched in order to the workloads of the
+profile run, other kernels are ignored, and a dispatch out of plan is an
+error); --gpus above 1 is refused; measured traffic is reported only from a
+profile of the current kernel sources."""
 import csv
 import os
 import subprocess
@@ -78,3 +80,22 @@ def test_the_one_time_table_packing_is_not_a_step(tmp_path):
     r = run(tmp_path)
     assert r.returncode == 0, r.stderr
     assert "pack_embed" not in r.stdout
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_recorded_traffic_needs_the_current_sources(tmp_path, monkeypatch):
+    # traffic is reported only from a profile taken of the current kernel sources
+    f = tmp_path / "hbm_traffic.txt"
+    line = "C2 kernel=k fetch_kib=1 write_kib=1 fetch_bytes=1000 write_bytes=24 ratio=1\n"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    f.write_text(f"# header\nsource_hash {bench.source_hash()}\n" + line)
+    assert bench.recorded_traffic("C2") == 1024
+    assert bench.recorded_traffic("C3") is None
+    f.write_text("# header\nsource_hash 0123456789abcdef\n" + line)
+    assert bench.recorded_traffic("C2") is None

@@ -60,8 +60,8 @@ typedef enum rowstats_probs_dtype {
 } rowstats_probs_dtype;
 
 /*
- * Argmax, Gumbel-max sample, entropy and (optionally) the softmax of every
- * row of a [rows, vocab] fp32 logits matrix.
+ * For each row of a [rows, vocab] fp32 logits matrix: the argmax, a
+ * Gumbel-max sample and the entropy, and on request the softmax.
  * Defined by: diffusion_gemma_sampler page, module docstring (one read per
  * row, online max and sum, noise drawn inline, probs written once),
  * sample_row_stats (arguments, outputs, the greedy rule) and
@@ -132,9 +132,9 @@ int rowstats_run_noalloc(const float *logits, int64_t row_stride, int64_t rows,
  *   out[r, j] = sum_c q_r[c] * E[c, j],   q_r = dtype(softmax(s_r)),
  * q_r being the probabilities rowstats_run writes with the same probs_dtype
  * (each within one unit of the exact rounding).
- * Defined by: diffusion_gemma_sampler page, module docstring (the softmax is
- * produced in the model dtype for the self-conditioning matmul); the
- * statistics as for rowstats_run.
+ * Defined by: diffusion_gemma_sampler page, module docstring (the step's
+ * probabilities, kept in the model's own dtype, are the input of the
+ * self-conditioning matrix product); the statistics as for rowstats_run.
  *
  *   logits ... seed, argmax, sample, entropy   as for rowstats_run.
  *   dtype       ROWSTATS_PROBS_BF16 or ROWSTATS_PROBS_FP16: the model dtype,
@@ -209,8 +209,8 @@ int rowstats_selfcond_product(const void *probs, int64_t probs_stride,
 /*
  * Top-K logprobs of the rows of kept slots.
  * Defined by: diffusion_gemma_sampler page, stash_converged_logprobs
- * docstring (rows of slots that did not converge are skipped; kept rows are
- * divided by their temperature; the K largest with ties to the lower id) and
+ * docstring (only the rows of converged slots are read, each scaled by
+ * 1 / temperature; the K largest values, equal ones by lower id) and
  * the _lp_topk_kernel docstring (keys order by value, then by lower index,
  * so the top-K is unique; the K-th largest block maximum bounds it).
  *
@@ -236,11 +236,12 @@ int topk_logprobs(const float *logits, int64_t row_stride, int64_t rows,
  * row each of the argmax, then the request's token ids or the num_topk
  * largest, then padding.
  * Defined by: diffusion_gemma_sampler page, stash_converged_logprobs
- * (docstring: request j owns rows src[j] * canvas_len + p for p < valid[j],
- * divided by temps[j]; kept requests go to out_*[slots[j], p], laid out as
- * the argmax, then the request's token ids if it has any, else the num_topk
- * largest with ties to the lower id, padded with token 0 at -inf; requests
- * not kept are skipped; launcher: num_topk + 1 <= width) and the
+ * (docstring: for a kept request j, position p below valid[j] reads row
+ * src[j] * canvas_len + p, scaled by 1 / temps[j], and writes
+ * out_*[slots[j], p]; column 0 is the argmax, the next columns the
+ * request's listed token ids or else its num_topk largest, equal values by
+ * lower id, and the cells left token 0 at -inf; other requests are not
+ * touched; launcher: num_topk + 1 <= width) and the
  * _lp_topk_kernel docstring (the key order). Where the page shows no body
  * this library reads it as stated below.
  *

@@ -8,10 +8,12 @@
  *
  * Source of the semantics: the vLLM API page "diffusion_gemma_sampler"
  * (DiffusionGemma sampler):
- *   - module docstring: per canvas row, the argmax of the temperature-scaled
- *     logits, a Gumbel-max sample, the softmax entropy and the softmax itself;
- *   - sample_row_stats (docstring): row i uses temps[i // canvas_len]; a zero
- *     temperature is greedy and the entropy clamps the temperature at 1e-10;
+ *   - module docstring: for each canvas row, the argmax of the logits divided
+ *     by the temperature, a Gumbel-max sample, the softmax entropy and the
+ *     softmax;
+ *   - sample_row_stats (docstring): row i takes its temperature from
+ *     temps[i // canvas_len]; T = 0 means greedy, and for the entropy the
+ *     temperature is clamped at 1e-10;
  *   - sample_row_stats_reference: scaled = logits / clamp(T, 1e-10),
  *     Gumbel noise applied only where T > 0, entropy over p > 0 only;
  *   - _lp_topk_kernel docstring: keys order by value, then by lower index;

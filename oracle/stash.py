@@ -6,14 +6,15 @@ baseline may import this module; the product path never does.
 Follows the vLLM API page "diffusion_gemma_sampler", the docstring and the
 launcher of ``stash_converged_logprobs``:
 
-* request ``j`` owns the logits rows ``src[j] * canvas_len + p`` for
-  ``p < valid[j]`` (and ``p < canvas_len``: the launch grid has one program
-  per canvas position), divided by ``temps[j]``;
-* only requests with ``keep[j]`` are read; their rows go to
-  ``out_*[slots[j], p]``;
-* a stash row is laid out as: the argmax, then the request's token ids if it
-  has any, else the ``num_topk`` largest (ties to the lower id), padded with
-  token 0 at -inf; the launcher asserts ``num_topk + 1 <= width``.
+* the rows of request ``j`` are ``src[j] * canvas_len + p``, one per position
+  ``p`` below ``valid[j]`` (and below ``canvas_len``: the launch grid has one
+  program per canvas position), each scaled by ``1 / temps[j]``;
+* a request is read only when ``keep[j]`` is set; position ``p`` of it is
+  written to ``out_*[slots[j], p]``;
+* within a stash row, column 0 is the argmax; the next columns hold the
+  request's token ids when it lists some, otherwise its ``num_topk``
+  largest (equal values by lower id); the cells left are token 0 at -inf;
+  the launcher checks ``num_topk + 1 <= width``.
 
 Readings where the page shows no body (each is listed in the design notes):
 

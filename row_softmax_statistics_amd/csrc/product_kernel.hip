@@ -4,7 +4,8 @@
 // table in the same dtype, on gfx950 matrix cores.
 //
 // Method: vLLM API page "diffusion_gemma_sampler", module docstring (the
-// softmax is produced in the model dtype for the self-conditioning matmul).
+// step's probabilities, kept in the model's own dtype, are the input of the
+// self-conditioning matrix product).
 //
 // E is a weight: it is packed once into the order in which the matrix cores
 // take their B operand, so that every wave loads its E fragments from HBM

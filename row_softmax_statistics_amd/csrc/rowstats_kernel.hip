@@ -1,9 +1,9 @@
 // One-pass row statistics (argmax, Gumbel-max sample, entropy, optional
 // softmax) of temperature-scaled fp32 logits on gfx950.
 //
-// Method: vLLM API page "diffusion_gemma_sampler", module docstring (each
-// row is read once with an online max and sum, the noise is drawn inline and
-// the probabilities are written once) and sample_row_stats /
+// Method: vLLM API page "diffusion_gemma_sampler", module docstring (a
+// single read of each row keeps a running maximum and sum, generates the
+// noise in place and stores the probabilities a single time) and sample_row_stats /
 // sample_row_stats_reference (the statistics and the greedy rule).
 //
 // Work split. A row is cut into C chunks of 2048 columns, and a group of C

@@ -4,7 +4,8 @@
 // on gfx950 bf16 matrix cores, without writing the probabilities.
 //
 // Method: vLLM API page "diffusion_gemma_sampler", module docstring (the
-// softmax is produced in the model dtype for the self-conditioning matmul).
+// step's probabilities, kept in the model's own dtype, are the input of the
+// self-conditioning matrix product).
 //
 // The row-statistics kernel (stats only) runs first and leaves each row's
 // maximum m and 1 / S (S = sum 2^32 exp(s - m)) in its row results. This

@@ -5,9 +5,9 @@
 // temperature; the K largest with ties to the lower id) and the
 // _lp_topk_kernel docstring (64-bit keys: order-preserving int32 of the
 // value in the high word, inverted column in the low word, so keys are
-// distinct and the top-K is unique; the K largest block maxima are K
-// distinct elements at or above the K-th largest block maximum, so nothing
-// below it can be in the top-K).
+// distinct and the top-K is unique; the maxima of K different blocks are
+// K different elements, none below the K-th largest block maximum t, so no
+// element under t belongs to the top-K).
 //
 // Work split. A small pre-pass writes the list of kept rows. Then, as in
 // the row-statistics kernel, a group of C member waves reduces one kept row
@@ -359,8 +359,9 @@ __device__ __forceinline__ int count_at_max(const TopKParams &p, int64_t row, fl
   return wave_allreduce(cnt, SumI());
 }
 
-// One stash row: the argmax, then the request's token ids or the K_out
-// largest keys, then token 0 at -inf up to the width; and the argmax's rank
+// One stash row: column 0 holds the argmax; after it come the request's
+// own token ids or else its K_out largest keys; the cells left up to the
+// width hold token 0 at -inf; and the argmax's rank
 // (the columns at or above its value). buf holds the row's K largest keys
 // in rank order, M its maximum and logS = log sum exp(s - M).
 __device__ __forceinline__ void write_stash_row(const TopKParams &p, int64_t pos, int64_t row,

@@ -375,8 +375,8 @@ def test_topk_two_level_closed_form():
 
 
 def test_block_max_threshold_lemma():
-    # the K largest block maxima are K distinct elements at or above the K-th
-    # largest block max t, so every top-K element is >= t; checked on data
+    # the maxima of K different blocks are K different elements, none below
+    # the K-th largest block maximum t, so every top-K element is >= t; checked on data
     # with many duplicates and on every block width
     for trial in range(200):
         vocab = int(RNG.integers(1, 300))

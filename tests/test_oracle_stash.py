@@ -1,11 +1,11 @@
 """Pins of the stash oracle (CPU only).
 
 The layout rules come from the stash_converged_logprobs docstring on the
-vLLM API page "diffusion_gemma_sampler": request j's rows
-src[j] * canvas_len + p for p < valid[j], divided by temps[j], go to
-out_*[slots[j], p] when keep[j]; a row is the argmax, then the request's
-token ids if it has any, else the num_topk largest (ties to the lower id),
-padded with token 0 at -inf. The values are pinned to the separately
+vLLM API page "diffusion_gemma_sampler": for a kept request j, position p
+below valid[j] reads row src[j] * canvas_len + p, scaled by 1 / temps[j],
+and writes out_*[slots[j], p]; column 0 of a stash row is the argmax, the
+next ones the request's listed token ids or else its num_topk largest
+(equal values by lower id), the rest token 0 at -inf. The values are pinned to the separately
 pinned C oracle of the top-K entry point, to closed forms and to
 invariants of log-softmax.
 """

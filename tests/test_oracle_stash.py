@@ -198,3 +198,20 @@ def test_id_count_limits_and_bad_ids():
     oi, ov, rk = _run(x, 2, [0], [0], [1], [1], [1.0], 2, np.array([0], np.int32), ids,
                       n_slots=1, width=4)
     assert oi[0, 0].tolist() == [9, 9, 8, 0]
+
+
+def test_num_topk_equal_to_the_vocabulary():
+    """With num_topk = V the row lists every column once, in descending value
+    with equal values by lower id (a brute-force sort on quantised values),
+    and the probabilities of the list sum to one."""
+    rng = np.random.default_rng(5)
+    V = 257
+    x = (np.round(rng.standard_normal((3, V)) * 2.0) / 2.0).astype(np.float32)
+    oi, ov, rk = _run(x, 3, [0], [0], [1], [3], [1.0], V, np.zeros(1, np.int32), None,
+                      n_slots=1, width=V + 1)
+    for p in range(3):
+        want = sorted(range(V), key=lambda c: (-float(x[p, c]), c))
+        assert oi[0, p, 1:].tolist() == want
+        assert oi[0, p, 0] == want[0]
+        assert rk[0, p] == int(np.count_nonzero(x[p] == x[p].max()))
+        assert abs(math.fsum(np.exp(ov[0, p, 1:].astype(np.float64))) - 1.0) < 1e-5
